@@ -1,0 +1,337 @@
+"""Pins of the CPU oracle against closed forms, invariants and brute force.
+
+Each ``check_*`` helper takes the function under test so that the mutation
+tests at the bottom can show that a planted mistake in the oracle (on the CPU)
+is rejected by at least one pin.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from decode_megakernel_wave_amd import inputs
+from oracle import brute, chain as ochain, decoder as od
+
+EPS = 1e-5
+
+
+# ---------------------------------------------------------------- RMSNorm
+def check_rmsnorm(fn) -> bool:
+    rng = np.random.default_rng(3)
+    ok = True
+    # mean(h^2) = m / (m + eps) with unit gains, m = mean(x^2) (exact identity)
+    for scale in (0.02, 1.0, 7.0):
+        x = rng.standard_normal(256) * scale
+        m = np.mean(x * x)
+        h = fn(x, np.ones(256), EPS)
+        ok &= abs(np.mean(h * h) - m / (m + EPS)) < 1e-12
+    # constant vector c*1 -> c / sqrt(c^2 + eps) everywhere
+    for c in (-3.0, 0.01, 2.5):
+        h = fn(np.full(64, c), np.ones(64), EPS)
+        ok &= np.allclose(h, c / math.sqrt(c * c + EPS), rtol=0, atol=1e-14)
+    # the gain multiplies element-wise after normalising
+    g = np.arange(1, 9, dtype=np.float64)
+    h = fn(np.ones(8), g, 0.0)
+    ok &= np.allclose(h, g, rtol=0, atol=1e-14)
+    return bool(ok)
+
+
+def test_rmsnorm_pins():
+    assert check_rmsnorm(od.rmsnorm)
+
+
+# ---------------------------------------------------------------- RoPE
+def check_rope(fn) -> bool:
+    rng = np.random.default_rng(4)
+    hd, theta = 8, 10000.0
+    ok = True
+    u = rng.standard_normal((3, hd))
+    # R_0 is the identity; rotations keep the norm of every head
+    ok &= np.allclose(fn(u, 0, theta), u, atol=1e-15)
+    ok &= np.allclose(np.linalg.norm(fn(u, 37, theta), axis=-1), np.linalg.norm(u, axis=-1))
+    # relative position: <R_p q, R_p' k> = <R_{p-p'} q, k>
+    q, k = rng.standard_normal(hd), rng.standard_normal(hd)
+    for p, pp in ((5, 2), (100, 31), (7, 7)):
+        lhs = np.dot(fn(q[None], p, theta)[0], fn(k[None], pp, theta)[0])
+        rhs = np.dot(fn(q[None], p - pp, theta)[0], k)
+        ok &= abs(lhs - rhs) < 1e-12
+    # explicit angles: pair (i, i + hd/2) turns by p * theta^(-2i/hd)
+    # hd=4, theta=100: w_0 = 1, w_1 = 100^(-1/2) = 0.1
+    for i, p, ang in ((0, 1, 1.0), (1, 10, 1.0), (1, 5, 0.5), (0, 3, 3.0)):
+        e = np.zeros((1, 4))
+        e[0, i] = 1.0
+        r = fn(e, p, 100.0)[0]
+        want = np.zeros(4)
+        want[i], want[i + 2] = math.cos(ang), math.sin(ang)
+        ok &= np.allclose(r, want, atol=1e-14)
+    # one position per row of a [P, heads, hd] block equals the scalar form
+    U = rng.standard_normal((4, 2, hd))
+    blk = fn(U, np.arange(4), theta)
+    ok &= all(np.allclose(blk[t], fn(U[t], t, theta), atol=1e-15) for t in range(4))
+    return bool(ok)
+
+
+def test_rope_pins():
+    assert check_rope(od.rope_rotate)
+
+
+# ---------------------------------------------------------------- softmax / attention
+def check_attend(fn) -> bool:
+    rng = np.random.default_rng(5)
+    ok = True
+    # one cached position: the output is that position's value row
+    q, K, V = rng.standard_normal(16), rng.standard_normal((1, 16)), rng.standard_normal((1, 16))
+    ok &= np.allclose(fn(q, K, V), V[0], atol=1e-15)
+    # identical keys: uniform weights, the output is the mean value row
+    K = np.tile(rng.standard_normal(16), (5, 1))
+    V = rng.standard_normal((5, 16))
+    ok &= np.allclose(fn(q, K, V), V.mean(axis=0), atol=1e-14)
+    # scale 1/sqrt(hd): hd=4, scores (c/2, 0) with c = 2 ln 3 give weights (3/4, 1/4)
+    c = 2.0 * math.log(3.0)
+    q = np.array([c, 0.0, 0.0, 0.0])
+    K = np.array([[1.0, 0, 0, 0], [0, 0, 0, 0]])
+    V = np.array([[1.0, 0, 0, 0], [0, 1.0, 0, 0]])
+    ok &= np.allclose(fn(q, K, V), [0.75, 0.25, 0, 0], atol=1e-14)
+    return bool(ok)
+
+
+def test_softmax_invariants():
+    rng = np.random.default_rng(6)
+    s = rng.standard_normal((7, 33)) * 5
+    p = od.softmax(s)
+    assert np.allclose(p.sum(axis=-1), 1.0, atol=1e-14)
+    assert np.allclose(od.softmax(s + 123.0), p, atol=1e-14)
+    assert np.all(p > 0)
+
+
+def test_attend_pins():
+    assert check_attend(od.attend)
+
+
+def check_silu(fn) -> bool:
+    ok = fn(np.array(0.0)) == 0.0
+    ok &= abs(fn(np.array(1.0)) - 1.0 / (1.0 + math.exp(-1.0))) < 1e-15
+    ok &= abs(fn(np.array(-2.0)) - (-2.0 / (1.0 + math.exp(2.0)))) < 1e-15
+    ok &= abs(fn(np.array(40.0)) - 40.0) < 1e-12
+    return bool(ok)
+
+
+def test_silu_pins():
+    assert check_silu(od.silu)
+
+
+def test_fp16_round_closed_forms():
+    ulp = 2.0 ** -10
+    cases = {
+        1.0 + 2.0 ** -11: 1.0,                 # tie -> even (1.0)
+        1.0 + 3 * 2.0 ** -11: 1.0 + 2 * ulp,   # tie -> even mantissa
+        1.0 + 2.0 ** -11 + 2.0 ** -30: 1.0 + ulp,
+        65504.0: 65504.0,
+        65519.0: 65504.0,
+        65520.0: math.inf,                     # tie between 65504 and 2^16 -> overflow
+        2.0 ** -25: 0.0,                       # half of the smallest subnormal -> 0
+        3 * 2.0 ** -25: 2.0 ** -23,            # subnormal tie -> even
+        -0.1: -0.0999755859375,
+    }
+    for x, want in cases.items():
+        assert od.fp16_round(np.array(x)) == want, x
+
+
+# ---------------------------------------------------------------- whole-model pins
+SMALL_GQA = inputs.ModelConfig("small-gqa", n_layers=2, d_model=64, n_heads=4, n_kv_heads=2,
+                               head_dim=16, ffn=96, vocab=50)
+
+
+def _dec(w, cfg, max_seq=64):
+    return od.Decoder(w, cfg.n_heads, cfg.n_kv_heads, cfg.rms_eps, cfg.rope_theta, max_seq=max_seq)
+
+
+def test_zero_blocks_reduce_to_lm_head_of_embedding():
+    cfg = SMALL_GQA
+    w = inputs.make_weights(cfg, seed=11)
+    for lw in w["layers"]:
+        lw["wo"][:] = 0
+        lw["w_down"][:] = 0
+    dec = _dec(w, cfg)
+    ids = inputs.make_prompt(cfg, 5, seed=3)
+    lg = dec.prefill(ids)
+    e = w["embed"][ids[-1]].astype(np.float64)
+    want = w["lm_head"].astype(np.float64) @ (e / np.sqrt(np.mean(e * e) + cfg.rms_eps))
+    assert np.max(np.abs(lg - want)) < 1e-12
+    lg2 = dec.step(int(ids[0]), 5)
+    e = w["embed"][ids[0]].astype(np.float64)
+    want = w["lm_head"].astype(np.float64) @ (e / np.sqrt(np.mean(e * e) + cfg.rms_eps))
+    assert np.max(np.abs(lg2 - want)) < 1e-12
+
+
+def test_single_position_attention_passes_rounded_v():
+    # one layer, W_o = I, no MLP: x1 = e + fp16(v) of each query head's kv head
+    cfg = inputs.ModelConfig("p1", n_layers=1, d_model=64, n_heads=4, n_kv_heads=2,
+                             head_dim=16, ffn=32, vocab=40)
+    w = inputs.make_weights(cfg, seed=12)
+    w["layers"][0]["wo"][:] = np.eye(64, dtype=np.float16)
+    w["layers"][0]["w_down"][:] = 0
+    tok = 7
+    lg = _dec(w, cfg).prefill([tok])
+    e = w["embed"][tok].astype(np.float64)
+    h = e / np.sqrt(np.mean(e * e) + cfg.rms_eps)
+    v = w["layers"][0]["wv"].astype(np.float64) @ h
+    v = v.astype(np.float16).astype(np.float64)
+    x1 = e.copy()
+    for j in range(4):            # query heads 0,1 use kv head 0; 2,3 use kv head 1
+        g = j // 2
+        x1[16 * j:16 * (j + 1)] += v[16 * g:16 * (g + 1)]
+    want = w["lm_head"].astype(np.float64) @ (x1 / np.sqrt(np.mean(x1 * x1) + cfg.rms_eps))
+    assert np.max(np.abs(lg - want)) < 1e-12
+
+
+def test_argmax_tie_takes_lowest_index():
+    cfg = SMALL_GQA
+    w = inputs.make_weights(cfg, seed=13)
+    w["lm_head"][:] = 0
+    r = inputs.make_weights(cfg, seed=14)["lm_head"][0]
+    w["lm_head"][2] = r
+    w["lm_head"][5] = r
+    dec = _dec(w, cfg)
+    ids = inputs.make_prompt(cfg, 6, seed=4)
+    t0, toks, logs = dec.greedy(ids, 3)
+    for lg, t in zip(logs, toks):
+        assert lg[2] == lg[5] and lg[2] != 0
+        assert t == (2 if lg[2] > 0 else 0)
+
+
+def test_gqa_equals_mha_with_repeated_kv_heads():
+    cfg = SMALL_GQA
+    w = inputs.make_weights(cfg, seed=15)
+    mha = {k: v for k, v in w.items() if k != "layers"}
+    mha["layers"] = []
+    hd = cfg.head_dim
+    for lw in w["layers"]:
+        m = dict(lw)
+        for key in ("wk", "wv"):
+            rows = [lw[key][hd * (j * cfg.n_kv_heads // cfg.n_heads):][:hd] for j in range(cfg.n_heads)]
+            m[key] = np.concatenate(rows, axis=0)
+        mha["layers"].append(m)
+    ids = inputs.make_prompt(cfg, 9, seed=5)
+    a = _dec(w, cfg).greedy(ids, 4)
+    b = od.Decoder(mha, cfg.n_heads, cfg.n_heads, max_seq=64).greedy(ids, 4)
+    assert a[0] == b[0] and np.array_equal(a[1], b[1])
+    assert np.max(np.abs(a[2] - b[2])) < 1e-12
+
+
+def _compare_with_brute(cfg, seed, P, n, tol, gains="ones"):
+    w = inputs.make_weights(cfg, seed=seed, gains=gains)
+    ids = inputs.make_prompt(cfg, P, seed=seed + 1)
+    dec = _dec(w, cfg, max_seq=P + n + 1)
+    t0, toks, logs = dec.greedy(ids, n)
+    seq = np.concatenate([ids, [t0], toks[:-1]])
+    ref = brute.forward_all(w, seq, cfg.n_heads, cfg.n_kv_heads, cfg.rms_eps, cfg.rope_theta)
+    assert int(np.argmax(ref[P - 1])) == t0
+    err = np.max(np.abs(ref[P:] - logs))
+    assert err < tol, err
+    return dec, ids, t0, toks, logs
+
+
+def test_incremental_decode_matches_full_recompute_tiny():
+    # the tiny decoder: 2 layers, d 256, 4x64 MHA, ffn 688, vocab 1024, P 32, 16 steps
+    _compare_with_brute(inputs.TINY, seed=0, P=32, n=16, tol=1e-9)
+
+
+def test_incremental_decode_matches_full_recompute_gqa_perturbed_gains():
+    _compare_with_brute(SMALL_GQA, seed=21, P=12, n=8, tol=1e-9, gains="perturbed")
+
+
+def test_prefill_plus_decode_equals_longer_prefill():
+    cfg = SMALL_GQA
+    w = inputs.make_weights(cfg, seed=31)
+    ids = inputs.make_prompt(cfg, 10, seed=32)
+    dec = _dec(w, cfg)
+    dec.prefill(ids[:6])
+    for p in range(6, 10):
+        lg = dec.step(int(ids[p]), p)
+    assert np.max(np.abs(lg - _dec(w, cfg).prefill(ids))) < 1e-11
+
+
+def test_top2_margin():
+    assert od.top2_margin(np.array([0.1, 3.0, 2.5, -1.0])) == pytest.approx(0.5)
+    assert od.top2_margin(np.array([[1.0, 1.0, 0.0]]))[0] == 0.0
+
+
+# ---------------------------------------------------------------- chain
+def test_chain_zero_and_scaled_identity():
+    x0 = inputs.make_chain_x0(32)
+    assert np.all(ochain.chain(np.zeros((3, 32, 32), np.float16), x0) == 0.0)
+    W = np.stack([np.eye(32, dtype=np.float16) * np.float16(0.5)] * 6)
+    y = ochain.chain(W, x0)
+    for r in range(32):
+        v = float(x0[r])
+        for i in range(6):
+            v = math.tanh(0.5 * v)
+            assert abs(y[i, r] - v) < 1e-15
+
+
+def test_chain_matches_explicit_loops():
+    W = inputs.make_chain_weights(n=24, stages=5, seed=3, std=0.3)
+    x0 = inputs.make_chain_x0(24, seed=4)
+    assert np.max(np.abs(ochain.chain(W, x0) - brute.chain_loops(W, x0))) < 1e-13
+
+
+# ---------------------------------------------------------------- planted mistakes
+def test_pins_reject_planted_mistakes_in_helpers():
+    bad_rms = [
+        lambda x, g, eps: x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) * g,          # eps dropped
+        lambda x, g, eps: (x - x.mean(-1, keepdims=True)) / np.sqrt(x.var(-1, keepdims=True) + eps) * g,
+        lambda x, g, eps: x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps) * g,     # sum not mean
+    ]
+    for f in bad_rms:
+        assert not check_rmsnorm(f)
+
+    def rope_sign(u, pos, theta):
+        return od.rope_rotate(u, -np.asarray(pos), theta)
+
+    def rope_interleaved(u, pos, theta):
+        hd = u.shape[-1]
+        perm = np.arange(hd).reshape(2, hd // 2).T.reshape(-1)  # (i, i+hd/2) -> (2i, 2i+1)
+        inv = np.argsort(perm)
+        return od.rope_rotate(u[..., perm], pos, theta)[..., inv]
+
+    def rope_exponent(u, pos, theta):
+        return od.rope_rotate(u, pos, theta ** 0.5)
+
+    for f in (rope_sign, rope_interleaved, rope_exponent):
+        assert not check_rope(f)
+
+    def attend_unscaled(q, K, V):
+        return od.softmax(K @ q) @ V
+
+    def attend_no_max(q, K, V):   # wrong normalisation: divides by T instead of the sum
+        e = np.exp(K @ q / np.sqrt(q.shape[-1]))
+        return (e / len(e)) @ V
+
+    for f in (attend_unscaled, attend_no_max):
+        assert not check_attend(f)
+
+    assert not check_silu(lambda z: 1.0 / (1.0 + np.exp(-z)))
+    assert not check_silu(lambda z: z * np.tanh(z))
+
+
+@pytest.mark.parametrize("mistake", ["kv_group_interleaved", "no_kv_rounding", "no_rope_on_k",
+                                     "pos_off_by_one", "silu_scaled"])
+def test_brute_force_rejects_planted_mistakes_in_decoder(monkeypatch, mistake):
+    cfg = SMALL_GQA
+    if mistake == "kv_group_interleaved":
+        monkeypatch.setattr(od.Decoder, "kv_head_of", lambda self, j: j % self.n_kv)
+    elif mistake == "no_kv_rounding":
+        monkeypatch.setattr(od, "fp16_round", lambda x: np.asarray(x, dtype=np.float64))
+    elif mistake == "no_rope_on_k":
+        orig = od.rope_rotate
+        monkeypatch.setattr(od, "rope_rotate",
+                            lambda u, pos, theta: orig(u, pos, theta) if u.shape[-2] == cfg.n_heads else u)
+    elif mistake == "pos_off_by_one":
+        orig = od.rope_rotate
+        monkeypatch.setattr(od, "rope_rotate", lambda u, pos, theta: orig(u, np.asarray(pos) + 1, theta))
+    elif mistake == "silu_scaled":
+        orig = od.silu
+        monkeypatch.setattr(od, "silu", lambda z: orig(z) * 0.5)
+    with pytest.raises(AssertionError):
+        _compare_with_brute(cfg, seed=41, P=8, n=4, tol=1e-9)
