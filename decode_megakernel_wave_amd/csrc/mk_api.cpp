@@ -1,0 +1,867 @@
+// mk_api.cpp -- the C ABI: context lifecycle, weight repacking, launches.
+//
+// The launcher follows the one-wave rule of "8 - Ecrire son megakernel"
+// (section 8.3): set the dynamic LDS size, query how many workgroups fit on a
+// CU, launch exactly CUs x occupancy workgroups and refuse to launch when the
+// kernel does not fit (launching more would deadlock silently).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "../../include/mk.h"
+#include "mk_layout.h"
+#include "mk_plan.h"
+
+using namespace mk;
+
+extern "C" {
+hipError_t mk_launch_monokernel(const KParams* kp_dev, int grid, int lds_bytes, hipStream_t s);
+hipError_t mk_kernel_attributes(int lds_bytes, int* occupancy);
+hipError_t mk_launch_fill32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
+hipError_t mk_launch_fill_kv(uint16_t* kc, uint16_t* vc, int64_t rows, int max_seq, int hd, int p0, int p1, hipStream_t s);
+hipError_t mk_launch_gather(uint16_t* dst, const void* desc, int64_t n_chunks, hipStream_t s);
+hipError_t mk_launch_count32(const uint32_t* p, int64_t n, uint32_t v, unsigned long long* out, hipStream_t s);
+hipError_t mk_launch_count_kv(const uint16_t* kc, const uint16_t* vc, int64_t rows, int max_seq, int hd, int p0, int p1,
+                              unsigned long long* out, hipStream_t s);
+}
+
+namespace {
+
+thread_local std::string g_create_error;
+
+struct GatherDesc {
+  const uint16_t* src;
+  int32_t valid;
+  int32_t pad;
+};
+
+enum State { ST_CREATED = 0, ST_LOADED = 1, ST_READY = 2 };
+
+// Device memory shared by the decoder and the chain.
+struct Engine {
+  int device = 0;
+  hipStream_t stream = nullptr;
+  mk_options opt{};
+  Plan plan;
+  int n_cu = 0, occ = 0, grid = 0;
+  std::string err;
+  // device buffers
+  uint8_t* d_stream = nullptr;
+  Ins* d_ins = nullptr;
+  int32_t* d_ins_off = nullptr;
+  int64_t* d_wave_off = nullptr;
+  int32_t* d_wave_n = nullptr;
+  float* d_arena = nullptr;
+  int64_t arena_words = 0, lmp_word_off = 0;
+  uint32_t* d_counters = nullptr;
+  Fault* d_fault = nullptr;
+  uint32_t* d_abort = nullptr;
+  uint32_t* d_trace = nullptr;
+  uint32_t* d_progress = nullptr;
+  uint64_t* d_dbg = nullptr;
+  int64_t trace_words = 0;
+  int32_t* d_tokens = nullptr;
+  int32_t* d_forced = nullptr;
+  float* d_logits = nullptr;
+  int64_t logits_cap = 0;
+  KParams* d_kp = nullptr;
+  KParams h_kp{};
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  mk_stats last{};
+  std::vector<void*> allocs;
+
+  int fail(int code, const std::string& msg) {
+    err = msg;
+    return code;
+  }
+  int hip_fail(hipError_t e, const char* what) {
+    err = std::string(what) + ": " + hipGetErrorString(e);
+    return MK_EHIP;
+  }
+  template <typename T>
+  int alloc(T** p, size_t bytes) {
+    void* q = nullptr;
+    if (bytes == 0) bytes = 256;
+    hipError_t e = hipMalloc(&q, bytes);
+    if (e != hipSuccess) {
+      err = "hipMalloc of " + std::to_string(bytes) + " bytes failed: " + hipGetErrorString(e);
+      return MK_ENOMEM;
+    }
+    allocs.push_back(q);
+    *p = (T*)q;
+    return MK_OK;
+  }
+  void release() {
+    if (stream) hipStreamSynchronize(stream);
+    for (void* p : allocs) hipFree(p);
+    allocs.clear();
+    if (ev0) hipEventDestroy(ev0);
+    if (ev1) hipEventDestroy(ev1);
+    ev0 = ev1 = nullptr;
+  }
+};
+
+#define HIPCHK(eng, x)                                       \
+  do {                                                       \
+    hipError_t e_ = (x);                                     \
+    if (e_ != hipSuccess) return (eng).hip_fail(e_, #x);     \
+  } while (0)
+#define CHK(x)                 \
+  do {                         \
+    int r_ = (x);              \
+    if (r_ != MK_OK) return r_; \
+  } while (0)
+
+int sanitize_options(const mk_options* in, mk_options* out) {
+  mk_default_options(out);
+  if (in) *out = *in;
+  if (out->sync_mode != MK_SYNC_SENTINEL && out->sync_mode != MK_SYNC_COUNTER) return MK_EINVAL;
+  if (!(out->xcd_replicas == 1 || out->xcd_replicas == 2 || out->xcd_replicas == 4 || out->xcd_replicas == 8)) return MK_EINVAL;
+  if (out->attn_splits < 0 || out->attn_splits > 64) return MK_EINVAL;
+  if (out->trace_steps < 0 || out->watchdog_ms <= 0 || out->grid < 0) return MK_EINVAL;
+  return MK_OK;
+}
+
+// Device, occupancy and grid (the one-wave launch).
+int engine_setup(Engine& g, int device, void* stream, const mk_options* opts, int lds_bytes) {
+  if (sanitize_options(opts, &g.opt) != MK_OK) return g.fail(MK_EINVAL, "invalid options");
+  g.device = device;
+  g.stream = (hipStream_t)stream;
+  int ndev = 0;
+  HIPCHK(g, hipGetDeviceCount(&ndev));
+  if (device < 0 || device >= ndev) return g.fail(MK_EINVAL, "no such device");
+  HIPCHK(g, hipSetDevice(device));
+  hipDeviceProp_t prop;
+  HIPCHK(g, hipGetDeviceProperties(&prop, device));
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return g.fail(MK_EINVAL, std::string("the kernels are built for gfx950, device is ") + prop.gcnArchName);
+  g.n_cu = prop.multiProcessorCount;
+  if (lds_bytes > (int)prop.sharedMemPerBlock) return g.fail(MK_EOCC, "LDS footprint exceeds the per-workgroup limit");
+  HIPCHK(g, mk_kernel_attributes(lds_bytes, &g.occ));
+  if (g.occ < 1) return g.fail(MK_EOCC, "the monokernel does not fit on a CU (occupancy 0)");
+  const int wave = g.n_cu * g.occ;
+  g.grid = g.opt.grid > 0 ? g.opt.grid : wave;
+  if (g.grid > wave) return g.fail(MK_EOCC, "requested grid exceeds CUs x occupancy: workgroups would not all be resident");
+  HIPCHK(g, hipEventCreate(&g.ev0));
+  HIPCHK(g, hipEventCreate(&g.ev1));
+  return MK_OK;
+}
+
+int upload_plan(Engine& g) {
+  const Plan& p = g.plan;
+  CHK(g.alloc(&g.d_ins, p.ins.size() * sizeof(Ins)));
+  CHK(g.alloc(&g.d_ins_off, p.ins_off.size() * sizeof(int32_t)));
+  CHK(g.alloc(&g.d_wave_off, p.wave_off.size() * sizeof(int64_t)));
+  CHK(g.alloc(&g.d_wave_n, p.wave_n.size() * sizeof(int32_t)));
+  CHK(g.alloc(&g.d_stream, (size_t)p.stream_bytes()));
+  HIPCHK(g, hipMemcpy(g.d_ins, p.ins.data(), p.ins.size() * sizeof(Ins), hipMemcpyHostToDevice));
+  HIPCHK(g, hipMemcpy(g.d_ins_off, p.ins_off.data(), p.ins_off.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+  HIPCHK(g, hipMemcpy(g.d_wave_off, p.wave_off.data(), p.wave_off.size() * sizeof(int64_t), hipMemcpyHostToDevice));
+  HIPCHK(g, hipMemcpy(g.d_wave_n, p.wave_n.data(), p.wave_n.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+  CHK(g.alloc(&g.d_counters, std::max(1, p.n_sync) * sizeof(uint32_t)));
+  CHK(g.alloc(&g.d_fault, sizeof(Fault)));
+  CHK(g.alloc(&g.d_abort, sizeof(uint32_t)));
+  CHK(g.alloc(&g.d_kp, sizeof(KParams)));
+  CHK(g.alloc(&g.d_progress, (size_t)g.grid * 4));
+  CHK(g.alloc(&g.d_dbg, (size_t)g.grid * kThreads * 8));
+  if (g.opt.trace_steps > 0) {
+    g.trace_words = (int64_t)g.grid * g.opt.trace_steps * p.max_ins * 8;
+    CHK(g.alloc(&g.d_trace, g.trace_words * 4));
+  }
+  return MK_OK;
+}
+
+// Repack weights: every chunk of every wavefront stream from its source row.
+int repack(Engine& g, const std::vector<const uint16_t*>& mats) {
+  const Plan& p = g.plan;
+  const int64_t n = (int64_t)p.chunks.size();
+  if (n == 0) return MK_OK;
+  std::vector<GatherDesc> desc(n);
+  for (int64_t i = 0; i < n; ++i) {
+    const ChunkSrc& s = p.chunks[i];
+    const int cols = p.mat_cols(s.mat);
+    const uint16_t* base = mats[s.mat];
+    if (!base) return g.fail(MK_EINVAL, "a weight pointer is NULL");
+    desc[i].src = base + (int64_t)s.row * cols + (int64_t)s.cc * kChunkHalfs;
+    desc[i].valid = std::max(0, std::min(kChunkHalfs, cols - s.cc * kChunkHalfs));
+    desc[i].pad = 0;
+  }
+  void* d_desc = nullptr;
+  hipError_t e = hipMalloc(&d_desc, desc.size() * sizeof(GatherDesc));
+  if (e != hipSuccess) return g.fail(MK_ENOMEM, "hipMalloc for the repack table failed");
+  e = hipMemcpyAsync(d_desc, desc.data(), desc.size() * sizeof(GatherDesc), hipMemcpyHostToDevice, g.stream);
+  if (e == hipSuccess) e = mk_launch_gather((uint16_t*)g.d_stream, d_desc, n, g.stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(g.stream);
+  hipFree(d_desc);
+  if (e != hipSuccess) return g.hip_fail(e, "weight repack");
+  return MK_OK;
+}
+
+void fill_common_params(Engine& g, KParams& k) {
+  const Plan& p = g.plan;
+  k.ins = g.d_ins;
+  k.ins_off = g.d_ins_off;
+  k.stream = g.d_stream;
+  k.wave_off = g.d_wave_off;
+  k.wave_n = g.d_wave_n;
+  k.counters = g.d_counters;
+  k.fault = g.d_fault;
+  k.abort_flag = g.d_abort;
+  k.trace = g.d_trace;
+  k.progress = g.d_progress;
+  k.dbg = getenv("MK_DEBUG_ARGMAX") ? g.d_dbg : nullptr;
+  k.trace_steps = g.opt.trace_steps;
+  k.max_ins = p.max_ins;
+  k.S = p.S;
+  k.R = p.R;
+  k.sync_mode = p.sync_mode;
+  k.lm_slots = p.lm_slots;
+  k.watchdog_ticks = (uint64_t)g.opt.watchdog_ms * 100000ull;  // 100 MHz wall clock
+}
+
+// Reset sync state, launch once, wait, collect the fault record.
+int launch(Engine& g, KParams& k, int n_steps) {
+  HIPCHK(g, mk_launch_fill32(g.d_counters, std::max(1, g.plan.n_sync), 0u, g.stream));
+  HIPCHK(g, mk_launch_fill32((uint32_t*)g.d_fault, sizeof(Fault) / 4, 0u, g.stream));
+  HIPCHK(g, mk_launch_fill32(g.d_abort, 1, 0u, g.stream));
+  HIPCHK(g, mk_launch_fill32(g.d_progress, g.grid, 0u, g.stream));
+  if (g.d_trace) HIPCHK(g, mk_launch_fill32(g.d_trace, g.trace_words, 0u, g.stream));
+  g.h_kp = k;
+  HIPCHK(g, hipMemcpyAsync(g.d_kp, &g.h_kp, sizeof(KParams), hipMemcpyHostToDevice, g.stream));
+  HIPCHK(g, hipEventRecord(g.ev0, g.stream));
+  HIPCHK(g, mk_launch_monokernel(g.d_kp, g.grid, g.plan.lds_bytes, g.stream));
+  HIPCHK(g, hipEventRecord(g.ev1, g.stream));
+  HIPCHK(g, hipStreamSynchronize(g.stream));
+  float ms = 0.f;
+  HIPCHK(g, hipEventElapsedTime(&ms, g.ev0, g.ev1));
+  Fault f{};
+  HIPCHK(g, hipMemcpy(&f, g.d_fault, sizeof(Fault), hipMemcpyDeviceToHost));
+  g.last.gpu_ms = ms;
+  g.last.steps = n_steps;
+  g.last.grid = g.grid;
+  g.last.block = kThreads;
+  g.last.lds_bytes = g.plan.lds_bytes;
+  g.last.ring_depth = kRing;
+  g.last.stream_bytes = g.plan.stream_bytes();
+  g.last.weight_bytes = g.plan.weight_bytes;
+  g.last.n_cu = g.n_cu;
+  g.last.occupancy = g.occ;
+  memcpy(&g.last.fault, &f, sizeof(Fault));
+  if (f.code == MK_ETIMEOUT) {
+    char buf[256];
+    snprintf(buf, sizeof buf,
+             "device watchdog: workgroup %d, instruction %d (op %d, layer %d, index %d), step %d waited too long",
+             f.cta, f.pc, f.op, f.layer, f.index, f.step);
+    std::string msg = buf;
+    // where every workgroup stood: the slowest ones first
+    std::vector<uint32_t> prog(g.grid);
+    if (hipMemcpy(prog.data(), g.d_progress, prog.size() * 4, hipMemcpyDeviceToHost) == hipSuccess) {
+      uint32_t lo = UINT32_MAX;
+      for (uint32_t v : prog) lo = std::min(lo, v);
+      int shown = 0;
+      msg += "; least progress (step<<16|pc+1) " + std::to_string(lo) + " at workgroups";
+      for (int i = 0; i < g.grid && shown < 16; ++i)
+        if (prog[i] == lo) {
+          msg += " " + std::to_string(i);
+          ++shown;
+        }
+    }
+    return g.fail(MK_ETIMEOUT, msg);
+  }
+  if (f.code == MK_ENAN) return g.fail(MK_ENAN, "a NaN logit was produced");
+  return MK_OK;
+}
+
+}  // namespace
+
+// ============================================================ decoder context
+struct mk_ctx {
+  Engine g;
+  mk_config cfg{};
+  int state = ST_CREATED;
+  int pos = 0, next_tok = 0;
+  std::vector<int32_t> hist;  // token consumed at each position
+  int last_pos0 = 0, last_n = 0;
+  // model buffers
+  uint16_t* d_embed = nullptr;
+  uint16_t* d_norms = nullptr;
+  float* d_rope = nullptr;
+  uint16_t* d_kc = nullptr;
+  uint16_t* d_vc = nullptr;
+  Buf xa{}, xm{}, q{}, o{}, m{};
+  float* att_o = nullptr;
+  float* att_ml = nullptr;
+  uint64_t* lmp = nullptr;
+  int64_t lmp_es = 0, lmp_rs = 0;
+  int64_t layout[16] = {0};
+  struct Region { int64_t off, words; };
+  std::vector<Region> epoch_regions[3];  // per epoch: word ranges that a step fully writes
+};
+
+namespace {
+
+int ctx_alloc_arena(mk_ctx* c) {
+  Engine& g = c->g;
+  const Plan& p = g.plan;
+  const mk_config& k = c->cfg;
+  const int L = k.n_layers, R = p.R, qd = k.n_heads * k.head_dim, S = p.S;
+  int64_t off = 0;
+  auto take = [&](Buf& b, int n, int reps) {
+    b.rs = reps > 1 ? n : 0;
+    b.ls = (int64_t)n * reps;
+    b.es = b.ls * L;
+    const int64_t o = off;
+    for (int e = 0; e < 3; ++e) c->epoch_regions[e].push_back({o + e * b.es, b.es});
+    off += ((3 * b.es + 63) / 64) * 64;
+    return o;
+  };
+  const int64_t oxa = take(c->xa, k.d_model, R);
+  const int64_t oxm = take(c->xm, k.d_model, R);
+  const int64_t oq = take(c->q, qd, 1);
+  const int64_t oo = take(c->o, qd, R);
+  const int64_t om = take(c->m, k.ffn, R);
+  const int64_t att_es = (int64_t)L * k.n_heads * S * k.head_dim;
+  const int64_t oao = off;
+  for (int e = 0; e < 3; ++e) c->epoch_regions[e].push_back({oao + e * att_es, att_es});
+  off += ((3 * att_es + 63) / 64) * 64;
+  const int64_t ml_es = (int64_t)L * k.n_heads * S * 2;
+  const int64_t oml = off;
+  for (int e = 0; e < 3; ++e) c->epoch_regions[e].push_back({oml + e * ml_es, ml_es});
+  off += ((3 * ml_es + 63) / 64) * 64;
+  g.lmp_word_off = off;
+  c->lmp_rs = p.lm_slots;
+  c->lmp_es = (int64_t)p.lm_slots * R;
+  off += ((3 * c->lmp_es * 2 + 63) / 64) * 64;
+  g.arena_words = off;
+  const int64_t lay[9] = {oxa, oxm, oq, oo, om, oao, oml, g.lmp_word_off, off};
+  for (int i = 0; i < 9; ++i) c->layout[i] = lay[i];
+  CHK(g.alloc(&g.d_arena, off * 4));
+  float* a = g.d_arena;
+  c->xa.p = a + oxa;
+  c->xm.p = a + oxm;
+  c->q.p = a + oq;
+  c->o.p = a + oo;
+  c->m.p = a + om;
+  c->att_o = a + oao;
+  c->att_ml = a + oml;
+  c->lmp = (uint64_t*)(a + g.lmp_word_off);
+  return MK_OK;
+}
+
+int ctx_run(mk_ctx* c, int n, int first_token, const int32_t* forced, int32_t* tokens_out, float* logits_out) {
+  Engine& g = c->g;
+  const mk_config& k = c->cfg;
+  const int pos0 = c->pos;
+  if (n < 1) return g.fail(MK_EINVAL, "n_steps must be at least 1");
+  if ((int64_t)pos0 + n > k.max_seq) return g.fail(MK_ERANGE, "decode would run past max_seq");
+  HIPCHK(g, hipSetDevice(g.device));
+  if (forced) {
+    for (int i = 0; i < n; ++i)
+      if (forced[i] < 0 || forced[i] >= k.vocab) return g.fail(MK_ERANGE, "token id outside [0, vocab)");
+    HIPCHK(g, hipMemcpyAsync(g.d_forced, forced, n * sizeof(int32_t), hipMemcpyHostToDevice, g.stream));
+  }
+  if (logits_out && (int64_t)n * k.vocab > g.logits_cap) {
+    if (g.d_logits) {
+      HIPCHK(g, hipStreamSynchronize(g.stream));
+      hipFree(g.d_logits);
+      g.allocs.erase(std::remove(g.allocs.begin(), g.allocs.end(), (void*)g.d_logits), g.allocs.end());
+      g.d_logits = nullptr;
+    }
+    CHK(g.alloc(&g.d_logits, (size_t)n * k.vocab * 4));
+    g.logits_cap = (int64_t)n * k.vocab;
+  }
+  // re-arm every sync buffer and the KV positions this launch writes
+  HIPCHK(g, mk_launch_fill32((uint32_t*)g.d_arena, g.lmp_word_off, kSent32, g.stream));
+  HIPCHK(g, mk_launch_fill32((uint32_t*)g.d_arena + g.lmp_word_off, g.arena_words - g.lmp_word_off, 0u, g.stream));
+  HIPCHK(g, mk_launch_fill_kv(c->d_kc, c->d_vc, (int64_t)k.n_layers * k.n_kv_heads, k.max_seq, k.head_dim, pos0, pos0 + n,
+                              g.stream));
+  KParams kp{};
+  fill_common_params(g, kp);
+  kp.n_steps = n;
+  kp.pos0 = pos0;
+  kp.first_token = first_token;
+  kp.chain = 0;
+  kp.forced = forced ? g.d_forced : nullptr;
+  kp.tokens = g.d_tokens;
+  kp.logits = logits_out ? g.d_logits : nullptr;
+  kp.embed = c->d_embed;
+  kp.norms = c->d_norms;
+  kp.rope = c->d_rope;
+  kp.kc = c->d_kc;
+  kp.vc = c->d_vc;
+  kp.xa = c->xa;
+  kp.xm = c->xm;
+  kp.q = c->q;
+  kp.o = c->o;
+  kp.m = c->m;
+  kp.att_o = c->att_o;
+  kp.att_ml = c->att_ml;
+  kp.lmp = c->lmp;
+  kp.lmp_es = c->lmp_es;
+  kp.lmp_rs = c->lmp_rs;
+  kp.L = k.n_layers;
+  kp.d = k.d_model;
+  kp.nq = k.n_heads;
+  kp.nkv = k.n_kv_heads;
+  kp.hd = k.head_dim;
+  kp.f = k.ffn;
+  kp.V = k.vocab;
+  kp.max_seq = k.max_seq;
+  kp.eps = k.rms_eps;
+  kp.vec_floats = (g.plan.lds_bytes - lds_bytes_for(0)) / 4;
+  c->last_pos0 = pos0;
+  c->last_n = n;
+  int rc = launch(g, kp, n);
+  // algorithmic bytes: weights + one embedding row + K/V of positions 0..pos per step
+  const int64_t kv_pos = 2LL * k.n_layers * k.n_kv_heads * k.head_dim * 2;
+  int64_t bytes = 0;
+  for (int s = 0; s < n; ++s) bytes += g.plan.weight_bytes + 2LL * k.d_model + kv_pos * (pos0 + s + 1);
+  g.last.algo_bytes = bytes;
+  g.last.kv_bytes_per_pos = kv_pos;
+  g.last.pos0 = pos0;
+  if (rc != MK_OK && rc != MK_ENAN) return rc;
+  HIPCHK(g, hipMemcpy(tokens_out, g.d_tokens, n * sizeof(int32_t), hipMemcpyDeviceToHost));
+  if (logits_out) HIPCHK(g, hipMemcpy(logits_out, g.d_logits, (size_t)n * k.vocab * 4, hipMemcpyDeviceToHost));
+  return rc;
+}
+
+void advance(mk_ctx* c, int n, const int32_t* consumed_first, const int32_t* forced, const int32_t* toks) {
+  c->hist.resize(c->pos);
+  for (int s = 0; s < n; ++s) c->hist.push_back(forced ? forced[s] : (s == 0 ? *consumed_first : toks[s - 1]));
+  c->pos += n;
+  c->next_tok = toks[n - 1];
+}
+
+}  // namespace
+
+extern "C" {
+
+int mk_default_options(mk_options* o) {
+  if (!o) return MK_EINVAL;
+  o->sync_mode = MK_SYNC_SENTINEL;
+  o->xcd_replicas = 8;
+  o->attn_splits = 0;
+  o->trace_steps = 0;
+  o->watchdog_ms = 2000;
+  o->grid = 0;
+  return MK_OK;
+}
+
+static mk::Dims dims_of(const mk_config* cfg) {
+  mk::Dims d;
+  d.L = cfg->n_layers;
+  d.d = cfg->d_model;
+  d.nq = cfg->n_heads;
+  d.nkv = cfg->n_kv_heads;
+  d.hd = cfg->head_dim;
+  d.f = cfg->ffn;
+  d.V = cfg->vocab;
+  d.max_seq = cfg->max_seq;
+  return d;
+}
+
+int mk_plan_check(const mk_config* cfg, const mk_options* opts, int32_t n_cta, mk_plan_info* info, const char** msg) {
+  static thread_local std::string m;
+  mk_options o;
+  if (msg) *msg = "";
+  if (!cfg || sanitize_options(opts, &o) != MK_OK) {
+    m = "invalid options";
+    if (msg) *msg = m.c_str();
+    return MK_EINVAL;
+  }
+  Plan p;
+  m = build_plan(dims_of(cfg), n_cta, o.attn_splits, o.xcd_replicas, o.sync_mode, &p);
+  if (!m.empty()) {
+    if (msg) *msg = m.c_str();
+    return MK_EINVAL;
+  }
+  if (info) {
+    info->n_cta = p.n_cta;
+    info->max_ins_per_cta = p.max_ins;
+    info->n_sync_ids = p.n_sync;
+    info->lds_bytes = p.lds_bytes;
+    info->stream_chunks = (int64_t)p.chunks.size();
+    info->stream_bytes = p.stream_bytes();
+    info->weight_bytes = p.weight_bytes;
+    int mn = INT32_MAX, mx = 0;
+    for (int32_t v : p.wave_n) {
+      mn = std::min(mn, v);
+      mx = std::max(mx, v);
+    }
+    info->min_wave_chunks = mn;
+    info->max_wave_chunks = mx;
+    info->attn_splits = p.S;
+  }
+  return MK_OK;
+}
+
+int mk_create(const mk_config* cfg, const mk_options* opts, int device, void* hip_stream, mk_ctx** out) {
+  g_create_error.clear();
+  if (!cfg || !out) {
+    g_create_error = "NULL argument";
+    return MK_EINVAL;
+  }
+  *out = nullptr;
+  mk_ctx* c = new mk_ctx();
+  c->cfg = *cfg;
+  Engine& g = c->g;
+  auto bail = [&](int rc) {
+    g_create_error = g.err.empty() ? "mk_create failed" : g.err;
+    g.release();
+    delete c;
+    return rc;
+  };
+  mk_options o;
+  if (sanitize_options(opts, &o) != MK_OK) {
+    g.err = "invalid options";
+    return bail(MK_EINVAL);
+  }
+  // the grid depends on the occupancy, which depends on the LDS size: size it first
+  Plan probe;
+  std::string msg = build_plan(dims_of(cfg), 1, o.attn_splits > 0 ? o.attn_splits : 1, o.xcd_replicas, o.sync_mode, &probe);
+  if (!msg.empty()) {
+    g.err = msg;
+    return bail(MK_EINVAL);
+  }
+  int rc = engine_setup(g, device, hip_stream, &o, probe.lds_bytes);
+  if (rc != MK_OK) return bail(rc);
+  msg = build_plan(dims_of(cfg), g.grid, o.attn_splits, o.xcd_replicas, o.sync_mode, &g.plan);
+  if (!msg.empty()) {
+    g.err = msg;
+    return bail(MK_EINVAL);
+  }
+  if ((rc = upload_plan(g)) != MK_OK) return bail(rc);
+  const mk_config& k = *cfg;
+  const int64_t kv_words = (int64_t)k.n_layers * k.n_kv_heads * k.max_seq * k.head_dim;
+  if ((rc = g.alloc(&c->d_kc, kv_words * 2)) != MK_OK) return bail(rc);
+  if ((rc = g.alloc(&c->d_vc, kv_words * 2)) != MK_OK) return bail(rc);
+  if ((rc = g.alloc(&c->d_embed, (size_t)k.vocab * k.d_model * 2)) != MK_OK) return bail(rc);
+  if ((rc = g.alloc(&c->d_norms, (size_t)(2 * k.n_layers + 1) * k.d_model * 2)) != MK_OK) return bail(rc);
+  if ((rc = g.alloc(&c->d_rope, (size_t)k.max_seq * k.head_dim * 4)) != MK_OK) return bail(rc);
+  if ((rc = g.alloc(&g.d_tokens, (size_t)k.max_seq * 4)) != MK_OK) return bail(rc);
+  if ((rc = g.alloc(&g.d_forced, (size_t)k.max_seq * 4)) != MK_OK) return bail(rc);
+  if ((rc = ctx_alloc_arena(c)) != MK_OK) return bail(rc);
+  // RoPE table: cos/sin of pos * theta^(-2i/hd), computed in double
+  {
+    const int hh = k.head_dim / 2;
+    std::vector<float> t((size_t)k.max_seq * hh * 2);
+    for (int p = 0; p < k.max_seq; ++p)
+      for (int i = 0; i < hh; ++i) {
+        const double w = pow((double)k.rope_theta, -2.0 * i / k.head_dim);
+        const double a = (double)p * w;
+        t[((size_t)p * hh + i) * 2] = (float)cos(a);
+        t[((size_t)p * hh + i) * 2 + 1] = (float)sin(a);
+      }
+    hipError_t e = hipMemcpy(c->d_rope, t.data(), t.size() * 4, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      g.hip_fail(e, "rope upload");
+      return bail(MK_EHIP);
+    }
+  }
+  *out = c;
+  return MK_OK;
+}
+
+int mk_load_weights(mk_ctx* c, const mk_weights* w) {
+  if (!c || !w) return MK_EINVAL;
+  Engine& g = c->g;
+  const mk_config& k = c->cfg;
+  const int L = k.n_layers;
+  if (!w->embed || !w->final_norm || !w->lm_head || !w->attn_norm || !w->wq || !w->wk || !w->wv || !w->wo ||
+      !w->mlp_norm || !w->w_gate || !w->w_up || !w->w_down)
+    return g.fail(MK_EINVAL, "a weight pointer is NULL");
+  HIPCHK(g, hipSetDevice(g.device));
+  std::vector<const uint16_t*> mats(7 * L + 1, nullptr);
+  for (int l = 0; l < L; ++l) {
+    mats[7 * l + MQ] = (const uint16_t*)w->wq[l];
+    mats[7 * l + MK] = (const uint16_t*)w->wk[l];
+    mats[7 * l + MV] = (const uint16_t*)w->wv[l];
+    mats[7 * l + MO] = (const uint16_t*)w->wo[l];
+    mats[7 * l + MG] = (const uint16_t*)w->w_gate[l];
+    mats[7 * l + MU] = (const uint16_t*)w->w_up[l];
+    mats[7 * l + MD] = (const uint16_t*)w->w_down[l];
+  }
+  mats[7 * L] = (const uint16_t*)w->lm_head;
+  CHK(repack(g, mats));
+  const size_t drow = (size_t)k.d_model * 2;
+  HIPCHK(g, hipMemcpyAsync(c->d_embed, w->embed, (size_t)k.vocab * drow, hipMemcpyDeviceToDevice, g.stream));
+  for (int l = 0; l < L; ++l) {
+    if (!w->attn_norm[l] || !w->mlp_norm[l]) return g.fail(MK_EINVAL, "a norm pointer is NULL");
+    HIPCHK(g, hipMemcpyAsync((uint8_t*)c->d_norms + (2 * l) * drow, w->attn_norm[l], drow, hipMemcpyDeviceToDevice, g.stream));
+    HIPCHK(g, hipMemcpyAsync((uint8_t*)c->d_norms + (2 * l + 1) * drow, w->mlp_norm[l], drow, hipMemcpyDeviceToDevice, g.stream));
+  }
+  HIPCHK(g, hipMemcpyAsync((uint8_t*)c->d_norms + 2 * L * drow, w->final_norm, drow, hipMemcpyDeviceToDevice, g.stream));
+  HIPCHK(g, hipStreamSynchronize(g.stream));
+  c->state = ST_LOADED;
+  c->pos = 0;
+  c->hist.clear();
+  return MK_OK;
+}
+
+int mk_prefill(mk_ctx* c, const int32_t* ids, int32_t n, int32_t* t0_out) {
+  if (!c || !ids || !t0_out) return MK_EINVAL;
+  if (c->state < ST_LOADED) return c->g.fail(MK_ESTATE, "prefill before mk_load_weights");
+  if (n < 1) return c->g.fail(MK_EINVAL, "empty prompt");
+  if (n > c->cfg.max_seq) return c->g.fail(MK_ERANGE, "prompt longer than max_seq");
+  c->pos = 0;
+  c->hist.clear();
+  std::vector<int32_t> toks(n);
+  int rc = ctx_run(c, n, 0, ids, toks.data(), nullptr);
+  if (rc != MK_OK) {
+    c->state = ST_LOADED;
+    return rc;
+  }
+  advance(c, n, nullptr, ids, toks.data());
+  *t0_out = toks[n - 1];
+  c->state = ST_READY;
+  return MK_OK;
+}
+
+int mk_decode(mk_ctx* c, int32_t n, int32_t* tokens_out, float* logits_out) {
+  if (!c || !tokens_out) return MK_EINVAL;
+  if (c->state < ST_READY) return c->g.fail(MK_ESTATE, "decode before prefill");
+  const int first = c->next_tok;
+  int rc = ctx_run(c, n, first, nullptr, tokens_out, logits_out);
+  if (rc != MK_OK) {
+    if (rc == MK_ETIMEOUT) c->state = ST_LOADED;
+    return rc;
+  }
+  advance(c, n, &first, nullptr, tokens_out);
+  return MK_OK;
+}
+
+int mk_decode_forced(mk_ctx* c, int32_t n, const int32_t* tokens_in, int32_t* tokens_out, float* logits_out) {
+  if (!c || !tokens_in || !tokens_out) return MK_EINVAL;
+  if (c->state < ST_READY) return c->g.fail(MK_ESTATE, "decode before prefill");
+  int rc = ctx_run(c, n, 0, tokens_in, tokens_out, logits_out);
+  if (rc != MK_OK) {
+    if (rc == MK_ETIMEOUT) c->state = ST_LOADED;
+    return rc;
+  }
+  advance(c, n, nullptr, tokens_in, tokens_out);
+  return MK_OK;
+}
+
+int mk_generate(mk_ctx* c, const int32_t* ids, int32_t n_prompt, int32_t n_steps, int32_t* tokens_out) {
+  if (!c || !tokens_out) return MK_EINVAL;
+  int rc = mk_prefill(c, ids, n_prompt, tokens_out);
+  if (rc != MK_OK || n_steps == 0) return rc;
+  return mk_decode(c, n_steps, tokens_out + 1, nullptr);
+}
+
+int mk_rewind(mk_ctx* c, int32_t pos) {
+  if (!c) return MK_EINVAL;
+  if (c->state < ST_READY) return c->g.fail(MK_ESTATE, "rewind before prefill");
+  if (pos < 1 || pos > c->pos) return c->g.fail(MK_ERANGE, "rewind position outside [1, current]");
+  if (pos == c->pos) return MK_OK;
+  c->next_tok = c->hist[pos];
+  c->pos = pos;
+  c->hist.resize(pos);
+  return MK_OK;
+}
+
+int mk_position(const mk_ctx* c, int32_t* pos, int32_t* next_token) {
+  if (!c) return MK_EINVAL;
+  if (pos) *pos = c->pos;
+  if (next_token) *next_token = c->next_tok;
+  return MK_OK;
+}
+
+int mk_get_stats(const mk_ctx* c, mk_stats* out) {
+  if (!c || !out) return MK_EINVAL;
+  *out = c->g.last;
+  return MK_OK;
+}
+
+int mk_count_sentinels(mk_ctx* c, int64_t* count) {
+  if (!c || !count) return MK_EINVAL;
+  Engine& g = c->g;
+  if (c->last_n < 1) return g.fail(MK_ESTATE, "no launch yet");
+  HIPCHK(g, hipSetDevice(g.device));
+  unsigned long long* d = nullptr;
+  HIPCHK(g, hipMalloc(&d, 8));
+  hipError_t e = hipMemsetAsync(d, 0, 8, g.stream);
+  const int el = (c->last_n - 1) % 3;
+  for (const auto& r : c->epoch_regions[el])
+    if (e == hipSuccess) e = mk_launch_count32((const uint32_t*)g.d_arena + r.off, r.words, kSent32, d, g.stream);
+  const mk_config& k = c->cfg;
+  if (e == hipSuccess)
+    e = mk_launch_count_kv(c->d_kc, c->d_vc, (int64_t)k.n_layers * k.n_kv_heads, k.max_seq, k.head_dim, c->last_pos0,
+                           c->last_pos0 + c->last_n, d, g.stream);
+  unsigned long long h = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&h, d, 8, hipMemcpyDeviceToHost, g.stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(g.stream);
+  // argmax keys of the last step (sentinel 0)
+  std::vector<uint64_t> keys(c->lmp_es);
+  if (e == hipSuccess)
+    e = hipMemcpy(keys.data(), c->lmp + el * c->lmp_es, keys.size() * 8, hipMemcpyDeviceToHost);
+  hipFree(d);
+  if (e != hipSuccess) return g.hip_fail(e, "sentinel count");
+  for (uint64_t v : keys) h += v == kSent64;
+  *count = (int64_t)h;
+  return MK_OK;
+}
+
+int mk_read_trace(mk_ctx* c, uint32_t* host_buf, int64_t capacity, int64_t* n_records) {
+  if (!c || !n_records) return MK_EINVAL;
+  Engine& g = c->g;
+  *n_records = g.trace_words / 8;
+  if (!host_buf) return MK_OK;
+  if (capacity < *n_records) return g.fail(MK_EINVAL, "trace buffer too small");
+  if (g.trace_words) HIPCHK(g, hipMemcpy(host_buf, g.d_trace, g.trace_words * 4, hipMemcpyDeviceToHost));
+  return MK_OK;
+}
+
+int mk_debug_layout(const mk_ctx* c, int64_t* offsets) {
+  if (!c || !offsets) return MK_EINVAL;
+  for (int i = 0; i < 16; ++i) offsets[i] = c->layout[i];
+  return MK_OK;
+}
+
+int mk_debug_arena(mk_ctx* c, int64_t word_off, int64_t n_words, uint32_t* host) {
+  if (!c || !host || word_off < 0 || n_words < 0 || word_off + n_words > c->g.arena_words) return MK_EINVAL;
+  HIPCHK(c->g, hipMemcpy(host, (uint32_t*)c->g.d_arena + word_off, n_words * 4, hipMemcpyDeviceToHost));
+  return MK_OK;
+}
+
+int mk_debug_progress(mk_ctx* c, uint32_t* host, int32_t capacity) {
+  if (!c || !host || capacity < c->g.grid) return MK_EINVAL;
+  HIPCHK(c->g, hipMemcpy(host, c->g.d_progress, (size_t)c->g.grid * 4, hipMemcpyDeviceToHost));
+  return MK_OK;
+}
+
+int mk_debug_argmax_reads(mk_ctx* c, uint64_t* host, int64_t capacity) {
+  if (!c || !host || capacity < (int64_t)c->g.grid * kThreads) return MK_EINVAL;
+  HIPCHK(c->g, hipMemcpy(host, c->g.d_dbg, (size_t)c->g.grid * kThreads * 8, hipMemcpyDeviceToHost));
+  return MK_OK;
+}
+
+const char* mk_last_error(const mk_ctx* c) {
+  if (!c) return g_create_error.c_str();
+  return c->g.err.c_str();
+}
+
+void mk_destroy(mk_ctx* c) {
+  if (!c) return;
+  hipSetDevice(c->g.device);
+  c->g.release();
+  delete c;
+}
+
+}  // extern "C"
+
+// ============================================================ chain microbenchmark
+struct mk_chain {
+  Engine g;
+  int n = 0, stages = 0;
+  Buf y{};
+};
+
+extern "C" {
+
+int mk_chain_create(int32_t n, int32_t stages, const void* W, const mk_options* opts, int device, void* hip_stream,
+                    mk_chain** out) {
+  g_create_error.clear();
+  if (!out || !W) {
+    g_create_error = "NULL argument";
+    return MK_EINVAL;
+  }
+  *out = nullptr;
+  mk_chain* ch = new mk_chain();
+  Engine& g = ch->g;
+  auto bail = [&](int rc) {
+    g_create_error = g.err.empty() ? "mk_chain_create failed" : g.err;
+    g.release();
+    delete ch;
+    return rc;
+  };
+  mk_options o;
+  if (sanitize_options(opts, &o) != MK_OK) {
+    g.err = "invalid options";
+    return bail(MK_EINVAL);
+  }
+  mk::Dims dm;
+  dm.chain = true;
+  dm.chain_n = n;
+  dm.chain_stages = stages;
+  Plan probe;
+  std::string msg = build_plan(dm, 1, 1, o.xcd_replicas, o.sync_mode, &probe);
+  if (!msg.empty()) {
+    g.err = msg;
+    return bail(MK_EINVAL);
+  }
+  int rc = engine_setup(g, device, hip_stream, &o, probe.lds_bytes);
+  if (rc != MK_OK) return bail(rc);
+  msg = build_plan(dm, g.grid, 1, o.xcd_replicas, o.sync_mode, &g.plan);
+  if (!msg.empty()) {
+    g.err = msg;
+    return bail(MK_EINVAL);
+  }
+  if ((rc = upload_plan(g)) != MK_OK) return bail(rc);
+  ch->n = n;
+  ch->stages = stages;
+  const int R = g.plan.R;
+  ch->y.rs = R > 1 ? n : 0;
+  ch->y.ls = (int64_t)n * R;
+  ch->y.es = 0;
+  g.arena_words = ch->y.ls * stages;
+  g.lmp_word_off = g.arena_words;
+  if ((rc = g.alloc(&g.d_arena, g.arena_words * 4)) != MK_OK) return bail(rc);
+  if ((rc = g.alloc(&g.d_tokens, 64)) != MK_OK) return bail(rc);
+  ch->y.p = g.d_arena;
+  std::vector<const uint16_t*> mats(stages);
+  for (int i = 0; i < stages; ++i) mats[i] = (const uint16_t*)W + (int64_t)i * n * n;
+  if ((rc = repack(g, mats)) != MK_OK) return bail(rc);
+  *out = ch;
+  return MK_OK;
+}
+
+int mk_chain_run(mk_chain* ch, const float* x0, float* y) {
+  if (!ch || !x0 || !y) return MK_EINVAL;
+  Engine& g = ch->g;
+  HIPCHK(g, hipSetDevice(g.device));
+  HIPCHK(g, mk_launch_fill32((uint32_t*)g.d_arena, g.arena_words, kSent32, g.stream));
+  KParams kp{};
+  fill_common_params(g, kp);
+  kp.n_steps = 1;
+  kp.chain = 1;
+  kp.tokens = g.d_tokens;
+  kp.y = ch->y;
+  kp.x0 = x0;
+  kp.chain_n = ch->n;
+  kp.L = ch->stages;
+  kp.vec_floats = (g.plan.lds_bytes - lds_bytes_for(0)) / 4;
+  int rc = launch(g, kp, 1);
+  g.last.algo_bytes = g.plan.weight_bytes;
+  if (rc != MK_OK) return rc;
+  // y[i] = replica 0 of stage i
+  HIPCHK(g, hipMemcpy2DAsync(y, (size_t)ch->n * 4, ch->y.p, (size_t)ch->y.ls * 4, (size_t)ch->n * 4, ch->stages,
+                             hipMemcpyDeviceToDevice, g.stream));
+  HIPCHK(g, hipStreamSynchronize(g.stream));
+  return MK_OK;
+}
+
+int mk_chain_stats(const mk_chain* ch, mk_stats* out) {
+  if (!ch || !out) return MK_EINVAL;
+  *out = ch->g.last;
+  return MK_OK;
+}
+
+const char* mk_chain_last_error(const mk_chain* ch) {
+  if (!ch) return g_create_error.c_str();
+  return ch->g.err.c_str();
+}
+
+void mk_chain_destroy(mk_chain* ch) {
+  if (!ch) return;
+  hipSetDevice(ch->g.device);
+  ch->g.release();
+  delete ch;
+}
+
+}  // extern "C"

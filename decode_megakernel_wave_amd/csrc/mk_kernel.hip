@@ -1,0 +1,1045 @@
+// mk_kernel.hip -- the persistent decode monokernel for gfx950 (MI355X).
+//
+// One launch runs n decode steps.  Every workgroup (one per CU, sized by the
+// occupancy query: "8 - Ecrire son megakernel", section 8.3) walks its own
+// instruction list once per step ("8 - Ecrire son megakernel", section 8.2):
+// fused RMSNorm+QKV+RoPE, split attention, the split merge, O-projection,
+// gate/up, down projection, LM head and the greedy argmax.
+//
+// Synchronisation ("7 - AMD et le monokernel", section 7.3): every output
+// buffer starts out holding a sentinel NaN bit pattern; producers overwrite
+// it with agent-coherent stores and consumers poll each element they read
+// with agent-coherent (L2-bypassing) loads until it is no longer the
+// sentinel.  No counter, no fence per stage.  Each element is checked, which
+// is the rule the page gives for writes that are not ordered among
+// themselves.  Buffers rotate over three step epochs; the producer of an
+// element re-arms it for the step after next.  One release fence per step
+// (before the per-workgroup argmax key) orders the re-arms and KV writes.
+// The atomic-counter protocol ("8 - Ecrire son megakernel", section 8.5:
+// release fence, counter increment; acquire poll with back-off) is kept as
+// a selectable comparison path on the same buffers.
+//
+// Weight streaming ("7 - AMD et le monokernel", section 7.5): each
+// wavefront owns one contiguous stream of 1 KB chunks (built by the host in
+// exactly the order the wavefront consumes them) and keeps kRing chunks in
+// flight with nontemporal global->LDS loads, refilling a ring slot as soon as
+// it has been read.  The ring runs across stage and step boundaries, so the
+// next stage's weights are already arriving while the wavefront waits for
+// its inputs.  GEMVs are fp16 x fp32 with fp32 accumulation and wavefront
+// DPP reductions; no matrix cores are needed at batch 1.
+//
+// Per-XCD copies ("7 - AMD et le monokernel", section 7.4): vectors that
+// every workgroup re-reads (residual stream, attention output, MLP
+// activation, argmax keys) are written R times; a workgroup reads the copy
+// of its own XCD.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mk_layout.h"
+
+using namespace mk;
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned u4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- memory helpers
+// Cross-workgroup traffic (sentinel polls, published outputs, counters) uses
+// system-scope atomics, which gfx950 encodes with both cache-policy bits
+// (sc0 sc1): the access bypasses the CU's L1 and the XCD's L2 and goes to the
+// memory-side coherence point.  This is the HIP counterpart of the uncached
+// read the sentinel needs ("7 - AMD et le monokernel", section 7.3): a poll
+// must never be answered from a cached copy.  Agent-scope (sc1 only) loads were
+// measured to keep returning a stale line on another XCD.
+#define MK_SCOPE __HIP_MEMORY_SCOPE_SYSTEM
+__device__ __forceinline__ uint32_t ldc32(const void* p) {
+  return __hip_atomic_load((const uint32_t*)p, __ATOMIC_RELAXED, MK_SCOPE);
+}
+__device__ __forceinline__ uint16_t ldc16(const void* p) {
+  return __hip_atomic_load((const uint16_t*)p, __ATOMIC_RELAXED, MK_SCOPE);
+}
+__device__ __forceinline__ uint64_t ldc64(const void* p) {
+  return __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, MK_SCOPE);
+}
+__device__ __forceinline__ void stc32(void* p, uint32_t v) {
+  __hip_atomic_store((uint32_t*)p, v, __ATOMIC_RELAXED, MK_SCOPE);
+}
+__device__ __forceinline__ void stc16(void* p, uint16_t v) {
+  __hip_atomic_store((uint16_t*)p, v, __ATOMIC_RELAXED, MK_SCOPE);
+}
+__device__ __forceinline__ void stc64(void* p, uint64_t v) {
+  __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, MK_SCOPE);
+}
+__device__ __forceinline__ void stcf(float* p, float v) { stc32(p, __float_as_uint(v)); }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  uint64_t v = (uint64_t)p;
+  uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
+}
+
+// Workgroup barrier that waits for LDS traffic only (HIP's __syncthreads
+// would also drain every outstanding global load, emptying the weight ring).
+__device__ __forceinline__ void cta_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ int xcc_id() {
+  int x;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+  return x & 15;
+}
+
+// ---------------------------------------------------------------- wavefront reductions (DPP)
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xF, false));
+}
+// Sum over the 64 lanes; the result is uniform.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp<0xB1>(v);         // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);         // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);        // row_half_mirror
+  v += dpp<0x140>(v);        // row_mirror: every lane holds its 16-lane row sum
+  v += dpp<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v += dpp<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 1));
+  v = fmaxf(v, __shfl_xor(v, 2));
+  v = fmaxf(v, __shfl_xor(v, 4));
+  v = fmaxf(v, __shfl_xor(v, 8));
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
+// ---------------------------------------------------------------- weight ring
+struct Ring {
+  uint32_t lds;          // LDS byte address of this wavefront's ring
+  const uint8_t* g;      // stream base
+  uint32_t n;            // chunks per step
+  uint32_t issue;        // next chunk (mod n) to request
+  uint32_t slot;         // ring slot holding the next chunk to consume
+};
+
+__device__ __forceinline__ void dma_chunk(uint32_t lds_addr, const uint8_t* g, uint32_t voff) {
+  uint32_t save;
+  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
+  g = (const uint8_t*)uniform_ptr(g);
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, %3 nt\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds_addr), "v"(voff), "s"(g)
+      : "memory");
+}
+
+__device__ __forceinline__ void ring_start(Ring& r) {
+  if (r.n == 0) return;
+  const uint32_t lane16 = lane_id() * 16;
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) {
+    dma_chunk(r.lds + i * 1024, r.g, r.issue * 1024 + lane16);
+    r.issue = (r.issue + 1 == r.n) ? 0 : r.issue + 1;
+  }
+  r.slot = 0;
+}
+
+// Next chunk of this wavefront's stream (16 bytes per lane), then refill its slot.
+typedef __attribute__((address_space(3))) const u4* lds_u4_ptr;
+__device__ __forceinline__ u4 ring_next(Ring& r) {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kRing - 1) : "memory");
+  const u4 v = *(lds_u4_ptr)(uintptr_t)(r.lds + r.slot * 1024 + lane_id() * 16);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  dma_chunk(r.lds + r.slot * 1024, r.g, r.issue * 1024 + lane_id() * 16);
+  r.issue = (r.issue + 1 == r.n) ? 0 : r.issue + 1;
+  r.slot = (r.slot + 1 == kRing) ? 0 : r.slot + 1;
+  return v;
+}
+
+__device__ __forceinline__ float dot8(u4 w, const float* a) {
+  const h8 h = __builtin_bit_cast(h8, w);
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s = fmaf((float)h[e], a[e], s);
+  return s;
+}
+
+// ---------------------------------------------------------------- per-workgroup context
+struct Smem {
+  uint8_t* base;
+  float* vec;        // staged input vector [kpad]
+  float* scratch;    // [kScratchFloats]
+  float* resid;      // [1024]
+  uint32_t* flags;   // [2][kWaves] failure flags
+  float* wsum;       // [kWaves] partial sums of squares
+  uint64_t* keys;    // [kWaves]
+  uint32_t* misc;    // [16]
+};
+
+struct Cx {
+  const KParams* kp;
+  Smem sm;
+  int cta, wave, lane, tid, rep, xcc;
+  int step, pos, e, e1, tok, pc;
+  int flag_parity;
+  bool fail;          // this thread saw a timeout or abort
+  uint64_t deadline;
+  int poll_iters;
+};
+
+__device__ __forceinline__ void raise_fault(Cx& c, int code, int op, int layer, int index) {
+  const KParams& kp = *c.kp;
+  if (atomicCAS((unsigned*)&kp.fault->code, 0u, (unsigned)code) == 0u) {
+    kp.fault->cta = c.cta;
+    kp.fault->pc = c.pc;
+    kp.fault->op = op;
+    kp.fault->step = c.step;
+    kp.fault->layer = layer;
+    kp.fault->index = index;
+  }
+  if (code == -7) stc32(kp.abort_flag, 1u);
+}
+
+// Watchdog: called from poll loops; true when this thread must stop waiting.
+__device__ __forceinline__ bool expired(Cx& c, int op, int layer, int index) {
+  if ((++c.poll_iters & 63) != 0) return false;
+  if (ldc32(c.kp->abort_flag)) return true;
+  const uint64_t now = __builtin_amdgcn_s_memrealtime();
+  if (c.deadline == 0) {
+    c.deadline = now + c.kp->watchdog_ticks;
+    return false;
+  }
+  if (now > c.deadline) {
+    raise_fault(c, -7, op, layer, index);
+    return true;
+  }
+  return false;
+}
+
+// Workgroup-wide OR of the per-thread failure flags (also a barrier).
+__device__ __forceinline__ bool cta_failed(Cx& c) {
+  const uint64_t b = __ballot(c.fail);
+  uint32_t* f = c.sm.flags + c.flag_parity * kWaves;
+  if (c.lane == 0) f[c.wave] = b != 0;
+  cta_sync();
+  bool any = false;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) any |= f[w] != 0;
+  c.flag_parity ^= 1;
+  return any;
+}
+
+// Trace: time at which an instruction's inputs were staged.
+__device__ __forceinline__ void mark_ready(Cx& c) {
+  if (c.kp->trace && c.tid == 0 && c.step < c.kp->trace_steps) c.sm.misc[0] = (uint32_t)__builtin_amdgcn_s_memrealtime();
+}
+
+// Counter mode: one thread waits until the stage counter reaches its target.
+__device__ __forceinline__ bool sentinel_mode(const Cx& c) { return c.kp->sync_mode == 0; }
+
+__device__ __forceinline__ void counter_wait(Cx& c, int sid, int n_in, int op, int layer) {
+  if (sentinel_mode(c)) return;
+  if (c.tid == 0 && sid >= 0) {
+    const uint32_t target = (uint32_t)n_in * (uint32_t)(c.step + 1);
+    uint32_t* ctr = c.kp->counters + sid;
+    int tries = 0;
+    while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, MK_SCOPE) < target) {
+      // exponential back-off ("8 - Ecrire son megakernel", section 8.5)
+      const int k = tries < 4 ? (1 << tries) : 16;
+      for (int i = 0; i < k; ++i) __builtin_amdgcn_s_sleep(1);
+      ++tries;
+      if (expired(c, op, layer, sid)) {
+        c.fail = true;
+        break;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void counter_signal(Cx& c, int sid) {
+  if (sentinel_mode(c) || sid < 0) return;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  cta_sync();
+  if (c.tid == 0) __hip_atomic_fetch_add(c.kp->counters + sid, 1u, __ATOMIC_RELAXED, MK_SCOPE);
+}
+
+// Poll one fp32 word until it stops being the sentinel (sentinel mode) or
+// read it once (counter mode, after the counter wait).
+__device__ __forceinline__ float poll_f32(Cx& c, const float* p, int op, int layer) {
+  uint32_t v = ldc32(p);
+  if (sentinel_mode(c)) {
+    while (v == kSent32 && !c.fail) {
+      if (expired(c, op, layer, -1)) {
+        c.fail = true;
+        break;
+      }
+      v = ldc32(p);
+    }
+  }
+  return __uint_as_float(v);
+}
+
+// Stage n fp32 values of a sync buffer into LDS dst[0..npad) (zero padded),
+// multiplied by the fp16 gain when one is given.  All loads of a thread are
+// issued before any is checked.  Returns this thread's sum of squares of the
+// raw values (for RMSNorm).
+__device__ __forceinline__ float stage_vec(Cx& c, const float* src, float* dst, int n, int npad, const uint16_t* gain, int op, int layer) {
+  constexpr int kPer = 16;  // floats a thread stages per round
+  float ss = 0.f;
+  for (int base = c.tid * 4; base < npad; base += kThreads * kPer) {
+    uint32_t v[kPer];
+    float g[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer / 4; ++k) {
+      const int i = base + k * kThreads * 4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[k * 4 + j] = (i + j < n) ? ldc32(src + i + j) : 0u;
+      if (gain && i < n) {
+        const uint2 w = *(const uint2*)(gain + i);
+        const _Float16* h = (const _Float16*)&w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) g[k * 4 + j] = (float)h[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) g[k * 4 + j] = 1.f;
+      }
+    }
+    if (sentinel_mode(c)) {
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int i = base + (k / 4) * kThreads * 4 + (k % 4);
+        while (i < n && v[k] == kSent32 && !c.fail) {
+          if (expired(c, op, layer, i)) {
+            c.fail = true;
+            break;
+          }
+          v[k] = ldc32(src + i);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kPer / 4; ++k) {
+      const int i = base + k * kThreads * 4;
+      if (i < npad) {
+        f4 x;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float f = __uint_as_float(v[k * 4 + j]);
+          ss += f * f;
+          x[j] = f * g[k * 4 + j];
+        }
+        *(f4*)(dst + i) = x;
+      }
+    }
+  }
+  return ss;
+}
+
+// Stage an fp16 row of read-only data (an embedding row) as fp32, times the
+// gain; returns this thread's sum of squares of the raw values.
+__device__ __forceinline__ float stage_row_h(Cx& c, const uint16_t* src, float* dst, int n, int npad, const uint16_t* gain) {
+  float ss = 0.f;
+  for (int i = c.tid * 4; i < npad; i += kThreads * 4) {
+    f4 v = {0.f, 0.f, 0.f, 0.f};
+    if (i < n) {
+      const uint2 w = *(const uint2*)(src + i);
+      const uint2 gw = *(const uint2*)(gain + i);
+      const _Float16* h = (const _Float16*)&w;
+      const _Float16* gh = (const _Float16*)&gw;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float f = (float)h[j];
+        ss += f * f;
+        v[j] = f * (float)gh[j];
+      }
+    }
+    *(f4*)(dst + i) = v;
+  }
+  return ss;
+}
+
+__device__ __forceinline__ float* buf_at(const Buf& b, int e, int l, int r) {
+  return b.p + e * b.es + (int64_t)l * b.ls + (int64_t)r * b.rs;
+}
+
+// Store value v at element idx of every replica of b (epoch e) and re-arm the
+// same element for epoch e1 (sentinel mode).  Called by the whole wavefront
+// with a uniform value; lanes 0..R-1 store, lanes R..2R-1 re-arm.
+__device__ __forceinline__ void publish(const Cx& c, const Buf& b, int l, int64_t idx, float v) {
+  const int R = c.kp->R;
+  if (c.lane < R) stcf(buf_at(b, c.e, l, c.lane) + idx, v);
+  else if (c.lane < 2 * R && sentinel_mode(c)) stc32(buf_at(b, c.e1, l, c.lane - R) + idx, kSent32);
+}
+
+// ---------------------------------------------------------------- GEMV core
+// Streams this wavefront's chunks of instruction `in` through the ring and
+// calls epi(u_local, row0, row1) once per unit with uniform sums.
+template <int CPS, typename Epi>
+__device__ __forceinline__ void gemv(Cx& c, Ring& ring, const Ins& in, const float* vec, float scale, Epi epi) {
+  const int ks = in.ks, rg = kWaves / ks, ki = c.wave % ks, gi = c.wave / ks;
+  const int upr = in.upr;
+  float act[CPS][8];
+  const int col0 = ki * CPS * kChunkHalfs + c.lane * 8;
+#pragma unroll
+  for (int k = 0; k < CPS; ++k) {
+    const f4 a = *(const f4*)(vec + col0 + k * kChunkHalfs);
+    const f4 b = *(const f4*)(vec + col0 + k * kChunkHalfs + 4);
+    act[k][0] = a[0]; act[k][1] = a[1]; act[k][2] = a[2]; act[k][3] = a[3];
+    act[k][4] = b[0]; act[k][5] = b[1]; act[k][6] = b[2]; act[k][7] = b[3];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) act[k][e] *= scale;
+  }
+  for (int u = gi; u < in.nu; u += rg) {
+    float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < CPS; ++k) r0 += dot8(ring_next(ring), act[k]);
+    if (upr == 2) {
+#pragma unroll
+      for (int k = 0; k < CPS; ++k) r1 += dot8(ring_next(ring), act[k]);
+    }
+    r0 = wave_sum(r0);
+    if (upr == 2) r1 = wave_sum(r1);
+    if (ks == 1) {
+      epi(u, r0, r1);
+    } else if (c.lane == 0) {
+      c.sm.scratch[(u * upr) * ks + ki] = r0;
+      if (upr == 2) c.sm.scratch[(u * upr + 1) * ks + ki] = r1;
+    }
+  }
+  if (ks > 1) {
+    cta_sync();
+    if (ki == 0) {
+      for (int u = gi; u < in.nu; u += rg) {
+        float s0 = 0.f, s1 = 0.f;
+        for (int k = 0; k < ks; ++k) s0 += c.sm.scratch[(u * upr) * ks + k];
+        if (upr == 2)
+          for (int k = 0; k < ks; ++k) s1 += c.sm.scratch[(u * upr + 1) * ks + k];
+        epi(u, s0, s1);
+      }
+    }
+  }
+}
+
+template <typename Epi>
+__device__ __forceinline__ void gemv_dispatch(Cx& c, Ring& ring, const Ins& in, const float* vec, float scale, Epi epi) {
+  switch (in.cps) {
+    case 1: gemv<1>(c, ring, in, vec, scale, epi); break;
+    case 2: gemv<2>(c, ring, in, vec, scale, epi); break;
+    case 3: gemv<3>(c, ring, in, vec, scale, epi); break;
+    default: gemv<4>(c, ring, in, vec, scale, epi); break;
+  }
+}
+
+// Closes the staging of an instruction's inputs: barrier, trace mark and,
+// for RMSNorm inputs, the workgroup sum of squares of the n staged values
+// (ss_thread = this thread's share).  Returns the RMSNorm scale (1 without norm).
+__device__ __forceinline__ float finish_staging(Cx& c, int n, bool norm, float ss_thread) {
+  if (norm) {
+    const float p = wave_sum(ss_thread);
+    if (c.lane == 0) c.sm.wsum[c.wave] = p;
+  }
+  cta_sync();
+  mark_ready(c);
+  if (!norm) return 1.0f;
+  float ss = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) ss += c.sm.wsum[w];
+  return 1.0f / __builtin_sqrtf(ss / (float)n + c.kp->eps);
+}
+
+// Stage the layer input x_l (embedding row for layer 0) times the gain.
+__device__ __forceinline__ float stage_layer_input(Cx& c, int l, int npad, const uint16_t* gain, int op) {
+  const KParams& kp = *c.kp;
+  if (l == 0) return stage_row_h(c, kp.embed + (int64_t)c.tok * kp.d, c.sm.vec, kp.d, npad, gain);
+  return stage_vec(c, buf_at(kp.xm, c.e, l - 1, c.rep), c.sm.vec, kp.d, npad, gain, op, l);
+}
+
+// Residual rows [u0, u0+nu) of x_l (embedding for layer 0) into sm.resid.
+__device__ __forceinline__ void stage_resid(Cx& c, const float* src, const uint16_t* emb, int u0, int nu, int op, int layer) {
+  for (int i = c.tid; i < nu; i += kThreads) {
+    float v;
+    if (emb) v = (float)__builtin_bit_cast(_Float16, emb[u0 + i]);
+    else v = poll_f32(c, src + u0 + i, op, layer);
+    c.sm.resid[i] = v;
+  }
+}
+
+// ---------------------------------------------------------------- ops
+__device__ __forceinline__ void op_qkv(Cx& c, Ring& ring, const Ins& in) {
+  const KParams& kp = *c.kp;
+  const int l = in.layer;
+  counter_wait(c, in.sync_in, in.n_in, OP_QKV, l);
+  if (!sentinel_mode(c)) cta_sync();
+  const uint16_t* g1 = kp.norms + (int64_t)l * 2 * kp.d;
+  const float ss = stage_layer_input(c, l, in.kpad, g1, OP_QKV);
+  const float scale = finish_staging(c, kp.d, true, ss);
+  const int hh = kp.hd / 2, nqh = kp.nq * hh, nkh = kp.nkv * hh;
+  const float* rope = kp.rope + (int64_t)c.pos * hh * 2;
+  gemv_dispatch(c, ring, in, c.sm.vec, scale, [&](int u, float a, float b) {
+    int g = in.u0 + u;
+    if (g < nqh + nkh) {  // rotary pair (i, i + hd/2) of a q or k head
+      const bool isq = g < nqh;
+      if (!isq) g -= nqh;
+      const int head = g / hh, i = g % hh;
+      const float cs = rope[2 * i], sn = rope[2 * i + 1];
+      const float ra = a * cs - b * sn, rb = a * sn + b * cs;
+      if (isq) {
+        float* q = buf_at(kp.q, c.e, l, 0) + head * kp.hd + i;
+        float* q1 = buf_at(kp.q, c.e1, l, 0) + head * kp.hd + i;
+        if (c.lane == 0) stcf(q, ra);
+        else if (c.lane == 1) stcf(q + hh, rb);
+        else if (c.lane == 2 && sentinel_mode(c)) stc32(q1, kSent32);
+        else if (c.lane == 3 && sentinel_mode(c)) stc32(q1 + hh, kSent32);
+      } else {
+        uint16_t* k = kp.kc + (((int64_t)l * kp.nkv + head) * kp.max_seq + c.pos) * kp.hd + i;
+        if (c.lane == 0) stc16(k, __builtin_bit_cast(uint16_t, (_Float16)ra));
+        else if (c.lane == 1) stc16(k + hh, __builtin_bit_cast(uint16_t, (_Float16)rb));
+      }
+    } else {  // value rows
+      g -= nqh + nkh;
+      const int head = g / hh, i = g % hh;
+      uint16_t* v = kp.vc + (((int64_t)l * kp.nkv + head) * kp.max_seq + c.pos) * kp.hd + i;
+      if (c.lane == 0) stc16(v, __builtin_bit_cast(uint16_t, (_Float16)a));
+      else if (c.lane == 1) stc16(v + hh, __builtin_bit_cast(uint16_t, (_Float16)b));
+    }
+  });
+  counter_signal(c, in.sync_out);
+}
+
+// Split attention for (kv head, split) units: unnormalised partial
+// O = sum_t 2^(s_t - m) v_t, L = sum_t 2^(s_t - m), m = max_t s_t, with
+// scores s_t = q.k_t / sqrt(hd) * log2(e).
+__device__ __forceinline__ void op_att(Cx& c, const Ins& in) {
+  const KParams& kp = *c.kp;
+  const int l = in.layer;
+  const int G = kp.nq / kp.nkv, hd = kp.hd, S = kp.S;
+  const int T = c.pos + 1;
+  const int chunk = (T + S - 1) / S;
+  const float qscale = kLog2e / __builtin_sqrtf((float)hd);
+  counter_wait(c, in.sync_in, in.n_in, OP_ATT, l);
+  if (!sentinel_mode(c)) cta_sync();
+  float* qs = c.sm.vec;              // [G][hd]
+  float* kcur = c.sm.vec + G * hd;   // [hd]
+  float* vcur = kcur + hd;           // [hd]
+  for (int ui = 0; ui < in.nu; ++ui) {
+    const int U = in.u0 + ui, g = U / S, sp = U % S;
+    const int t0 = sp * chunk, t1 = min(T, t0 + chunk);
+    const bool has_cur = t0 <= c.pos && c.pos < t1;
+    // stage q of the group and, for the split holding the current position, its K/V
+    const float* qsrc = buf_at(kp.q, c.e, l, 0) + g * G * hd;
+    if (c.tid < G * hd) qs[c.tid] = poll_f32(c, qsrc + c.tid, OP_ATT, l) * qscale;
+    if (has_cur && c.tid < 2 * hd) {
+      const int i = c.tid % hd;
+      const uint16_t* src = (c.tid < hd ? kp.kc : kp.vc) + (((int64_t)l * kp.nkv + g) * kp.max_seq + c.pos) * hd + i;
+      uint16_t v = ldc16(src);
+      if (sentinel_mode(c)) {
+        while (v == kSent16 && !c.fail) {
+          if (expired(c, OP_ATT, l, i)) {
+            c.fail = true;
+            break;
+          }
+          v = ldc16(src);
+        }
+      }
+      (c.tid < hd ? kcur : vcur)[i] = (float)__builtin_bit_cast(_Float16, v);
+    }
+    cta_sync();
+    if (ui == 0) mark_ready(c);
+    // each wavefront: positions t0 + wave, t0 + wave + kWaves, ...
+    constexpr int kMaxG = 8, kMaxDpl = 4;
+    const int dpl = hd / 64;  // dims per lane
+    float m[kMaxG], lsum[kMaxG], o[kMaxG][kMaxDpl];
+#pragma unroll
+    for (int j = 0; j < kMaxG; ++j) {
+      m[j] = -INFINITY;
+      lsum[j] = 0.f;
+#pragma unroll
+      for (int k = 0; k < kMaxDpl; ++k) o[j][k] = 0.f;
+    }
+    const uint16_t* kbase = kp.kc + ((int64_t)l * kp.nkv + g) * kp.max_seq * hd + c.lane * dpl;
+    const uint16_t* vbase = kp.vc + ((int64_t)l * kp.nkv + g) * kp.max_seq * hd + c.lane * dpl;
+    for (int t = t0 + c.wave; t < t1; t += kWaves) {
+      float kv[kMaxDpl], vv[kMaxDpl];
+      if (t == c.pos) {
+#pragma unroll
+        for (int k = 0; k < kMaxDpl; ++k)
+          if (k < dpl) { kv[k] = kcur[c.lane * dpl + k]; vv[k] = vcur[c.lane * dpl + k]; }
+      } else {
+        const uint16_t* kr = kbase + (int64_t)t * hd;
+        const uint16_t* vr = vbase + (int64_t)t * hd;
+#pragma unroll
+        for (int k = 0; k < kMaxDpl; ++k)
+          if (k < dpl) {
+            kv[k] = (float)__builtin_bit_cast(_Float16, kr[k]);
+            vv[k] = (float)__builtin_bit_cast(_Float16, vr[k]);
+          }
+      }
+#pragma unroll
+      for (int j = 0; j < kMaxG; ++j) {
+        if (j >= G) break;
+        float s = 0.f;
+#pragma unroll
+        for (int k = 0; k < kMaxDpl; ++k)
+          if (k < dpl) s += qs[j * hd + c.lane * dpl + k] * kv[k];
+        s = wave_sum(s);
+        const float mn = fmaxf(m[j], s);
+        const float a = exp2f(m[j] - mn), p = exp2f(s - mn);
+        lsum[j] = lsum[j] * a + p;
+#pragma unroll
+        for (int k = 0; k < kMaxDpl; ++k)
+          if (k < dpl) o[j][k] = o[j][k] * a + p * vv[k];
+        m[j] = mn;
+      }
+    }
+    // combine the wavefronts: scratch [wave][G][hd + 2]
+    float* sc = c.sm.scratch;
+    const int rec = hd + 2;
+#pragma unroll
+    for (int j = 0; j < kMaxG; ++j) {
+      if (j >= G) break;
+      float* r = sc + (c.wave * G + j) * rec;
+#pragma unroll
+      for (int k = 0; k < kMaxDpl; ++k)
+        if (k < dpl) r[2 + c.lane * dpl + k] = o[j][k];
+      if (c.lane == 0) { r[0] = m[j]; r[1] = lsum[j]; }
+    }
+    cta_sync();
+    if (c.tid < G * hd) {
+      const int j = c.tid / hd, dd = c.tid % hd;
+      float M = -INFINITY;
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sc[(w * G + j) * rec]);
+      float Lt = 0.f, Ot = 0.f;
+      if (M != -INFINITY) {
+        for (int w = 0; w < kWaves; ++w) {
+          const float* r = sc + (w * G + j) * rec;
+          const float a = exp2f(r[0] - M);
+          Lt += a * r[1];
+          Ot += a * r[2 + dd];
+        }
+      }
+      const int qh = g * G + j;
+      const int64_t po = ((((int64_t)c.e * kp.L + l) * kp.nq + qh) * S + sp);
+      const int64_t po1 = ((((int64_t)c.e1 * kp.L + l) * kp.nq + qh) * S + sp);
+      stcf(kp.att_o + po * hd + dd, Ot);
+      if (sentinel_mode(c)) stc32(kp.att_o + po1 * hd + dd, kSent32);
+      if (dd == 0) {
+        stcf(kp.att_ml + po * 2, M);
+        stcf(kp.att_ml + po * 2 + 1, Lt);
+        if (sentinel_mode(c)) {
+          stc32(kp.att_ml + po1 * 2, kSent32);
+          stc32(kp.att_ml + po1 * 2 + 1, kSent32);
+        }
+      }
+    }
+    cta_sync();  // LDS reused by the next unit
+  }
+  counter_signal(c, in.sync_out);
+}
+
+// Merge the S splits of one query head for kRedDims output dims.
+__device__ __forceinline__ void op_red(Cx& c, const Ins& in) {
+  const KParams& kp = *c.kp;
+  const int l = in.layer, hd = kp.hd, S = kp.S, nb = hd / kRedDims;
+  counter_wait(c, in.sync_in, in.n_in, OP_RED, l);
+  if (!sentinel_mode(c)) cta_sync();
+  for (int ui = c.wave; ui < in.nu; ui += kWaves) {
+    const int U = in.u0 + ui, h = U / nb, b = U % nb;
+    const int s = c.lane;
+    const int64_t base = (((int64_t)c.e * kp.L + l) * kp.nq + h) * S + s;
+    float ms = -INFINITY, ls = 0.f, os[kRedDims];
+#pragma unroll
+    for (int d = 0; d < kRedDims; ++d) os[d] = 0.f;
+    if (s < S) {
+      uint32_t raw[2 + kRedDims];
+      const float* ml = kp.att_ml + base * 2;
+      const float* ov = kp.att_o + base * hd + b * kRedDims;
+      raw[0] = ldc32(ml);
+      raw[1] = ldc32(ml + 1);
+#pragma unroll
+      for (int d = 0; d < kRedDims; ++d) raw[2 + d] = ldc32(ov + d);
+      if (sentinel_mode(c)) {
+#pragma unroll
+        for (int k = 0; k < 2 + kRedDims; ++k) {
+          const float* p = k < 2 ? ml + k : ov + (k - 2);
+          while (raw[k] == kSent32 && !c.fail) {
+            if (expired(c, OP_RED, l, k)) {
+              c.fail = true;
+              break;
+            }
+            raw[k] = ldc32(p);
+          }
+        }
+      }
+      ms = __uint_as_float(raw[0]);
+      ls = __uint_as_float(raw[1]);
+#pragma unroll
+      for (int d = 0; d < kRedDims; ++d) os[d] = __uint_as_float(raw[2 + d]);
+    }
+    if (ui == 0) mark_ready(c);
+    const float M = wave_max(ms);
+    const float w = (s < S && ms != -INFINITY) ? exp2f(ms - M) : 0.f;
+    const float Lt = wave_sum(w * ls);
+    const float inv = 1.0f / Lt;
+#pragma unroll
+    for (int d = 0; d < kRedDims; ++d) {
+      const float v = wave_sum(w * os[d]) * inv;
+      publish(c, kp.o, l, (int64_t)h * hd + b * kRedDims + d, v);
+    }
+  }
+  counter_signal(c, in.sync_out);
+}
+
+__device__ __forceinline__ void op_oproj(Cx& c, Ring& ring, const Ins& in) {
+  const KParams& kp = *c.kp;
+  const int l = in.layer;
+  counter_wait(c, in.sync_in, in.n_in, OP_OPROJ, l);
+  if (!sentinel_mode(c)) cta_sync();
+  stage_vec(c, buf_at(kp.o, c.e, l, c.rep), c.sm.vec, kp.nq * kp.hd, in.kpad, nullptr, OP_OPROJ, l);
+  stage_resid(c, l == 0 ? nullptr : buf_at(kp.xm, c.e, l - 1, c.rep), l == 0 ? kp.embed + (int64_t)c.tok * kp.d : nullptr,
+              in.u0, in.nu, OP_OPROJ, l);
+  finish_staging(c, 0, false, 0.f);
+  gemv_dispatch(c, ring, in, c.sm.vec, 1.f, [&](int u, float y, float) {
+    publish(c, kp.xa, l, in.u0 + u, c.sm.resid[u] + y);
+  });
+  counter_signal(c, in.sync_out);
+}
+
+__device__ __forceinline__ void op_upgate(Cx& c, Ring& ring, const Ins& in) {
+  const KParams& kp = *c.kp;
+  const int l = in.layer;
+  counter_wait(c, in.sync_in, in.n_in, OP_UPGATE, l);
+  if (!sentinel_mode(c)) cta_sync();
+  const uint16_t* g2 = kp.norms + ((int64_t)l * 2 + 1) * kp.d;
+  const float ss = stage_vec(c, buf_at(kp.xa, c.e, l, c.rep), c.sm.vec, kp.d, in.kpad, g2, OP_UPGATE, l);
+  const float scale = finish_staging(c, kp.d, true, ss);
+  gemv_dispatch(c, ring, in, c.sm.vec, scale, [&](int u, float gt, float up) {
+    const float silu = gt / (1.0f + __expf(-gt));
+    publish(c, kp.m, l, in.u0 + u, silu * up);
+  });
+  counter_signal(c, in.sync_out);
+}
+
+__device__ __forceinline__ void op_down(Cx& c, Ring& ring, const Ins& in) {
+  const KParams& kp = *c.kp;
+  const int l = in.layer;
+  counter_wait(c, in.sync_in, in.n_in, OP_DOWN, l);
+  if (!sentinel_mode(c)) cta_sync();
+  stage_vec(c, buf_at(kp.m, c.e, l, c.rep), c.sm.vec, kp.f, in.kpad, nullptr, OP_DOWN, l);
+  stage_resid(c, buf_at(kp.xa, c.e, l, c.rep), nullptr, in.u0, in.nu, OP_DOWN, l);
+  finish_staging(c, 0, false, 0.f);
+  gemv_dispatch(c, ring, in, c.sm.vec, 1.f, [&](int u, float y, float) {
+    publish(c, kp.xm, l, in.u0 + u, c.sm.resid[u] + y);
+  });
+  counter_signal(c, in.sync_out);
+}
+
+// Argmax key: order-preserving map of the logit in the high word, the
+// complemented row index in the low word (max key = max logit, lowest index).
+__device__ __forceinline__ uint64_t argmax_key(float v, int idx) {
+  uint32_t b = __float_as_uint(v);
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)b << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)idx);
+}
+
+__device__ __forceinline__ void op_lmhead(Cx& c, Ring& ring, const Ins& in) {
+  const KParams& kp = *c.kp;
+  const int L = kp.L;
+  counter_wait(c, in.sync_in, in.n_in, OP_LMHEAD, L);
+  if (!sentinel_mode(c)) cta_sync();
+  uint64_t best = 1;  // below every real key
+  if (in.nu > 0) {
+    const uint16_t* gf = kp.norms + (int64_t)L * 2 * kp.d;
+    const float ss = stage_vec(c, buf_at(kp.xm, c.e, L - 1, c.rep), c.sm.vec, kp.d, in.kpad, gf, OP_LMHEAD, L);
+    const float scale = finish_staging(c, kp.d, true, ss);
+    float* lo = kp.logits ? kp.logits + (int64_t)c.step * kp.V : nullptr;
+    float bv = -INFINITY;
+    int bi = -1;
+    bool nan = false;
+    gemv_dispatch(c, ring, in, c.sm.vec, scale, [&](int u, float y, float) {
+      const int row = in.u0 + u;
+      if (lo && c.lane == 0) lo[row] = y;
+      if (y != y) nan = true;
+      else if (bi < 0 || y > bv || (y == bv && row < bi)) { bv = y; bi = row; }
+    });
+    if (nan && c.lane == 0) raise_fault(c, -8, OP_LMHEAD, L, c.step);
+    if (c.lane == 0) c.sm.keys[c.wave] = bi >= 0 ? argmax_key(bv, bi) : 1;
+    cta_sync();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) best = max(best, c.sm.keys[w]);
+  }
+  // re-arm the slot for the step after next, then one release fence per step
+  // orders this step's stores (KV cache, re-arms) before the key.
+  uint64_t* slot = kp.lmp + c.e * kp.lmp_es + in.slot;
+  uint64_t* slot1 = kp.lmp + c.e1 * kp.lmp_es + in.slot;
+  if (sentinel_mode(c) && c.wave == 0 && c.lane < kp.R) stc64(slot1 + c.lane * kp.lmp_rs, kSent64);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  cta_sync();
+  if (c.wave == 0 && c.lane < kp.R) stc64(slot + c.lane * kp.lmp_rs, best);
+  if (!sentinel_mode(c) && c.tid == 0)
+    __hip_atomic_fetch_add(kp.counters + in.sync_out, 1u, __ATOMIC_RELAXED, MK_SCOPE);
+}
+
+__device__ __forceinline__ void op_argmax(Cx& c, const Ins& in) {
+  const KParams& kp = *c.kp;
+  counter_wait(c, in.sync_in, in.n_in, OP_ARGMAX, kp.L);
+  if (!sentinel_mode(c)) cta_sync();
+  const uint64_t* src = kp.lmp + c.e * kp.lmp_es + c.rep * kp.lmp_rs;
+  uint64_t k = 0;
+  for (int i = c.tid; i < in.nu; i += kThreads) {
+    uint64_t v = ldc64(src + i);
+    if (sentinel_mode(c)) {
+      while (v == kSent64 && !c.fail) {
+        if (expired(c, OP_ARGMAX, kp.L, i)) {
+          c.fail = true;
+          break;
+        }
+        v = ldc64(src + i);
+      }
+    }
+    k = max(k, v);
+    if (kp.dbg) kp.dbg[(int64_t)c.cta * kThreads + i] = v;
+  }
+  // workgroup max
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint64_t o = __shfl_xor(k, off);
+    k = max(k, o);
+  }
+  if (c.lane == 0) c.sm.keys[c.wave] = k;
+  cta_sync();
+  mark_ready(c);
+  uint64_t best = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) best = max(best, c.sm.keys[w]);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  int tok = (int)(0xFFFFFFFFu - (uint32_t)best);
+  if (tok < 0 || tok >= kp.V) tok = 0;  // only on an aborted run
+  if (c.cta == 0 && c.tid == 0) kp.tokens[c.step] = tok;
+  c.tok = tok;
+}
+
+__device__ __forceinline__ void op_chain(Cx& c, Ring& ring, const Ins& in) {
+  const KParams& kp = *c.kp;
+  const int i = in.layer, n = kp.chain_n;
+  counter_wait(c, in.sync_in, in.n_in, OP_CHAIN, i);
+  if (!sentinel_mode(c)) cta_sync();
+  if (i == 0) {
+    for (int k = c.tid * 4; k < in.kpad; k += kThreads * 4)
+      *(f4*)(c.sm.vec + k) = k < n ? *(const f4*)(kp.x0 + k) : f4{0.f, 0.f, 0.f, 0.f};
+  } else {
+    stage_vec(c, buf_at(kp.y, 0, i - 1, c.rep), c.sm.vec, n, in.kpad, nullptr, OP_CHAIN, i);
+  }
+  finish_staging(c, 0, false, 0.f);
+  gemv_dispatch(c, ring, in, c.sm.vec, 1.f, [&](int u, float y, float) {
+    const float t = tanhf(y);
+    if (c.lane < kp.R) stcf(buf_at(kp.y, 0, i, c.lane) + in.u0 + u, t);
+  });
+  counter_signal(c, in.sync_out);
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kThreads, 1) void mk_monokernel(const KParams* __restrict__ kpp) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const KParams& kp = *kpp;
+  Cx c;
+  c.kp = kpp;
+  c.cta = blockIdx.x;
+  c.tid = threadIdx.x;
+  c.lane = lane_id();
+  c.wave = wave_id();
+  c.xcc = xcc_id();
+  c.rep = c.xcc % kp.R;
+  c.fail = false;
+  c.deadline = 0;
+  c.poll_iters = 0;
+  c.flag_parity = 0;
+  c.pc = 0;
+  // LDS carve-up (must match lds_bytes_for on the host)
+  c.sm.base = smem;
+  const uint32_t ring_base = (uint32_t)(uintptr_t)smem;
+  c.sm.vec = (float*)(smem + kWaves * kRing * 1024);
+  c.sm.scratch = c.sm.vec + kp.vec_floats;
+  c.sm.resid = c.sm.scratch + kScratchFloats;
+  c.sm.flags = (uint32_t*)(c.sm.resid + 1024);
+  c.sm.wsum = (float*)(c.sm.flags + 2 * kWaves);
+  c.sm.keys = (uint64_t*)(c.sm.wsum + kWaves);
+  c.sm.misc = (uint32_t*)(c.sm.keys + kWaves);
+
+  Ring ring;
+  {
+    const int wi = c.cta * kWaves + c.wave;
+    ring.lds = __builtin_amdgcn_readfirstlane(ring_base + c.wave * kRing * 1024);
+    ring.n = (uint32_t)kp.wave_n[wi];
+    ring.g = (const uint8_t*)uniform_ptr(kp.stream + kp.wave_off[wi] * 1024);
+    ring.issue = 0;
+    ring.slot = 0;
+    ring_start(ring);
+  }
+
+  // drop any line an earlier kernel (e.g. the sentinel fill) left in this XCD's L2
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const int beg = kp.ins_off[c.cta], end = kp.ins_off[c.cta + 1];
+  c.tok = kp.forced ? kp.forced[0] : kp.first_token;
+  uint32_t* trace = nullptr;
+  for (int step = 0; step < kp.n_steps; ++step) {
+    c.step = step;
+    c.pos = kp.pos0 + step;
+    c.e = step % 3;
+    c.e1 = (step + 1) % 3;
+    const bool tr = kp.trace && step < kp.trace_steps;
+    if (tr) trace = kp.trace + (((int64_t)c.cta * kp.trace_steps + step) * kp.max_ins) * 8;
+    for (int pc = beg; pc < end; ++pc) {
+      c.pc = pc - beg;
+      const Ins in = kp.ins[pc];
+      c.deadline = 0;  // every wait gets its own watchdog budget
+      c.poll_iters = 0;
+      uint64_t t_wait = 0;
+      if (tr) {
+        t_wait = __builtin_amdgcn_s_memrealtime();
+        if (c.tid == 0) c.sm.misc[0] = 0;
+      }
+      switch (in.op) {
+        case OP_QKV: op_qkv(c, ring, in); break;
+        case OP_ATT: op_att(c, in); break;
+        case OP_RED: op_red(c, in); break;
+        case OP_OPROJ: op_oproj(c, ring, in); break;
+        case OP_UPGATE: op_upgate(c, ring, in); break;
+        case OP_DOWN: op_down(c, ring, in); break;
+        case OP_LMHEAD: op_lmhead(c, ring, in); break;
+        case OP_ARGMAX: op_argmax(c, in); break;
+        case OP_CHAIN: op_chain(c, ring, in); break;
+        default: break;
+      }
+      if (c.tid == 0) kp.progress[c.cta] = ((uint32_t)step << 16) | (uint32_t)(c.pc + 1);
+      if (cta_failed(c)) goto done;
+      if (tr && c.tid == 0) {
+        const uint64_t t_done = __builtin_amdgcn_s_memrealtime();
+        uint32_t* r = trace + (int64_t)c.pc * 8;
+        r[0] = (uint32_t)c.cta;
+        r[1] = (uint32_t)step;
+        r[2] = (uint32_t)c.pc;
+        r[3] = (uint32_t)in.op | ((uint32_t)(in.layer & 0xFFFF) << 8);
+        r[4] = (uint32_t)t_wait;
+        r[5] = c.sm.misc[0] ? c.sm.misc[0] - (uint32_t)t_wait : 0u;
+        r[6] = (uint32_t)(t_done - t_wait);
+        r[7] = (uint32_t)c.xcc;
+      }
+    }
+    if (kp.forced && step + 1 < kp.n_steps) c.tok = kp.forced[step + 1];
+  }
+done:
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// ---------------------------------------------------------------- helper kernels
+// Fill n 32-bit words with a value.
+__global__ void mk_fill32(uint32_t* p, int64_t n, uint32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+// Re-arm the KV-cache positions [p0, p1) of every layer and kv head.
+__global__ void mk_fill_kv(uint16_t* kc, uint16_t* vc, int64_t rows, int max_seq, int hd, int p0, int p1) {
+  const int64_t per_row = (int64_t)(p1 - p0) * hd;
+  const int64_t n = rows * per_row;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / per_row, k = i % per_row;
+    const int64_t o = r * max_seq * hd + (int64_t)p0 * hd + k;
+    kc[o] = kSent16;
+    vc[o] = kSent16;
+  }
+}
+
+// Gather weights into wavefront streams: chunk i copies `valid` fp16 values
+// from src[i] and zero-fills the rest of its 512.
+struct GatherDesc {
+  const uint16_t* src;
+  int32_t valid;
+  int32_t pad;
+};
+__global__ void mk_gather(uint16_t* dst, const GatherDesc* desc, int64_t n_chunks) {
+  const int lane = threadIdx.x & 63;
+  const int64_t w = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  for (int64_t i = w; i < n_chunks; i += nw) {
+    const GatherDesc d = desc[i];
+    uint16_t* o = dst + i * kChunkHalfs + lane * 8;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int col = lane * 8 + k;
+      o[k] = col < d.valid ? d.src[col] : (uint16_t)0;
+    }
+  }
+}
+
+// Count words equal to the fp32 sentinel (or the fp16 one, for KV ranges).
+__global__ void mk_count32(const uint32_t* p, int64_t n, uint32_t v, unsigned long long* out) {
+  unsigned long long cnt = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) cnt += p[i] == v;
+  atomicAdd(out, cnt);
+}
+__global__ void mk_count_kv(const uint16_t* kc, const uint16_t* vc, int64_t rows, int max_seq, int hd, int p0, int p1,
+                            unsigned long long* out) {
+  const int64_t per_row = (int64_t)(p1 - p0) * hd;
+  const int64_t n = rows * per_row;
+  unsigned long long cnt = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / per_row, k = i % per_row;
+    const int64_t o = r * max_seq * hd + (int64_t)p0 * hd + k;
+    cnt += (kc[o] == kSent16) + (vc[o] == kSent16);
+  }
+  atomicAdd(out, cnt);
+}
+
+// ---------------------------------------------------------------- host-side launch wrappers
+// Internal to the library (not part of the C ABI in include/mk.h).
+#define MK_INTERNAL __attribute__((visibility("hidden")))
+extern "C" {
+// kp_dev: the parameters, already copied to device memory.
+MK_INTERNAL hipError_t mk_launch_monokernel(const KParams* kp_dev, int grid, int lds_bytes, hipStream_t s) {
+  hipLaunchKernelGGL(mk_monokernel, dim3(grid), dim3(kThreads), lds_bytes, s, kp_dev);
+  return hipGetLastError();
+}
+MK_INTERNAL hipError_t mk_kernel_attributes(int lds_bytes, int* occupancy) {
+  hipError_t e = hipFuncSetAttribute((const void*)mk_monokernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+  if (e != hipSuccess) return e;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, mk_monokernel, kThreads, lds_bytes);
+}
+MK_INTERNAL hipError_t mk_launch_fill32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int blocks = (int)std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(mk_fill32, dim3(blocks), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+MK_INTERNAL hipError_t mk_launch_fill_kv(uint16_t* kc, uint16_t* vc, int64_t rows, int max_seq, int hd, int p0, int p1, hipStream_t s) {
+  if (p1 <= p0) return hipSuccess;
+  hipLaunchKernelGGL(mk_fill_kv, dim3(2048), dim3(256), 0, s, kc, vc, rows, max_seq, hd, p0, p1);
+  return hipGetLastError();
+}
+MK_INTERNAL hipError_t mk_launch_gather(uint16_t* dst, const void* desc, int64_t n_chunks, hipStream_t s) {
+  if (n_chunks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mk_gather, dim3(4096), dim3(256), 0, s, dst, (const GatherDesc*)desc, n_chunks);
+  return hipGetLastError();
+}
+MK_INTERNAL hipError_t mk_launch_count32(const uint32_t* p, int64_t n, uint32_t v, unsigned long long* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mk_count32, dim3(1024), dim3(256), 0, s, p, n, v, out);
+  return hipGetLastError();
+}
+MK_INTERNAL hipError_t mk_launch_count_kv(const uint16_t* kc, const uint16_t* vc, int64_t rows, int max_seq, int hd, int p0, int p1,
+                              unsigned long long* out, hipStream_t s) {
+  if (p1 <= p0) return hipSuccess;
+  hipLaunchKernelGGL(mk_count_kv, dim3(1024), dim3(256), 0, s, kc, vc, rows, max_seq, hd, p0, p1, out);
+  return hipGetLastError();
+}
+}

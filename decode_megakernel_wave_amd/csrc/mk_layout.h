@@ -1,0 +1,113 @@
+// mk_layout.h -- data layouts shared by the host planner and the device
+// interpreter: instruction records, kernel parameters, GEMV work split and
+// the sentinel bit patterns.
+#pragma once
+#include <stdint.h>
+
+#if defined(__HIP__)
+#define MK_HD __host__ __device__ inline
+#else
+#define MK_HD inline
+#endif
+
+namespace mk {
+
+constexpr int kWaves = 8;                 // wavefronts per workgroup
+constexpr int kThreads = kWaves * 64;     // 512 threads
+constexpr int kRing = 12;                 // 1 KB weight chunks in flight per wavefront (LDS ring)
+constexpr int kChunkHalfs = 512;          // fp16 values per chunk = 64 lanes x 8
+constexpr int kMaxK = 16384;              // longest GEMV row
+constexpr int kRedDims = 8;               // output dims per attention-reduce unit
+constexpr int kScratchFloats = 4096;      // LDS scratch for cross-wave reductions
+
+// Sentinels: bit patterns no computed value takes.  A quiet NaN whose low
+// payload bits can come neither from arithmetic (default NaN 0x7FC00000) nor
+// from widening an fp16 value (low 13 bits zero).
+constexpr uint32_t kSent32 = 0x7FC05E17u;
+constexpr uint16_t kSent16 = 0x7E17u;     // fp16 quiet NaN with a payload
+constexpr uint64_t kSent64 = 0;           // argmax keys are never 0
+
+enum Op : uint8_t {
+  OP_END = 0,
+  OP_QKV = 1,     // RMSNorm + fused QKV GEMV + RoPE, K/V into the cache
+  OP_ATT = 2,     // split attention partials (m, l, o) per (kv head, split)
+  OP_RED = 3,     // log-sum-exp merge of the splits -> o
+  OP_OPROJ = 4,   // x += Wo o
+  OP_UPGATE = 5,  // RMSNorm + gate/up GEMV + silu(g) * u
+  OP_DOWN = 6,    // x += Wd m
+  OP_LMHEAD = 7,  // final RMSNorm + LM head GEMV + per-workgroup argmax
+  OP_ARGMAX = 8,  // every workgroup merges the per-workgroup argmax keys
+  OP_CHAIN = 9,   // GEMV-tanh chain stage
+};
+
+// One instruction of a workgroup's list (32 bytes).
+struct Ins {
+  uint8_t op;
+  uint8_t upr;       // rows per GEMV unit (2 for rotary / gate-up pairs)
+  uint8_t ks;        // K slices across wavefronts
+  uint8_t cps;       // 512-wide chunks per slice
+  int16_t layer;
+  int16_t sync_in;   // stage consumed (counter mode), -1 none
+  int16_t sync_out;  // stage produced, -1 none
+  int16_t n_in;      // producers of sync_in per step
+  int32_t u0;        // first global unit
+  int32_t nu;        // number of units
+  int32_t slot;      // argmax slot of this workgroup (LM head)
+  int32_t kpad;      // padded GEMV row length (columns staged in LDS)
+  int32_t pad;
+};
+static_assert(sizeof(Ins) == 32, "Ins must be 32 bytes");
+
+// GEMV split inside one workgroup: units are dealt round-robin to kWaves/ks
+// row groups; each row's chunks are split into ks slices of cps chunks.
+MK_HD int units_of_group(int nu, int rg, int gi) { return nu > gi ? (nu - gi + rg - 1) / rg : 0; }
+
+struct Buf {            // an activation buffer [epoch][layer][replica][n]
+  float* p;
+  int64_t es, ls, rs;   // element strides
+};
+
+struct Fault {
+  int32_t code, cta, pc, op, step, layer, index, pad;
+};
+
+// Kernel parameters (passed by value).
+struct KParams {
+  // program
+  const Ins* ins;
+  const int32_t* ins_off;     // [grid + 1]
+  int32_t n_steps, pos0, first_token, chain;
+  const int32_t* forced;      // [n_steps] or null
+  int32_t* tokens;            // [n_steps]
+  float* logits;              // [n_steps][V] or null
+  // weights
+  const uint8_t* stream;      // repacked weight chunks
+  const int64_t* wave_off;    // [grid * kWaves] chunk offsets
+  const int32_t* wave_n;      // [grid * kWaves] chunks per step
+  const uint16_t* embed;      // [V][d]
+  const uint16_t* norms;      // [L][2][d] then final [d]
+  const float* rope;          // [max_seq][hd/2][2] (cos, sin)
+  uint16_t* kc;               // [L][nkv][max_seq][hd]
+  uint16_t* vc;
+  // activations and sync
+  Buf xa, xm, q, o, m, y;
+  float* att_o;               // [3][L][nq][S][hd]
+  float* att_ml;              // [3][L][nq][S][2]
+  uint64_t* lmp;              // [3][R][lm_slots]
+  int64_t lmp_es, lmp_rs;
+  const float* x0;            // chain input
+  uint32_t* counters;         // [n_sync_ids]
+  Fault* fault;
+  uint32_t* abort_flag;
+  uint32_t* trace;            // [grid][trace_steps][max_ins][8]
+  uint32_t* progress;         // [grid]: (step << 16) | (pc + 1) of the last finished instruction
+  uint64_t* dbg;              // [grid][512] diagnostics (argmax: last key each thread read)
+  int32_t trace_steps, max_ins;
+  // dims
+  int32_t L, d, nq, nkv, hd, f, V, max_seq, S, R, sync_mode, lm_slots;
+  int32_t chain_n, vec_floats;
+  float eps;
+  uint64_t watchdog_ticks;    // 100 MHz ticks
+};
+
+}  // namespace mk

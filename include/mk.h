@@ -1,0 +1,210 @@
+/*
+ * mk.h -- C ABI of the batch-1 decode monokernel for MI355X (gfx950).
+ *
+ * One persistent GPU launch runs whole decode steps of a Llama-style fp16
+ * decoder: RMSNorm + QKV + RoPE, split attention over an fp16 KV cache, the
+ * attention reduction, O-projection, SwiGLU MLP, LM head and greedy argmax.
+ * The method is the "monokernel" of "7 - AMD et le monokernel" (section 7.1:
+ * one persistent kernel runs prefill, decode and sampling without
+ * interruption) with the per-SM instruction interpreter of "8 - Ecrire son
+ * megakernel" (section 8.2) and its one-wave launch (section 8.3).  Stages
+ * synchronise through NaN sentinels written into the output buffers
+ * ("7 - AMD et le monokernel", section 7.3); atomic counters
+ * ("8 - Ecrire son megakernel", section 8.5) are kept as a comparison path.
+ *
+ * Conventions for every call:
+ *  - returns MK_OK (0) or a negative MK_E* code; mk_last_error() gives text;
+ *  - no call allocates or frees memory owned by the caller;
+ *  - "device" pointers are addresses in the memory of the context's GPU
+ *    (e.g. the data pointer of a torch CUDA tensor); "host" pointers are
+ *    ordinary CPU memory owned by the caller;
+ *  - work is enqueued on the HIP stream given at creation; calls that return
+ *    results synchronise that stream before returning;
+ *  - one context must not be used from two threads at once.
+ *
+ * Weight layout: fp16, row-major [out, in] ("a row is one dot product").
+ * embed and lm_head are [vocab, d_model]; wq [n_heads*head_dim, d_model];
+ * wk, wv [n_kv_heads*head_dim, d_model]; wo [d_model, n_heads*head_dim];
+ * w_gate, w_up [ffn, d_model]; w_down [d_model, ffn]; norm gains [d_model].
+ * RoPE rotates the pairs (i, i + head_dim/2) of each q and k head by the
+ * angle pos * rope_theta^(-2i/head_dim); positions are 0-based.  Query head j
+ * reads kv head floor(j * n_kv_heads / n_heads).
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MK_OK = 0,
+  MK_EINVAL = -1,   /* bad argument or unsupported shape */
+  MK_ENOMEM = -2,   /* a device or host allocation failed */
+  MK_EHIP = -3,     /* a HIP runtime call failed */
+  MK_ESTATE = -4,   /* call out of order (e.g. decode before prefill or before weights) */
+  MK_ERANGE = -5,   /* position would run past max_seq, or a token id outside [0, vocab) */
+  MK_EOCC = -6,     /* the kernel does not fit one wave of co-resident workgroups */
+  MK_ETIMEOUT = -7, /* the device watchdog fired: a dependency was never satisfied */
+  MK_ENAN = -8      /* a NaN logit was produced */
+};
+
+enum { MK_SYNC_SENTINEL = 0, MK_SYNC_COUNTER = 1 };
+
+/* Decoder dimensions.  Constraints: head_dim in {64, 128, 256}; n_heads a
+ * multiple of n_kv_heads; d_model, ffn multiples of 4; d_model, ffn,
+ * n_heads*head_dim at most 16384; max_seq >= 2. */
+typedef struct mk_config {
+  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn, vocab, max_seq;
+  float rms_eps, rope_theta;
+} mk_config;
+
+/* Run-time options (mk_default_options fills the defaults). */
+typedef struct mk_options {
+  int32_t sync_mode;     /* MK_SYNC_SENTINEL (default) or MK_SYNC_COUNTER */
+  int32_t xcd_replicas;  /* copies of re-read activation vectors: 1, 2, 4 or 8 (default 8) */
+  int32_t attn_splits;   /* sequence splits per kv head, 1..64 (0 = choose) */
+  int32_t trace_steps;   /* record a per-instruction time journal for the first N steps (0 = off) */
+  int32_t watchdog_ms;   /* per-wait timeout inside the kernel (default 2000) */
+  int32_t grid;          /* workgroups to launch (0 = CUs x occupancy; larger values are refused) */
+} mk_options;
+
+/* Device pointers to canonical fp16 weights; per-layer entries are host
+ * arrays of n_layers device pointers.  Borrowed only for the duration of
+ * mk_load_weights (the library copies and repacks them). */
+typedef struct mk_weights {
+  const void* embed;
+  const void* final_norm;
+  const void* lm_head;
+  const void* const* attn_norm;
+  const void* const* wq;
+  const void* const* wk;
+  const void* const* wv;
+  const void* const* wo;
+  const void* const* mlp_norm;
+  const void* const* w_gate;
+  const void* const* w_up;
+  const void* const* w_down;
+} mk_weights;
+
+/* Error record written by the device watchdog / NaN check. */
+typedef struct mk_fault {
+  int32_t code;  /* 0, MK_ETIMEOUT or MK_ENAN */
+  int32_t cta, pc, op, step, layer, index, pad;
+} mk_fault;
+
+typedef struct mk_stats {
+  double gpu_ms;             /* duration of the last monokernel launch (HIP events on the bound stream) */
+  int32_t steps;             /* decode steps in that launch */
+  int32_t pos0;              /* first position of that launch */
+  int32_t grid, block, lds_bytes, ring_depth;
+  int64_t stream_bytes;      /* bytes of repacked weights streamed per step (with padding) */
+  int64_t weight_bytes;      /* algorithmic weight bytes per step (no padding) */
+  int64_t kv_bytes_per_pos;  /* K+V bytes per cached position over all layers */
+  int64_t algo_bytes;        /* algorithmic bytes of the last launch: sum over its steps */
+  int32_t n_cu, occupancy;
+  mk_fault fault;
+} mk_stats;
+
+typedef struct mk_ctx mk_ctx;
+
+int mk_default_options(mk_options* opts);
+
+/* Create a context on `device`, enqueueing on `hip_stream` (NULL = default
+ * stream).  Builds the per-workgroup instruction lists and allocates all
+ * device memory the library needs (repacked weights, KV cache, sync buffers). */
+int mk_create(const mk_config* cfg, const mk_options* opts, int device, void* hip_stream, mk_ctx** out);
+
+/* Copy and repack the weights (device pointers).  Synchronises. */
+int mk_load_weights(mk_ctx* ctx, const mk_weights* w);
+
+/* Run the prompt ids[0..n) (host) at positions 0..n-1 through the monokernel,
+ * token by token, filling the KV cache; *t0_out = greedy token after the
+ * prompt.  Resets the generation state.  Synchronises. */
+int mk_prefill(mk_ctx* ctx, const int32_t* ids, int32_t n, int32_t* t0_out);
+
+/* Decode n_steps greedy tokens in ONE launch.  Step s consumes the previous
+ * token at position pos+s.  tokens_out (host, n_steps) receives the tokens;
+ * logits_out (host, n_steps*vocab floats, or NULL) receives every step's
+ * logits.  Synchronises. */
+int mk_decode(mk_ctx* ctx, int32_t n_steps, int32_t* tokens_out, float* logits_out);
+
+/* Like mk_decode, but step s consumes tokens_in[s] (host) instead of the
+ * previous greedy token (teacher forcing).  tokens_out gets each step's argmax. */
+int mk_decode_forced(mk_ctx* ctx, int32_t n_steps, const int32_t* tokens_in,
+                     int32_t* tokens_out, float* logits_out);
+
+/* Prefill then decode: tokens_out (host) receives n_steps + 1 tokens: t0..t_n. */
+int mk_generate(mk_ctx* ctx, const int32_t* ids, int32_t n_prompt, int32_t n_steps, int32_t* tokens_out);
+
+/* Move the generation state back to position pos (1 <= pos <= current): the
+ * KV cache of positions < pos is kept and the token consumed at pos becomes
+ * the next input. */
+int mk_rewind(mk_ctx* ctx, int32_t pos);
+
+/* Current position and the token the next decode step consumes. */
+int mk_position(const mk_ctx* ctx, int32_t* pos, int32_t* next_token);
+
+int mk_get_stats(const mk_ctx* ctx, mk_stats* out);
+
+/* Count words still holding a sentinel in the sync buffers of the last step
+ * of the last launch and in the KV cache positions it wrote.  0 after a good run. */
+int mk_count_sentinels(mk_ctx* ctx, int64_t* count);
+
+/* Copy the time journal of the last launch into host memory.  Each record is
+ * 8 uint32: {cta, step, pc, op | layer << 8, t_wait_lo, t_ready - t_wait,
+ * t_done - t_wait, xcc}, in ticks of the 100 MHz device wall clock; unused
+ * records are zero.  *n_records receives the record count (capacity query if
+ * host_buf is NULL). */
+int mk_read_trace(mk_ctx* ctx, uint32_t* host_buf, int64_t capacity_records, int64_t* n_records);
+
+/* Diagnostics.  Copy n_words 32-bit words of the sync-buffer arena starting
+ * at word_off into host memory.  mk_debug_layout gives the word offsets of
+ * its regions: [0] xa, [1] xm, [2] q, [3] o, [4] m, [5] att_o, [6] att_ml,
+ * [7] argmax keys (uint64), [8] arena size; and [9] per-workgroup progress
+ * words follow in mk_debug_progress. */
+int mk_debug_layout(const mk_ctx* ctx, int64_t* offsets /* [16] */);
+int mk_debug_arena(mk_ctx* ctx, int64_t word_off, int64_t n_words, uint32_t* host);
+/* (step << 16) | (pc + 1) of the last instruction each workgroup finished in
+ * the last launch; host receives `grid` words. */
+int mk_debug_progress(mk_ctx* ctx, uint32_t* host, int32_t capacity);
+
+const char* mk_last_error(const mk_ctx* ctx);
+void mk_destroy(mk_ctx* ctx);
+
+/* ---- GEMV-tanh chain microbenchmark ------------------------------------
+ * stages dependent stages y_i = tanh(W_i y_{i-1}) (W_i fp16 [n, n] row-major,
+ * y fp32) spread over all workgroups of one persistent launch, with the same
+ * streaming and synchronisation as the decoder.  W is a device pointer to
+ * [stages][n][n] fp16 (borrowed during mk_chain_create only). */
+typedef struct mk_chain mk_chain;
+int mk_chain_create(int32_t n, int32_t stages, const void* W, const mk_options* opts,
+                    int device, void* hip_stream, mk_chain** out);
+/* x0: device [n] fp32; y: device [stages][n] fp32 (written).  Synchronises. */
+int mk_chain_run(mk_chain* ch, const float* x0, float* y);
+int mk_chain_stats(const mk_chain* ch, mk_stats* out);
+const char* mk_chain_last_error(const mk_chain* ch);
+void mk_chain_destroy(mk_chain* ch);
+
+/* ---- host-only planning (no GPU needed) --------------------------------- */
+typedef struct mk_plan_info {
+  int32_t n_cta, max_ins_per_cta, n_sync_ids, lds_bytes;
+  int64_t stream_chunks;     /* 1 KB chunks of repacked weights per step */
+  int64_t stream_bytes, weight_bytes;
+  int32_t min_wave_chunks, max_wave_chunks;
+  int32_t attn_splits;
+} mk_plan_info;
+
+/* Build the schedule for n_cta workgroups and check it: every consumed
+ * unit has exactly one producer earlier in the step, counters match the
+ * producer counts, every wave's stream is consistent.  Returns MK_OK or
+ * MK_EINVAL with the reason in *msg (a static string). */
+int mk_plan_check(const mk_config* cfg, const mk_options* opts, int32_t n_cta,
+                  mk_plan_info* info, const char** msg);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H */
