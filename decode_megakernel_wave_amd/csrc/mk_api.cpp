@@ -522,15 +522,9 @@ int mk_create(const mk_config* cfg, const mk_options* opts, int device, void* hi
     return bail(MK_EINVAL);
   }
   // the grid depends on the occupancy, which depends on the LDS size: size it first
-  Plan probe;
-  std::string msg = build_plan(dims_of(cfg), 1, o.attn_splits > 0 ? o.attn_splits : 1, o.xcd_replicas, o.sync_mode, &probe);
-  if (!msg.empty()) {
-    g.err = msg;
-    return bail(MK_EINVAL);
-  }
-  int rc = engine_setup(g, device, hip_stream, &o, probe.lds_bytes);
+  int rc = engine_setup(g, device, hip_stream, &o, plan_lds_bytes(dims_of(cfg)));
   if (rc != MK_OK) return bail(rc);
-  msg = build_plan(dims_of(cfg), g.grid, o.attn_splits, o.xcd_replicas, o.sync_mode, &g.plan);
+  std::string msg = build_plan(dims_of(cfg), g.grid, o.attn_splits, o.xcd_replicas, o.sync_mode, &g.plan);
   if (!msg.empty()) {
     g.err = msg;
     return bail(MK_EINVAL);
@@ -789,15 +783,9 @@ int mk_chain_create(int32_t n, int32_t stages, const void* W, const mk_options* 
   dm.chain = true;
   dm.chain_n = n;
   dm.chain_stages = stages;
-  Plan probe;
-  std::string msg = build_plan(dm, 1, 1, o.xcd_replicas, o.sync_mode, &probe);
-  if (!msg.empty()) {
-    g.err = msg;
-    return bail(MK_EINVAL);
-  }
-  int rc = engine_setup(g, device, hip_stream, &o, probe.lds_bytes);
+  int rc = engine_setup(g, device, hip_stream, &o, plan_lds_bytes(dm));
   if (rc != MK_OK) return bail(rc);
-  msg = build_plan(dm, g.grid, 1, o.xcd_replicas, o.sync_mode, &g.plan);
+  std::string msg = build_plan(dm, g.grid, 1, o.xcd_replicas, o.sync_mode, &g.plan);
   if (!msg.empty()) {
     g.err = msg;
     return bail(MK_EINVAL);

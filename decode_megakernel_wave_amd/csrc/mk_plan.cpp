@@ -129,6 +129,13 @@ bool is_gemv(uint8_t op) {
 
 }  // namespace
 
+int plan_lds_bytes(const Dims& dm) {
+  auto kpad = [](int K) { return ((K + kChunkHalfs - 1) / kChunkHalfs + 7) / 8 * 8 * kChunkHalfs; };
+  if (dm.chain) return lds_bytes_for(kpad(dm.chain_n));
+  const int G = dm.nkv > 0 ? dm.nq / dm.nkv : 1;
+  return lds_bytes_for(std::max({kpad(dm.d), kpad(dm.nq * dm.hd), kpad(dm.f), (G + 2) * dm.hd}));
+}
+
 std::string build_plan(const Dims& dm, int n_cta, int S, int R, int sync_mode, Plan* out) {
   Plan& p = *out;
   p = Plan();
@@ -182,6 +189,7 @@ std::string build_plan(const Dims& dm, int n_cta, int S, int R, int sync_mode, P
     p.weight_bytes = 2 * (per_layer * dm.L + (int64_t)dm.V * dm.d + (int64_t)dm.d * (2 * dm.L + 1) + dm.d);
   }
   p.lds_bytes = lds_bytes_for(kpad_max);
+  if (p.lds_bytes != plan_lds_bytes(dm)) return "internal: LDS footprint mismatch";
   if (p.lds_bytes > 160 * 1024) return "the LDS footprint exceeds 160 KB (row length too large for the ring)";
 
   // producer counts

@@ -46,6 +46,7 @@ struct Plan {
 std::string build_plan(const Dims& dm, int n_cta, int S, int R, int sync_mode, Plan* out);
 std::string check_plan(const Plan& p);
 int lds_bytes_for(int kpad_max);
+int plan_lds_bytes(const Dims& dm);  // LDS footprint of the monokernel for these dims (any grid)
 int choose_splits(int n_cta, int nkv, int max_seq);
 
 }  // namespace mk
