@@ -81,6 +81,7 @@ SIGNATURES = [
     ("mk_get_stats", C.c_int, [C.c_void_p, C.POINTER(mk_stats)]),
     ("mk_count_sentinels", C.c_int, [C.c_void_p, C.POINTER(C.c_int64)]),
     ("mk_read_trace", C.c_int, [C.c_void_p, C.POINTER(C.c_uint32), C.c_int64, C.POINTER(C.c_int64)]),
+    ("mk_debug_streams", C.c_int, [C.c_void_p, C.POINTER(C.c_void_p), C.POINTER(C.c_void_p), C.POINTER(C.c_void_p)]),
     ("mk_debug_layout", C.c_int, [C.c_void_p, C.POINTER(C.c_int64)]),
     ("mk_debug_arena", C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.POINTER(C.c_uint32)]),
     ("mk_debug_progress", C.c_int, [C.c_void_p, C.POINTER(C.c_uint32), C.c_int32]),
@@ -257,6 +258,12 @@ def mk_read_trace(ctx) -> np.ndarray:
     if n.value:
         _check(lib().mk_read_trace(ctx, buf.ctypes.data_as(C.POINTER(C.c_uint32)), n.value, C.byref(n)), ctx)
     return buf
+
+
+def mk_debug_streams(ctx):
+    b, o, n = C.c_void_p(), C.c_void_p(), C.c_void_p()
+    _check(lib().mk_debug_streams(ctx, C.byref(b), C.byref(o), C.byref(n)), ctx)
+    return b.value, o.value, n.value
 
 
 def mk_debug_layout(ctx) -> list:

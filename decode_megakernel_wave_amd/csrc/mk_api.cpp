@@ -711,6 +711,14 @@ int mk_read_trace(mk_ctx* c, uint32_t* host_buf, int64_t capacity, int64_t* n_re
   return MK_OK;
 }
 
+int mk_debug_streams(const mk_ctx* c, const void** base, const void** wave_off, const void** wave_n) {
+  if (!c || !base || !wave_off || !wave_n) return MK_EINVAL;
+  *base = c->g.d_stream;
+  *wave_off = c->g.d_wave_off;
+  *wave_n = c->g.d_wave_n;
+  return MK_OK;
+}
+
 int mk_debug_layout(const mk_ctx* c, int64_t* offsets) {
   if (!c || !offsets) return MK_EINVAL;
   for (int i = 0; i < 16; ++i) offsets[i] = c->layout[i];

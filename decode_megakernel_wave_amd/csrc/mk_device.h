@@ -1,0 +1,172 @@
+// mk_device.h -- gfx950 device primitives of the monokernel: coherent
+// loads/stores for cross-workgroup sync, wavefront DPP reductions, and the
+// per-wavefront LDS weight ring fed by nontemporal global->LDS loads.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mk_layout.h"
+
+namespace mk {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned u4 __attribute__((ext_vector_type(4)));
+typedef unsigned u2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- memory helpers
+// Cross-workgroup traffic (sentinel polls, published outputs, counters) uses
+// system-scope atomics, which gfx950 encodes with both cache-policy bits
+// (sc0 sc1): the access bypasses the CU's L1 and the XCD's L2 and goes to the
+// memory-side coherence point.  This is the HIP counterpart of the uncached
+// read the sentinel needs ("7 - AMD et le monokernel", section 7.3): a poll
+// must never be answered from a cached copy.  Agent-scope (sc1 only) loads were
+// measured to keep returning a stale line on another XCD.
+//
+// Every pointer that reaches device memory is cast to the global address
+// space (1) first, so the compiler emits global_* instead of flat_*
+// instructions: flat operations also count in lgkmcnt, which would make each
+// LDS barrier wait for outstanding global stores to be acknowledged.
+#ifndef MK_SYNC_SCOPE
+#define MK_SYNC_SCOPE __HIP_MEMORY_SCOPE_SYSTEM
+#endif
+#define MK_SCOPE MK_SYNC_SCOPE
+#define MK_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ MK_GLOBAL T* gp(T* p) { return (MK_GLOBAL T*)p; }
+
+__device__ __forceinline__ uint32_t ldc32(const void* p) {
+  return __hip_atomic_load(gp((const uint32_t*)p), __ATOMIC_RELAXED, MK_SCOPE);
+}
+__device__ __forceinline__ uint16_t ldc16(const void* p) {
+  return __hip_atomic_load(gp((const uint16_t*)p), __ATOMIC_RELAXED, MK_SCOPE);
+}
+__device__ __forceinline__ uint64_t ldc64(const void* p) {
+  return __hip_atomic_load(gp((const uint64_t*)p), __ATOMIC_RELAXED, MK_SCOPE);
+}
+__device__ __forceinline__ void stc32(void* p, uint32_t v) {
+  __hip_atomic_store(gp((uint32_t*)p), v, __ATOMIC_RELAXED, MK_SCOPE);
+}
+__device__ __forceinline__ void stc16(void* p, uint16_t v) {
+  __hip_atomic_store(gp((uint16_t*)p), v, __ATOMIC_RELAXED, MK_SCOPE);
+}
+__device__ __forceinline__ void stc64(void* p, uint64_t v) {
+  __hip_atomic_store(gp((uint64_t*)p), v, __ATOMIC_RELAXED, MK_SCOPE);
+}
+__device__ __forceinline__ void stcf(float* p, float v) { stc32(p, __float_as_uint(v)); }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  uint64_t v = (uint64_t)p;
+  uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
+}
+
+// Workgroup barrier that waits for LDS traffic only (HIP's __syncthreads
+// would also drain every outstanding global load, emptying the weight ring).
+__device__ __forceinline__ void cta_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ int xcc_id() {
+  int x;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+  return x & 15;
+}
+
+// ---------------------------------------------------------------- wavefront reductions (DPP)
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xF, false));
+}
+// Sum over the 64 lanes; the result is uniform.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp<0xB1>(v);         // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);         // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);        // row_half_mirror
+  v += dpp<0x140>(v);        // row_mirror: every lane holds its 16-lane row sum
+  v += dpp<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v += dpp<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 1));
+  v = fmaxf(v, __shfl_xor(v, 2));
+  v = fmaxf(v, __shfl_xor(v, 4));
+  v = fmaxf(v, __shfl_xor(v, 8));
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
+// ---------------------------------------------------------------- weight ring
+struct Ring {
+  uint32_t lds;          // LDS byte address of this wavefront's ring
+  const uint8_t* g;      // stream base
+  uint32_t n;            // chunks per step
+  uint32_t issue;        // next chunk (mod n) to request
+  uint32_t slot;         // ring slot holding the next chunk to consume
+};
+
+// The ring is touched only through inline asm (the DMA that fills a slot and
+// the ds_read that drains it), so none of these statements needs a "memory"
+// clobber: a clobber would make the compiler reload every value it keeps in
+// memory (kernel parameters, LDS pointers) after each chunk, and the next
+// lgkmcnt wait would then stall on those scalar loads.  Volatile asm
+// statements keep their program order relative to each other.
+__device__ __forceinline__ void dma_chunk(uint32_t lds_addr, const uint8_t* g, uint32_t voff) {
+  uint32_t save;
+  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
+  g = (const uint8_t*)uniform_ptr(g);
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, %3 nt\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds_addr), "v"(voff), "s"(g));
+}
+
+__device__ __forceinline__ void ring_start(Ring& r) {
+  if (r.n == 0) return;
+  const uint32_t lane16 = lane_id() * 16;
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) {
+    dma_chunk(r.lds + i * 1024, r.g, r.issue * 1024 + lane16);
+    r.issue = (r.issue + 1 == r.n) ? 0 : r.issue + 1;
+  }
+  r.slot = 0;
+}
+
+// Next chunk of this wavefront's stream (16 bytes per lane), then refill its
+// slot.  vmcnt(kRing-1): the oldest of the kRing outstanding DMAs (this slot)
+// has landed; lgkmcnt(0): the slot has been read before it is refilled.
+__device__ __forceinline__ u4 ring_next(Ring& r) {
+  const uint32_t addr = r.lds + r.slot * 1024 + lane_id() * 16;
+  u4 v;
+  asm volatile(
+      "s_waitcnt vmcnt(%1)\n\t"
+      "ds_read_b128 %0, %2\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(v)
+      : "n"(kRing - 1), "v"(addr));
+  dma_chunk(r.lds + r.slot * 1024, r.g, r.issue * 1024 + lane_id() * 16);
+  r.issue = (r.issue + 1 == r.n) ? 0 : r.issue + 1;
+  r.slot = (r.slot + 1 == kRing) ? 0 : r.slot + 1;
+  return v;
+}
+
+__device__ __forceinline__ float dot8(u4 w, const float* a) {
+  const h8 h = __builtin_bit_cast(h8, w);
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s = fmaf((float)h[e], a[e], s);
+  return s;
+}
+
+
+}  // namespace mk

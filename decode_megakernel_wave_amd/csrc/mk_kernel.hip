@@ -35,145 +35,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "mk_device.h"
 #include "mk_layout.h"
 
 using namespace mk;
 
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef unsigned u4 __attribute__((ext_vector_type(4)));
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-
 namespace {
-
-constexpr float kLog2e = 1.4426950408889634f;
-
-// ---------------------------------------------------------------- memory helpers
-// Cross-workgroup traffic (sentinel polls, published outputs, counters) uses
-// system-scope atomics, which gfx950 encodes with both cache-policy bits
-// (sc0 sc1): the access bypasses the CU's L1 and the XCD's L2 and goes to the
-// memory-side coherence point.  This is the HIP counterpart of the uncached
-// read the sentinel needs ("7 - AMD et le monokernel", section 7.3): a poll
-// must never be answered from a cached copy.  Agent-scope (sc1 only) loads were
-// measured to keep returning a stale line on another XCD.
-#define MK_SCOPE __HIP_MEMORY_SCOPE_SYSTEM
-__device__ __forceinline__ uint32_t ldc32(const void* p) {
-  return __hip_atomic_load((const uint32_t*)p, __ATOMIC_RELAXED, MK_SCOPE);
-}
-__device__ __forceinline__ uint16_t ldc16(const void* p) {
-  return __hip_atomic_load((const uint16_t*)p, __ATOMIC_RELAXED, MK_SCOPE);
-}
-__device__ __forceinline__ uint64_t ldc64(const void* p) {
-  return __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, MK_SCOPE);
-}
-__device__ __forceinline__ void stc32(void* p, uint32_t v) {
-  __hip_atomic_store((uint32_t*)p, v, __ATOMIC_RELAXED, MK_SCOPE);
-}
-__device__ __forceinline__ void stc16(void* p, uint16_t v) {
-  __hip_atomic_store((uint16_t*)p, v, __ATOMIC_RELAXED, MK_SCOPE);
-}
-__device__ __forceinline__ void stc64(void* p, uint64_t v) {
-  __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, MK_SCOPE);
-}
-__device__ __forceinline__ void stcf(float* p, float v) { stc32(p, __float_as_uint(v)); }
-
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
-
-__device__ __forceinline__ const void* uniform_ptr(const void* p) {
-  uint64_t v = (uint64_t)p;
-  uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (const void*)(((uint64_t)hi << 32) | lo);
-}
-
-// Workgroup barrier that waits for LDS traffic only (HIP's __syncthreads
-// would also drain every outstanding global load, emptying the weight ring).
-__device__ __forceinline__ void cta_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-__device__ __forceinline__ int xcc_id() {
-  int x;
-  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
-  return x & 15;
-}
-
-// ---------------------------------------------------------------- wavefront reductions (DPP)
-template <int CTRL, int ROWS = 0xF>
-__device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xF, false));
-}
-// Sum over the 64 lanes; the result is uniform.
-__device__ __forceinline__ float wave_sum(float v) {
-  v += dpp<0xB1>(v);         // quad_perm [1,0,3,2]
-  v += dpp<0x4E>(v);         // quad_perm [2,3,0,1]
-  v += dpp<0x141>(v);        // row_half_mirror
-  v += dpp<0x140>(v);        // row_mirror: every lane holds its 16-lane row sum
-  v += dpp<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
-  v += dpp<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
-}
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 1));
-  v = fmaxf(v, __shfl_xor(v, 2));
-  v = fmaxf(v, __shfl_xor(v, 4));
-  v = fmaxf(v, __shfl_xor(v, 8));
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
-}
-
-// ---------------------------------------------------------------- weight ring
-struct Ring {
-  uint32_t lds;          // LDS byte address of this wavefront's ring
-  const uint8_t* g;      // stream base
-  uint32_t n;            // chunks per step
-  uint32_t issue;        // next chunk (mod n) to request
-  uint32_t slot;         // ring slot holding the next chunk to consume
-};
-
-__device__ __forceinline__ void dma_chunk(uint32_t lds_addr, const uint8_t* g, uint32_t voff) {
-  uint32_t save;
-  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
-  g = (const uint8_t*)uniform_ptr(g);
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %2, %3 nt\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(save)
-      : "s"(lds_addr), "v"(voff), "s"(g)
-      : "memory");
-}
-
-__device__ __forceinline__ void ring_start(Ring& r) {
-  if (r.n == 0) return;
-  const uint32_t lane16 = lane_id() * 16;
-#pragma unroll
-  for (int i = 0; i < kRing; ++i) {
-    dma_chunk(r.lds + i * 1024, r.g, r.issue * 1024 + lane16);
-    r.issue = (r.issue + 1 == r.n) ? 0 : r.issue + 1;
-  }
-  r.slot = 0;
-}
-
-// Next chunk of this wavefront's stream (16 bytes per lane), then refill its slot.
-typedef __attribute__((address_space(3))) const u4* lds_u4_ptr;
-__device__ __forceinline__ u4 ring_next(Ring& r) {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kRing - 1) : "memory");
-  const u4 v = *(lds_u4_ptr)(uintptr_t)(r.lds + r.slot * 1024 + lane_id() * 16);
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  dma_chunk(r.lds + r.slot * 1024, r.g, r.issue * 1024 + lane_id() * 16);
-  r.issue = (r.issue + 1 == r.n) ? 0 : r.issue + 1;
-  r.slot = (r.slot + 1 == kRing) ? 0 : r.slot + 1;
-  return v;
-}
-
-__device__ __forceinline__ float dot8(u4 w, const float* a) {
-  const h8 h = __builtin_bit_cast(h8, w);
-  float s = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) s = fmaf((float)h[e], a[e], s);
-  return s;
-}
 
 // ---------------------------------------------------------------- per-workgroup context
 struct Smem {
@@ -254,7 +121,7 @@ __device__ __forceinline__ void counter_wait(Cx& c, int sid, int n_in, int op, i
     const uint32_t target = (uint32_t)n_in * (uint32_t)(c.step + 1);
     uint32_t* ctr = c.kp->counters + sid;
     int tries = 0;
-    while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, MK_SCOPE) < target) {
+    while (__hip_atomic_load(gp(ctr), __ATOMIC_ACQUIRE, MK_SCOPE) < target) {
       // exponential back-off ("8 - Ecrire son megakernel", section 8.5)
       const int k = tries < 4 ? (1 << tries) : 16;
       for (int i = 0; i < k; ++i) __builtin_amdgcn_s_sleep(1);
@@ -271,7 +138,7 @@ __device__ __forceinline__ void counter_signal(Cx& c, int sid) {
   if (sentinel_mode(c) || sid < 0) return;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   cta_sync();
-  if (c.tid == 0) __hip_atomic_fetch_add(c.kp->counters + sid, 1u, __ATOMIC_RELAXED, MK_SCOPE);
+  if (c.tid == 0) __hip_atomic_fetch_add(gp(c.kp->counters + sid), 1u, __ATOMIC_RELAXED, MK_SCOPE);
 }
 
 // Poll one fp32 word until it stops being the sentinel (sentinel mode) or
@@ -306,7 +173,7 @@ __device__ __forceinline__ float stage_vec(Cx& c, const float* src, float* dst, 
 #pragma unroll
       for (int j = 0; j < 4; ++j) v[k * 4 + j] = (i + j < n) ? ldc32(src + i + j) : 0u;
       if (gain && i < n) {
-        const uint2 w = *(const uint2*)(gain + i);
+        const u2 w = *gp((const u2*)(gain + i));
         const _Float16* h = (const _Float16*)&w;
 #pragma unroll
         for (int j = 0; j < 4; ++j) g[k * 4 + j] = (float)h[j];
@@ -316,15 +183,24 @@ __device__ __forceinline__ float stage_vec(Cx& c, const float* src, float* dst, 
       }
     }
     if (sentinel_mode(c)) {
+      // re-poll every element still holding the sentinel in one batch, so a
+      // late producer costs one more round trip, not one per element
+      for (;;) {
+        bool pending = false;
 #pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        const int i = base + (k / 4) * kThreads * 4 + (k % 4);
-        while (i < n && v[k] == kSent32 && !c.fail) {
-          if (expired(c, op, layer, i)) {
-            c.fail = true;
-            break;
-          }
-          v[k] = ldc32(src + i);
+        for (int k = 0; k < kPer; ++k) {
+          const int i = base + (k / 4) * kThreads * 4 + (k % 4);
+          pending |= i < n && v[k] == kSent32;
+        }
+        if (!pending || c.fail) break;
+        if (expired(c, op, layer, base)) {
+          c.fail = true;
+          break;
+        }
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+          const int i = base + (k / 4) * kThreads * 4 + (k % 4);
+          if (i < n && v[k] == kSent32) v[k] = ldc32(src + i);
         }
       }
     }
@@ -353,8 +229,8 @@ __device__ __forceinline__ float stage_row_h(Cx& c, const uint16_t* src, float* 
   for (int i = c.tid * 4; i < npad; i += kThreads * 4) {
     f4 v = {0.f, 0.f, 0.f, 0.f};
     if (i < n) {
-      const uint2 w = *(const uint2*)(src + i);
-      const uint2 gw = *(const uint2*)(gain + i);
+      const u2 w = *gp((const u2*)(src + i));
+      const u2 gw = *gp((const u2*)(gain + i));
       const _Float16* h = (const _Float16*)&w;
       const _Float16* gh = (const _Float16*)&gw;
 #pragma unroll
@@ -420,12 +296,24 @@ __device__ __forceinline__ void gemv(Cx& c, Ring& ring, const Ins& in, const flo
   if (ks > 1) {
     cta_sync();
     if (ki == 0) {
-      for (int u = gi; u < in.nu; u += rg) {
+      // one unit per lane: sum its ks partials (fixed order), then hand each
+      // sum to the epilogue as a uniform value
+      const int mine = units_of_group(in.nu, rg, gi);
+      for (int base = 0; base < mine; base += 64) {
+        const int j = base + c.lane;
         float s0 = 0.f, s1 = 0.f;
-        for (int k = 0; k < ks; ++k) s0 += c.sm.scratch[(u * upr) * ks + k];
-        if (upr == 2)
-          for (int k = 0; k < ks; ++k) s1 += c.sm.scratch[(u * upr + 1) * ks + k];
-        epi(u, s0, s1);
+        if (j < mine) {
+          const int u = gi + j * rg;
+          for (int k = 0; k < ks; ++k) s0 += c.sm.scratch[(u * upr) * ks + k];
+          if (upr == 2)
+            for (int k = 0; k < ks; ++k) s1 += c.sm.scratch[(u * upr + 1) * ks + k];
+        }
+        const int cnt = min(64, mine - base);
+        for (int t = 0; t < cnt; ++t) {
+          const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s0), t));
+          const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s1), t));
+          epi(gi + (base + t) * rg, a, b);
+        }
       }
     }
   }
@@ -469,7 +357,7 @@ __device__ __forceinline__ float stage_layer_input(Cx& c, int l, int npad, const
 __device__ __forceinline__ void stage_resid(Cx& c, const float* src, const uint16_t* emb, int u0, int nu, int op, int layer) {
   for (int i = c.tid; i < nu; i += kThreads) {
     float v;
-    if (emb) v = (float)__builtin_bit_cast(_Float16, emb[u0 + i]);
+    if (emb) v = (float)__builtin_bit_cast(_Float16, *gp(emb + u0 + i));
     else v = poll_f32(c, src + u0 + i, op, layer);
     c.sm.resid[i] = v;
   }
@@ -492,7 +380,7 @@ __device__ __forceinline__ void op_qkv(Cx& c, Ring& ring, const Ins& in) {
       const bool isq = g < nqh;
       if (!isq) g -= nqh;
       const int head = g / hh, i = g % hh;
-      const float cs = rope[2 * i], sn = rope[2 * i + 1];
+      const float cs = *gp(rope + 2 * i), sn = *gp(rope + 2 * i + 1);
       const float ra = a * cs - b * sn, rb = a * sn + b * cs;
       if (isq) {
         float* q = buf_at(kp.q, c.e, l, 0) + head * kp.hd + i;
@@ -556,8 +444,9 @@ __device__ __forceinline__ void op_att(Cx& c, const Ins& in) {
     }
     cta_sync();
     if (ui == 0) mark_ready(c);
-    // each wavefront: positions t0 + wave, t0 + wave + kWaves, ...
-    constexpr int kMaxG = 8, kMaxDpl = 4;
+    // each wavefront: positions t0 + wave, t0 + wave + kWaves, ... in batches
+    // of kBatch whose K/V loads are all issued before any score is computed
+    constexpr int kMaxG = 8, kMaxDpl = 4, kBatch = 4;
     const int dpl = hd / 64;  // dims per lane
     float m[kMaxG], lsum[kMaxG], o[kMaxG][kMaxDpl];
 #pragma unroll
@@ -569,37 +458,47 @@ __device__ __forceinline__ void op_att(Cx& c, const Ins& in) {
     }
     const uint16_t* kbase = kp.kc + ((int64_t)l * kp.nkv + g) * kp.max_seq * hd + c.lane * dpl;
     const uint16_t* vbase = kp.vc + ((int64_t)l * kp.nkv + g) * kp.max_seq * hd + c.lane * dpl;
-    for (int t = t0 + c.wave; t < t1; t += kWaves) {
-      float kv[kMaxDpl], vv[kMaxDpl];
-      if (t == c.pos) {
+    for (int tb = t0 + c.wave; tb < t1; tb += kWaves * kBatch) {
+      float kv[kBatch][kMaxDpl], vv[kBatch][kMaxDpl];
 #pragma unroll
-        for (int k = 0; k < kMaxDpl; ++k)
-          if (k < dpl) { kv[k] = kcur[c.lane * dpl + k]; vv[k] = vcur[c.lane * dpl + k]; }
-      } else {
-        const uint16_t* kr = kbase + (int64_t)t * hd;
-        const uint16_t* vr = vbase + (int64_t)t * hd;
+      for (int b = 0; b < kBatch; ++b) {
+        const int t = tb + b * kWaves;
+        if (t >= t1) break;
+        if (t == c.pos) {
 #pragma unroll
-        for (int k = 0; k < kMaxDpl; ++k)
-          if (k < dpl) {
-            kv[k] = (float)__builtin_bit_cast(_Float16, kr[k]);
-            vv[k] = (float)__builtin_bit_cast(_Float16, vr[k]);
-          }
+          for (int k = 0; k < kMaxDpl; ++k)
+            if (k < dpl) { kv[b][k] = kcur[c.lane * dpl + k]; vv[b][k] = vcur[c.lane * dpl + k]; }
+        } else {
+          const uint16_t* kr = kbase + (int64_t)t * hd;
+          const uint16_t* vr = vbase + (int64_t)t * hd;
+#pragma unroll
+          for (int k = 0; k < kMaxDpl; ++k)
+            if (k < dpl) {
+              kv[b][k] = (float)__builtin_bit_cast(_Float16, *gp(kr + k));
+              vv[b][k] = (float)__builtin_bit_cast(_Float16, *gp(vr + k));
+            }
+        }
       }
 #pragma unroll
-      for (int j = 0; j < kMaxG; ++j) {
-        if (j >= G) break;
-        float s = 0.f;
+      for (int b = 0; b < kBatch; ++b) {
+        const int t = tb + b * kWaves;
+        if (t >= t1) break;
 #pragma unroll
-        for (int k = 0; k < kMaxDpl; ++k)
-          if (k < dpl) s += qs[j * hd + c.lane * dpl + k] * kv[k];
-        s = wave_sum(s);
-        const float mn = fmaxf(m[j], s);
-        const float a = exp2f(m[j] - mn), p = exp2f(s - mn);
-        lsum[j] = lsum[j] * a + p;
+        for (int j = 0; j < kMaxG; ++j) {
+          if (j >= G) break;
+          float s = 0.f;
 #pragma unroll
-        for (int k = 0; k < kMaxDpl; ++k)
-          if (k < dpl) o[j][k] = o[j][k] * a + p * vv[k];
-        m[j] = mn;
+          for (int k = 0; k < kMaxDpl; ++k)
+            if (k < dpl) s += qs[j * hd + c.lane * dpl + k] * kv[b][k];
+          s = wave_sum(s);
+          const float mn = fmaxf(m[j], s);
+          const float a = exp2f(m[j] - mn), p = exp2f(s - mn);
+          lsum[j] = lsum[j] * a + p;
+#pragma unroll
+          for (int k = 0; k < kMaxDpl; ++k)
+            if (k < dpl) o[j][k] = o[j][k] * a + p * vv[b][k];
+          m[j] = mn;
+        }
       }
     }
     // combine the wavefronts: scratch [wave][G][hd + 2]
@@ -669,16 +568,18 @@ __device__ __forceinline__ void op_red(Cx& c, const Ins& in) {
 #pragma unroll
       for (int d = 0; d < kRedDims; ++d) raw[2 + d] = ldc32(ov + d);
       if (sentinel_mode(c)) {
+        for (;;) {
+          bool pending = false;
 #pragma unroll
-        for (int k = 0; k < 2 + kRedDims; ++k) {
-          const float* p = k < 2 ? ml + k : ov + (k - 2);
-          while (raw[k] == kSent32 && !c.fail) {
-            if (expired(c, OP_RED, l, k)) {
-              c.fail = true;
-              break;
-            }
-            raw[k] = ldc32(p);
+          for (int k = 0; k < 2 + kRedDims; ++k) pending |= raw[k] == kSent32;
+          if (!pending || c.fail) break;
+          if (expired(c, OP_RED, l, U)) {
+            c.fail = true;
+            break;
           }
+#pragma unroll
+          for (int k = 0; k < 2 + kRedDims; ++k)
+            if (raw[k] == kSent32) raw[k] = ldc32(k < 2 ? ml + k : ov + (k - 2));
         }
       }
       ms = __uint_as_float(raw[0]);
@@ -768,7 +669,7 @@ __device__ __forceinline__ void op_lmhead(Cx& c, Ring& ring, const Ins& in) {
     bool nan = false;
     gemv_dispatch(c, ring, in, c.sm.vec, scale, [&](int u, float y, float) {
       const int row = in.u0 + u;
-      if (lo && c.lane == 0) lo[row] = y;
+      if (lo && c.lane == 0) *gp(lo + row) = y;
       if (y != y) nan = true;
       else if (bi < 0 || y > bv || (y == bv && row < bi)) { bv = y; bi = row; }
     });
@@ -787,7 +688,7 @@ __device__ __forceinline__ void op_lmhead(Cx& c, Ring& ring, const Ins& in) {
   cta_sync();
   if (c.wave == 0 && c.lane < kp.R) stc64(slot + c.lane * kp.lmp_rs, best);
   if (!sentinel_mode(c) && c.tid == 0)
-    __hip_atomic_fetch_add(kp.counters + in.sync_out, 1u, __ATOMIC_RELAXED, MK_SCOPE);
+    __hip_atomic_fetch_add(gp(kp.counters + in.sync_out), 1u, __ATOMIC_RELAXED, MK_SCOPE);
 }
 
 __device__ __forceinline__ void op_argmax(Cx& c, const Ins& in) {
@@ -808,7 +709,7 @@ __device__ __forceinline__ void op_argmax(Cx& c, const Ins& in) {
       }
     }
     k = max(k, v);
-    if (kp.dbg) kp.dbg[(int64_t)c.cta * kThreads + i] = v;
+    if (kp.dbg) *gp(kp.dbg + (int64_t)c.cta * kThreads + i) = v;
   }
   // workgroup max
   for (int off = 32; off > 0; off >>= 1) {
@@ -824,7 +725,7 @@ __device__ __forceinline__ void op_argmax(Cx& c, const Ins& in) {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   int tok = (int)(0xFFFFFFFFu - (uint32_t)best);
   if (tok < 0 || tok >= kp.V) tok = 0;  // only on an aborted run
-  if (c.cta == 0 && c.tid == 0) kp.tokens[c.step] = tok;
+  if (c.cta == 0 && c.tid == 0) *gp(kp.tokens + c.step) = tok;
   c.tok = tok;
 }
 
@@ -835,7 +736,7 @@ __device__ __forceinline__ void op_chain(Cx& c, Ring& ring, const Ins& in) {
   if (!sentinel_mode(c)) cta_sync();
   if (i == 0) {
     for (int k = c.tid * 4; k < in.kpad; k += kThreads * 4)
-      *(f4*)(c.sm.vec + k) = k < n ? *(const f4*)(kp.x0 + k) : f4{0.f, 0.f, 0.f, 0.f};
+      *(f4*)(c.sm.vec + k) = k < n ? *gp((const f4*)(kp.x0 + k)) : f4{0.f, 0.f, 0.f, 0.f};
   } else {
     stage_vec(c, buf_at(kp.y, 0, i - 1, c.rep), c.sm.vec, n, in.kpad, nullptr, OP_CHAIN, i);
   }
@@ -921,11 +822,11 @@ __global__ __launch_bounds__(kThreads, 1) void mk_monokernel(const KParams* __re
         case OP_CHAIN: op_chain(c, ring, in); break;
         default: break;
       }
-      if (c.tid == 0) kp.progress[c.cta] = ((uint32_t)step << 16) | (uint32_t)(c.pc + 1);
+      if (c.tid == 0) *gp(kp.progress + c.cta) = ((uint32_t)step << 16) | (uint32_t)(c.pc + 1);
       if (cta_failed(c)) goto done;
       if (tr && c.tid == 0) {
         const uint64_t t_done = __builtin_amdgcn_s_memrealtime();
-        uint32_t* r = trace + (int64_t)c.pc * 8;
+        MK_GLOBAL uint32_t* r = gp(trace + (int64_t)c.pc * 8);
         r[0] = (uint32_t)c.cta;
         r[1] = (uint32_t)step;
         r[2] = (uint32_t)c.pc;

@@ -112,7 +112,9 @@ void choose_split(int nu, int upr, int kc_raw, int* ks_out, int* cps_out) {
     if (cps > 4) continue;
     if (ks > 1 && (int64_t)nu * upr * ks > kScratchFloats) continue;
     const int rg = kWaves / ks;
-    const int load = ((nu + rg - 1) / rg) * upr * cps;
+    // busiest wavefront: its chunks plus one chunk-equivalent per row for the
+    // wavefront reduction, plus the cross-wavefront merge when K is split
+    const int load = ((nu + rg - 1) / rg) * upr * (cps + 1) + (ks > 1 ? 2 : 0);
     if (best < 0 || load < best) {
       best = load;
       best_ks = ks;

@@ -171,6 +171,10 @@ int mk_debug_arena(mk_ctx* ctx, int64_t word_off, int64_t n_words, uint32_t* hos
  * the last launch; host receives `grid` words. */
 int mk_debug_progress(mk_ctx* ctx, uint32_t* host, int32_t capacity);
 
+/* Device addresses of the repacked weight streams: base, per-wavefront chunk
+ * offsets [grid * 8] (int64) and chunk counts [grid * 8] (int32). */
+int mk_debug_streams(const mk_ctx* ctx, const void** base, const void** wave_off, const void** wave_n);
+
 const char* mk_last_error(const mk_ctx* ctx);
 void mk_destroy(mk_ctx* ctx);
 
