@@ -91,6 +91,7 @@ SIGNATURES = [
                                   C.POINTER(C.c_void_p)]),
     ("mk_chain_run", C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p]),
     ("mk_chain_stats", C.c_int, [C.c_void_p, C.POINTER(mk_stats)]),
+    ("mk_chain_read_trace", C.c_int, [C.c_void_p, C.POINTER(C.c_uint32), C.c_int64, C.POINTER(C.c_int64)]),
     ("mk_chain_last_error", C.c_char_p, [C.c_void_p]),
     ("mk_chain_destroy", None, [C.c_void_p]),
     ("mk_plan_check", C.c_int, [C.POINTER(mk_config), C.POINTER(mk_options), C.c_int32, C.POINTER(mk_plan_info),
@@ -311,6 +312,16 @@ def mk_chain_stats(ch) -> dict:
     s = mk_stats()
     _check(lib().mk_chain_stats(ch, C.byref(s)), ch, chain=True)
     return _stats_dict(s)
+
+
+def mk_chain_read_trace(ch) -> np.ndarray:
+    n = C.c_int64()
+    _check(lib().mk_chain_read_trace(ch, None, 0, C.byref(n)), ch, chain=True)
+    buf = np.zeros((n.value, 8), dtype=np.uint32)
+    if n.value:
+        _check(lib().mk_chain_read_trace(ch, buf.ctypes.data_as(C.POINTER(C.c_uint32)), n.value, C.byref(n)),
+               ch, chain=True)
+    return buf
 
 
 def mk_chain_destroy(ch) -> None:

@@ -13,7 +13,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/mk.h"
+#include "mk.h"
 #include "mk_layout.h"
 #include "mk_plan.h"
 
@@ -63,7 +63,7 @@ struct Engine {
   uint32_t* d_abort = nullptr;
   uint32_t* d_trace = nullptr;
   uint32_t* d_progress = nullptr;
-  uint64_t* d_dbg = nullptr;
+  uint64_t* d_ts = nullptr;
   int64_t trace_words = 0;
   int32_t* d_tokens = nullptr;
   int32_t* d_forced = nullptr;
@@ -168,7 +168,7 @@ int upload_plan(Engine& g) {
   CHK(g.alloc(&g.d_abort, sizeof(uint32_t)));
   CHK(g.alloc(&g.d_kp, sizeof(KParams)));
   CHK(g.alloc(&g.d_progress, (size_t)g.grid * 4));
-  CHK(g.alloc(&g.d_dbg, (size_t)g.grid * kThreads * 8));
+  CHK(g.alloc(&g.d_ts, (size_t)g.grid * p.max_ins * 8 * 8));
   if (g.opt.trace_steps > 0) {
     g.trace_words = (int64_t)g.grid * g.opt.trace_steps * p.max_ins * 8;
     CHK(g.alloc(&g.d_trace, g.trace_words * 4));
@@ -214,7 +214,7 @@ void fill_common_params(Engine& g, KParams& k) {
   k.abort_flag = g.d_abort;
   k.trace = g.d_trace;
   k.progress = g.d_progress;
-  k.dbg = getenv("MK_DEBUG_ARGMAX") ? g.d_dbg : nullptr;
+  k.ts = getenv("MK_DEBUG_TS") ? g.d_ts : nullptr;
   k.trace_steps = g.opt.trace_steps;
   k.max_ins = p.max_ins;
   k.S = p.S;
@@ -222,6 +222,7 @@ void fill_common_params(Engine& g, KParams& k) {
   k.sync_mode = p.sync_mode;
   k.lm_slots = p.lm_slots;
   k.watchdog_ticks = (uint64_t)g.opt.watchdog_ms * 100000ull;  // 100 MHz wall clock
+  k.poll_sleep = getenv("MK_POLL_SLEEP") ? atoi(getenv("MK_POLL_SLEEP")) : 0;
 }
 
 // Reset sync state, launch once, wait, collect the fault record.
@@ -737,12 +738,6 @@ int mk_debug_progress(mk_ctx* c, uint32_t* host, int32_t capacity) {
   return MK_OK;
 }
 
-int mk_debug_argmax_reads(mk_ctx* c, uint64_t* host, int64_t capacity) {
-  if (!c || !host || capacity < (int64_t)c->g.grid * kThreads) return MK_EINVAL;
-  HIPCHK(c->g, hipMemcpy(host, c->g.d_dbg, (size_t)c->g.grid * kThreads * 8, hipMemcpyDeviceToHost));
-  return MK_OK;
-}
-
 const char* mk_last_error(const mk_ctx* c) {
   if (!c) return g_create_error.c_str();
   return c->g.err.c_str();
@@ -839,6 +834,25 @@ int mk_chain_run(mk_chain* ch, const float* x0, float* y) {
   HIPCHK(g, hipMemcpy2DAsync(y, (size_t)ch->n * 4, ch->y.p, (size_t)ch->y.ls * 4, (size_t)ch->n * 4, ch->stages,
                              hipMemcpyDeviceToDevice, g.stream));
   HIPCHK(g, hipStreamSynchronize(g.stream));
+  return MK_OK;
+}
+
+int mk_chain_read_trace(mk_chain* ch, uint32_t* host_buf, int64_t capacity, int64_t* n_records) {
+  if (!ch || !n_records) return MK_EINVAL;
+  Engine& g = ch->g;
+  *n_records = g.trace_words / 8;
+  if (!host_buf) return MK_OK;
+  if (capacity < *n_records) return g.fail(MK_EINVAL, "trace buffer too small");
+  if (g.trace_words) HIPCHK(g, hipMemcpy(host_buf, g.d_trace, g.trace_words * 4, hipMemcpyDeviceToHost));
+  return MK_OK;
+}
+
+int mk_chain_debug_ts(mk_chain* ch, uint64_t* host, int64_t capacity) {
+  if (!ch || !host) return MK_EINVAL;
+  Engine& g = ch->g;
+  const int64_t n = (int64_t)g.grid * g.plan.max_ins * 8;
+  if (capacity < n) return MK_EINVAL;
+  HIPCHK(g, hipMemcpy(host, g.d_ts, n * 8, hipMemcpyDeviceToHost));
   return MK_OK;
 }
 

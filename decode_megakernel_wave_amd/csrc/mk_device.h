@@ -68,9 +68,15 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
   return (const void*)(((uint64_t)hi << 32) | lo);
 }
 
-// Workgroup barrier that waits for LDS traffic only (HIP's __syncthreads
-// would also drain every outstanding global load, emptying the weight ring).
-__device__ __forceinline__ void cta_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Workgroup barrier ordering LDS traffic only: the fences name the "local"
+// address space, so outstanding global loads (the weight ring) and stores
+// stay in flight across it, and the compiler may keep values it loaded from
+// global memory in registers (no blanket memory clobber).
+__device__ __forceinline__ void cta_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 __device__ __forceinline__ int xcc_id() {
   int x;
@@ -158,6 +164,42 @@ __device__ __forceinline__ u4 ring_next(Ring& r) {
   r.issue = (r.issue + 1 == r.n) ? 0 : r.issue + 1;
   r.slot = (r.slot + 1 == kRing) ? 0 : r.slot + 1;
   return v;
+}
+
+// Next N chunks (N <= 4) with one LDS wait: vmcnt(kRing-N) means the N
+// oldest DMAs (these slots) have landed.
+template <int N>
+__device__ __forceinline__ void ring_read(Ring& r, u4 (&v)[4]) {
+  static_assert(N >= 1 && N <= 4 && N <= kRing, "ring_read reads 1..4 chunks");
+  uint32_t a[4];
+  uint32_t slot = r.slot;
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    a[k] = r.lds + slot * 1024 + lane_id() * 16;
+    slot = (slot + 1 == kRing) ? 0 : slot + 1;
+  }
+  if constexpr (N == 1) {
+    asm volatile("s_waitcnt vmcnt(%1)\n\tds_read_b128 %0, %2\n\ts_waitcnt lgkmcnt(0)"
+                 : "=v"(v[0]) : "n"(kRing - 1), "v"(a[0]));
+  } else if constexpr (N == 2) {
+    asm volatile("s_waitcnt vmcnt(%2)\n\tds_read_b128 %0, %3\n\tds_read_b128 %1, %4\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]) : "n"(kRing - 2), "v"(a[0]), "v"(a[1]));
+  } else if constexpr (N == 3) {
+    asm volatile("s_waitcnt vmcnt(%3)\n\tds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]) : "n"(kRing - 3), "v"(a[0]), "v"(a[1]), "v"(a[2]));
+  } else {
+    asm volatile("s_waitcnt vmcnt(%4)\n\tds_read_b128 %0, %5\n\tds_read_b128 %1, %6\n\tds_read_b128 %2, %7\n\t"
+                 "ds_read_b128 %3, %8\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+                 : "n"(kRing - 4), "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+  }
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    dma_chunk(r.lds + r.slot * 1024, r.g, r.issue * 1024 + lane_id() * 16);
+    r.issue = (r.issue + 1 == r.n) ? 0 : r.issue + 1;
+    r.slot = (r.slot + 1 == kRing) ? 0 : r.slot + 1;
+  }
 }
 
 __device__ __forceinline__ float dot8(u4 w, const float* a) {

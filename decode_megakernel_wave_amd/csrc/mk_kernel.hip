@@ -94,17 +94,31 @@ __device__ __forceinline__ bool expired(Cx& c, int op, int layer, int index) {
   return false;
 }
 
+// Back-off between failed poll rounds: limits the coherent-load traffic that
+// hundreds of waiting workgroups put on the memory system.
+__device__ __forceinline__ void poll_pause(const Cx& c) {
+  for (int i = 0; i < c.kp->poll_sleep; ++i) __builtin_amdgcn_s_sleep(1);
+}
+
 // Workgroup-wide OR of the per-thread failure flags (also a barrier).
 __device__ __forceinline__ bool cta_failed(Cx& c) {
   const uint64_t b = __ballot(c.fail);
   uint32_t* f = c.sm.flags + c.flag_parity * kWaves;
   if (c.lane == 0) f[c.wave] = b != 0;
   cta_sync();
-  bool any = false;
+  uint32_t any = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) any |= f[w] != 0;
+  for (int w = 0; w < kWaves; ++w) any |= f[w];
   c.flag_parity ^= 1;
-  return any;
+  // the value is the same in every lane; say so, or every branch on it (and
+  // the whole instruction loop) would be compiled as divergent
+  return __builtin_amdgcn_readfirstlane(any) != 0;
+}
+
+// Diagnostics: fine timestamp k of the current instruction (step 0, thread 0).
+__device__ __forceinline__ void ts_mark(const Cx& c, int k) {
+  if (c.kp->ts && c.step == 0 && c.tid == 0)
+    *gp(c.kp->ts + ((int64_t)c.cta * c.kp->max_ins + c.pc) * 8 + k) = __builtin_amdgcn_s_memrealtime();
 }
 
 // Trace: time at which an instruction's inputs were staged.
@@ -151,6 +165,7 @@ __device__ __forceinline__ float poll_f32(Cx& c, const float* p, int op, int lay
         c.fail = true;
         break;
       }
+      poll_pause(c);
       v = ldc32(p);
     }
   }
@@ -197,6 +212,7 @@ __device__ __forceinline__ float stage_vec(Cx& c, const float* src, float* dst, 
           c.fail = true;
           break;
         }
+        poll_pause(c);
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
           const int i = base + (k / 4) * kThreads * 4 + (k % 4);
@@ -276,13 +292,17 @@ __device__ __forceinline__ void gemv(Cx& c, Ring& ring, const Ins& in, const flo
 #pragma unroll
     for (int e = 0; e < 8; ++e) act[k][e] *= scale;
   }
+  ts_mark(c, 5);
   for (int u = gi; u < in.nu; u += rg) {
     float r0 = 0.f, r1 = 0.f;
+    u4 w[4];
+    ring_read<CPS>(ring, w);
 #pragma unroll
-    for (int k = 0; k < CPS; ++k) r0 += dot8(ring_next(ring), act[k]);
+    for (int k = 0; k < CPS; ++k) r0 += dot8(w[k], act[k]);
     if (upr == 2) {
+      ring_read<CPS>(ring, w);
 #pragma unroll
-      for (int k = 0; k < CPS; ++k) r1 += dot8(ring_next(ring), act[k]);
+      for (int k = 0; k < CPS; ++k) r1 += dot8(w[k], act[k]);
     }
     r0 = wave_sum(r0);
     if (upr == 2) r1 = wave_sum(r1);
@@ -293,6 +313,7 @@ __device__ __forceinline__ void gemv(Cx& c, Ring& ring, const Ins& in, const flo
       if (upr == 2) c.sm.scratch[(u * upr + 1) * ks + ki] = r1;
     }
   }
+  ts_mark(c, 6);
   if (ks > 1) {
     cta_sync();
     if (ki == 0) {
@@ -333,11 +354,13 @@ __device__ __forceinline__ void gemv_dispatch(Cx& c, Ring& ring, const Ins& in, 
 // for RMSNorm inputs, the workgroup sum of squares of the n staged values
 // (ss_thread = this thread's share).  Returns the RMSNorm scale (1 without norm).
 __device__ __forceinline__ float finish_staging(Cx& c, int n, bool norm, float ss_thread) {
+  ts_mark(c, 1);
   if (norm) {
     const float p = wave_sum(ss_thread);
     if (c.lane == 0) c.sm.wsum[c.wave] = p;
   }
   cta_sync();
+  ts_mark(c, 2);
   mark_ready(c);
   if (!norm) return 1.0f;
   float ss = 0.f;
@@ -577,6 +600,7 @@ __device__ __forceinline__ void op_red(Cx& c, const Ins& in) {
             c.fail = true;
             break;
           }
+          poll_pause(c);
 #pragma unroll
           for (int k = 0; k < 2 + kRedDims; ++k)
             if (raw[k] == kSent32) raw[k] = ldc32(k < 2 ? ml + k : ov + (k - 2));
@@ -705,11 +729,11 @@ __device__ __forceinline__ void op_argmax(Cx& c, const Ins& in) {
           c.fail = true;
           break;
         }
+        poll_pause(c);
         v = ldc64(src + i);
       }
     }
     k = max(k, v);
-    if (kp.dbg) *gp(kp.dbg + (int64_t)c.cta * kThreads + i) = v;
   }
   // workgroup max
   for (int off = 32; off > 0; off >>= 1) {
@@ -723,7 +747,7 @@ __device__ __forceinline__ void op_argmax(Cx& c, const Ins& in) {
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) best = max(best, c.sm.keys[w]);
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  int tok = (int)(0xFFFFFFFFu - (uint32_t)best);
+  int tok = __builtin_amdgcn_readfirstlane((int)(0xFFFFFFFFu - (uint32_t)best));
   if (tok < 0 || tok >= kp.V) tok = 0;  // only on an aborted run
   if (c.cta == 0 && c.tid == 0) *gp(kp.tokens + c.step) = tok;
   c.tok = tok;
@@ -810,6 +834,7 @@ __global__ __launch_bounds__(kThreads, 1) void mk_monokernel(const KParams* __re
         t_wait = __builtin_amdgcn_s_memrealtime();
         if (c.tid == 0) c.sm.misc[0] = 0;
       }
+      ts_mark(c, 0);
       switch (in.op) {
         case OP_QKV: op_qkv(c, ring, in); break;
         case OP_ATT: op_att(c, in); break;
@@ -822,8 +847,10 @@ __global__ __launch_bounds__(kThreads, 1) void mk_monokernel(const KParams* __re
         case OP_CHAIN: op_chain(c, ring, in); break;
         default: break;
       }
+      ts_mark(c, 3);
       if (c.tid == 0) *gp(kp.progress + c.cta) = ((uint32_t)step << 16) | (uint32_t)(c.pc + 1);
       if (cta_failed(c)) goto done;
+      ts_mark(c, 4);
       if (tr && c.tid == 0) {
         const uint64_t t_done = __builtin_amdgcn_s_memrealtime();
         MK_GLOBAL uint32_t* r = gp(trace + (int64_t)c.pc * 8);
@@ -840,7 +867,7 @@ __global__ __launch_bounds__(kThreads, 1) void mk_monokernel(const KParams* __re
     if (kp.forced && step + 1 < kp.n_steps) c.tok = kp.forced[step + 1];
   }
 done:
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(0)");
 }
 
 // ---------------------------------------------------------------- helper kernels

@@ -101,13 +101,15 @@ struct KParams {
   uint32_t* abort_flag;
   uint32_t* trace;            // [grid][trace_steps][max_ins][8]
   uint32_t* progress;         // [grid]: (step << 16) | (pc + 1) of the last finished instruction
-  uint64_t* dbg;              // [grid][512] diagnostics (argmax: last key each thread read)
+  uint64_t* ts;               // [grid][max_ins][8] fine timestamps of step 0 (diagnostics), or null
   int32_t trace_steps, max_ins;
   // dims
   int32_t L, d, nq, nkv, hd, f, V, max_seq, S, R, sync_mode, lm_slots;
   int32_t chain_n, vec_floats;
   float eps;
   uint64_t watchdog_ticks;    // 100 MHz ticks
+  int32_t poll_sleep;         // s_sleep units between failed poll rounds (0 = spin)
+  int32_t pad2;
 };
 
 }  // namespace mk

@@ -189,6 +189,15 @@ int mk_chain_create(int32_t n, int32_t stages, const void* W, const mk_options* 
 /* x0: device [n] fp32; y: device [stages][n] fp32 (written).  Synchronises. */
 int mk_chain_run(mk_chain* ch, const float* x0, float* y);
 int mk_chain_stats(const mk_chain* ch, mk_stats* out);
+/* Time journal of the last chain run (same record format as mk_read_trace). */
+int mk_chain_read_trace(mk_chain* ch, uint32_t* host_buf, int64_t capacity_records, int64_t* n_records);
+/* Fine timestamps of step 0 of the last chain run, recorded only when the
+ * environment variable MK_DEBUG_TS is set at run time: per workgroup and
+ * instruction, 8 uint64 device-clock (100 MHz) marks {0 instruction start, 1 inputs
+ * polled, 2 inputs staged (after the barrier), 3 op end, 4 failure check
+ * done, 5 activations in registers, 6 dot products done, 7 unused}; zero where not recorded.  capacity is in
+ * uint64 and must be at least grid * max_ins_per_cta * 8. */
+int mk_chain_debug_ts(mk_chain* ch, uint64_t* host, int64_t capacity);
 const char* mk_chain_last_error(const mk_chain* ch);
 void mk_chain_destroy(mk_chain* ch);
 
