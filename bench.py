@@ -58,6 +58,37 @@ def cpu_baseline(model, w, prompt_len: int = 64, steps: int = 8) -> dict:
                       f"512..1024; attention is ~2% of the bytes per token)"}
 
 
+# sources that decide what the monokernel reads and writes: the device code and the schedule
+KERNEL_SOURCES = ("mk_device.h", "mk_kernel.hip", "mk_layout.h", "mk_plan.cpp", "mk_plan.h")
+
+
+def kernel_sources_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        h.update(name.encode())
+        with open(os.path.join(ROOT, "decode_megakernel_wave_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, n: int, launch: dict):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE passes, scaled
+    by the copy-kernel calibration; None unless they were taken on these exact kernel sources
+    and this launch shape."""
+    path = os.path.join(ROOT, "profiles", f"mk_monokernel_{workload}_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sources_sha256_16") != kernel_sources_hash() or rec.get("decode_tokens_per_launch") != n:
+        return None
+    if any(rec.get("launch", {}).get(k) != v for k, v in launch.items()):
+        return None
+    return rec
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -68,6 +99,9 @@ def main() -> int:
     ap.add_argument("--sync", default="sentinel", choices=["sentinel", "counter"])
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 device-to-device copies of MIB MiB (torch) and exit: the reference "
+                         "kernel for scaling the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the monokernel runs on a single "
@@ -77,6 +111,17 @@ def main() -> int:
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 18  # fp32 elements
+        x = torch.ones(n, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(5):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {args.copy_calibration} MiB 5 times")
+        return 0
+
     import decode_megakernel_wave_amd as mk
     from decode_megakernel_wave_amd import inputs
 
@@ -125,6 +170,9 @@ def main() -> int:
 
     mean_ms = float(np.mean(kernel_ms))
     achieved = float(np.mean(algo)) / (mean_ms * 1e-3) / 1e9
+    traffic = measured_traffic(args.workload, n, {"grid": stats["grid"], "block": stats["block"],
+                                                  "lds_bytes": stats["lds_bytes"], "ring_depth": stats["ring_depth"],
+                                                  "sync": args.sync, "xcd_replicas": args.replicas})
     out = {
         "metric": "batch-1 decode tokens/s per request on 1 MI355X; achieved HBM TB/s of 8",
         "value": n * args.steps / wall,
@@ -144,7 +192,11 @@ def main() -> int:
                    "batch": 1, "sync": args.sync, "xcd_replicas": args.replicas, "grid": stats["grid"],
                    "block": stats["block"], "lds_bytes": stats["lds_bytes"], "ring_depth": stats["ring_depth"]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic["traffic_bytes_per_launch"] if traffic else None,
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "traffic_read_write": [traffic["fetch_bytes_per_launch"], traffic["write_bytes_per_launch"]]
+                     if traffic else None,
                      "kernel": "mk_monokernel", "kernel_ms": mean_ms,
                      "algo_bytes_per_launch": float(np.mean(algo))},
         "kernel_tokens_per_s": n / mean_ms * 1e3,

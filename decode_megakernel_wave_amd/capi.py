@@ -15,7 +15,8 @@ import numpy as np
 
 from . import inputs
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmk.so")
+# MK_LIBRARY selects another build of the same sources (tuning variants)
+_LIB_PATH = os.environ.get("MK_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmk.so")
 _lib = None
 
 MK_OK, MK_EINVAL, MK_ENOMEM, MK_EHIP, MK_ESTATE, MK_ERANGE, MK_EOCC, MK_ETIMEOUT, MK_ENAN = 0, -1, -2, -3, -4, -5, -6, -7, -8

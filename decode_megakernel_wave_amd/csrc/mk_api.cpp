@@ -418,10 +418,11 @@ int ctx_run(mk_ctx* c, int n, int first_token, const int32_t* forced, int32_t* t
   c->last_pos0 = pos0;
   c->last_n = n;
   int rc = launch(g, kp, n);
-  // algorithmic bytes: weights + one embedding row + K/V of positions 0..pos per step
+  // algorithmic bytes per step: the weights (the plan's figure already holds
+  // the norm gains and one embedding row) + K/V of positions 0..pos
   const int64_t kv_pos = 2LL * k.n_layers * k.n_kv_heads * k.head_dim * 2;
   int64_t bytes = 0;
-  for (int s = 0; s < n; ++s) bytes += g.plan.weight_bytes + 2LL * k.d_model + kv_pos * (pos0 + s + 1);
+  for (int s = 0; s < n; ++s) bytes += g.plan.weight_bytes + kv_pos * (pos0 + s + 1);
   g.last.algo_bytes = bytes;
   g.last.kv_bytes_per_pos = kv_pos;
   g.last.pos0 = pos0;

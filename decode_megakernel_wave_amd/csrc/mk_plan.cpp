@@ -16,6 +16,8 @@
 
 namespace mk {
 
+// ring | staged vector | scratch | residual rows | 512 B of small fields:
+// failure flags (64 B), wave sums (32), argmax keys (64), misc (64).
 int lds_bytes_for(int kpad_max) {
   return kWaves * kRing * 1024 + kpad_max * 4 + kScratchFloats * 4 + 1024 * 4 + 512;
 }
