@@ -245,7 +245,7 @@ int launch(Engine& g, KParams& k, int n_steps) {
   g.last.gpu_ms = ms;
   g.last.steps = n_steps;
   g.last.grid = g.grid;
-  g.last.block = kThreads;
+  g.last.block = kBlock;
   g.last.lds_bytes = g.plan.lds_bytes;
   g.last.ring_depth = kRing;
   g.last.stream_bytes = g.plan.stream_bytes();
@@ -845,6 +845,15 @@ int mk_chain_read_trace(mk_chain* ch, uint32_t* host_buf, int64_t capacity, int6
   if (!host_buf) return MK_OK;
   if (capacity < *n_records) return g.fail(MK_EINVAL, "trace buffer too small");
   if (g.trace_words) HIPCHK(g, hipMemcpy(host_buf, g.d_trace, g.trace_words * 4, hipMemcpyDeviceToHost));
+  return MK_OK;
+}
+
+int mk_debug_ts(mk_ctx* c, uint64_t* host, int64_t capacity) {
+  if (!c || !host) return MK_EINVAL;
+  Engine& g = c->g;
+  const int64_t n = (int64_t)g.grid * g.plan.max_ins * 8;
+  if (capacity < n) return MK_EINVAL;
+  HIPCHK(g, hipMemcpy(host, g.d_ts, n * 8, hipMemcpyDeviceToHost));
   return MK_OK;
 }
 

@@ -52,6 +52,7 @@ struct Smem {
   float* wsum;       // [kWaves] partial sums of squares
   uint64_t* keys;    // [kWaves]
   uint32_t* misc;    // [16]
+  uint32_t* bar;     // compute-wavefront barrier counter
 };
 
 struct Cx {
@@ -60,6 +61,7 @@ struct Cx {
   int cta, wave, lane, tid, rep, xcc;
   int step, pos, e, e1, tok, pc;
   int flag_parity;
+  uint32_t gen;       // barrier generation (kWaves per barrier entered)
   bool fail;          // this thread saw a timeout or abort
   uint64_t deadline;
   int poll_iters;
@@ -67,13 +69,16 @@ struct Cx {
 
 __device__ __forceinline__ void raise_fault(Cx& c, int code, int op, int layer, int index) {
   const KParams& kp = *c.kp;
-  if (atomicCAS((unsigned*)&kp.fault->code, 0u, (unsigned)code) == 0u) {
-    kp.fault->cta = c.cta;
-    kp.fault->pc = c.pc;
-    kp.fault->op = op;
-    kp.fault->step = c.step;
-    kp.fault->layer = layer;
-    kp.fault->index = index;
+  MK_GLOBAL Fault* f = gp(kp.fault);
+  int32_t expect = 0;
+  if (__hip_atomic_compare_exchange_strong(&f->code, &expect, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT)) {
+    f->cta = c.cta;
+    f->pc = c.pc;
+    f->op = op;
+    f->step = c.step;
+    f->layer = layer;
+    f->index = index;
   }
   if (code == -7) stc32(kp.abort_flag, 1u);
 }
@@ -100,12 +105,32 @@ __device__ __forceinline__ void poll_pause(const Cx& c) {
   for (int i = 0; i < c.kp->poll_sleep; ++i) __builtin_amdgcn_s_sleep(1);
 }
 
+// One instruction record.  The lists do not change during a launch, so they
+// are read through the constant address space: scalar loads into SGPRs.
+__device__ __forceinline__ Ins load_ins(const Ins* p) {
+  typedef const __attribute__((address_space(4))) u4 CU4;
+  struct Raw {
+    u4 a, b;
+  } raw = {((CU4*)p)[0], ((CU4*)p)[1]};
+  return __builtin_bit_cast(Ins, raw);
+}
+
+// Barrier of the compute wavefronts (the loaders run on their own).  A
+// barrier that times out (a wavefront never arrived) is a fault; after any
+// fault every barrier returns at once, so the workgroup drains.
+__device__ __forceinline__ void cta_sync(Cx& c) {
+  if (!lds_barrier(c.sm.bar, c.gen, c.kp->watchdog_ticks, c.kp->abort_flag)) {
+    raise_fault(c, -7, OP_END, -1, -2);
+    c.fail = true;
+  }
+}
+
 // Workgroup-wide OR of the per-thread failure flags (also a barrier).
 __device__ __forceinline__ bool cta_failed(Cx& c) {
   const uint64_t b = __ballot(c.fail);
   uint32_t* f = c.sm.flags + c.flag_parity * kWaves;
   if (c.lane == 0) f[c.wave] = b != 0;
-  cta_sync();
+  cta_sync(c);
   uint32_t any = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) any |= f[w];
@@ -135,7 +160,7 @@ __device__ __forceinline__ void counter_wait(Cx& c, int sid, int n_in, int op, i
     const uint32_t target = (uint32_t)n_in * (uint32_t)(c.step + 1);
     uint32_t* ctr = c.kp->counters + sid;
     int tries = 0;
-    while (__hip_atomic_load(gp(ctr), __ATOMIC_ACQUIRE, MK_SCOPE) < target) {
+    while (__hip_atomic_load(gp(ctr), __ATOMIC_RELAXED, MK_SCOPE) < target) {
       // exponential back-off ("8 - Ecrire son megakernel", section 8.5)
       const int k = tries < 4 ? (1 << tries) : 16;
       for (int i = 0; i < k; ++i) __builtin_amdgcn_s_sleep(1);
@@ -145,14 +170,18 @@ __device__ __forceinline__ void counter_wait(Cx& c, int sid, int n_in, int op, i
         break;
       }
     }
+    acquire_polled();
   }
 }
 
 __device__ __forceinline__ void counter_signal(Cx& c, int sid) {
   if (sentinel_mode(c) || sid < 0) return;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  cta_sync();
-  if (c.tid == 0) __hip_atomic_fetch_add(gp(c.kp->counters + sid), 1u, __ATOMIC_RELAXED, MK_SCOPE);
+  stores_acked();
+  cta_sync(c);
+  if (c.wave == 0) {
+    release_stores();
+    if (c.lane == 0) __hip_atomic_fetch_add(gp(c.kp->counters + sid), 1u, __ATOMIC_RELAXED, MK_SCOPE);
+  }
 }
 
 // Poll one fp32 word until it stops being the sentinel (sentinel mode) or
@@ -275,8 +304,20 @@ __device__ __forceinline__ void publish(const Cx& c, const Buf& b, int l, int64_
 }
 
 // ---------------------------------------------------------------- GEMV core
-// Streams this wavefront's chunks of instruction `in` through the ring and
-// calls epi(u_local, row0, row1) once per unit with uniform sums.
+// Next N chunks of this wavefront's weight stream: wait until they have
+// landed, then release their slots.
+template <int N>
+__device__ __forceinline__ void ring_read(Cx& c, Ring& r, u4 (&w)[4], const Ins& in) {
+  while (!ring_load<N>(r, w)) {
+    if (c.fail || expired(c, in.op, in.layer, (int)r.seq)) {
+      c.fail = true;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  ring_release<N>(r);
+}
+
 template <int CPS, typename Epi>
 __device__ __forceinline__ void gemv(Cx& c, Ring& ring, const Ins& in, const float* vec, float scale, Epi epi) {
   const int ks = in.ks, rg = kWaves / ks, ki = c.wave % ks, gi = c.wave / ks;
@@ -296,11 +337,12 @@ __device__ __forceinline__ void gemv(Cx& c, Ring& ring, const Ins& in, const flo
   for (int u = gi; u < in.nu; u += rg) {
     float r0 = 0.f, r1 = 0.f;
     u4 w[4];
-    ring_read<CPS>(ring, w);
+    ring_read<CPS>(c, ring, w, in);
+    if (u == gi) ts_mark(c, 7);
 #pragma unroll
     for (int k = 0; k < CPS; ++k) r0 += dot8(w[k], act[k]);
     if (upr == 2) {
-      ring_read<CPS>(ring, w);
+      ring_read<CPS>(c, ring, w, in);
 #pragma unroll
       for (int k = 0; k < CPS; ++k) r1 += dot8(w[k], act[k]);
     }
@@ -315,7 +357,7 @@ __device__ __forceinline__ void gemv(Cx& c, Ring& ring, const Ins& in, const flo
   }
   ts_mark(c, 6);
   if (ks > 1) {
-    cta_sync();
+    cta_sync(c);
     if (ki == 0) {
       // one unit per lane: sum its ks partials (fixed order), then hand each
       // sum to the epilogue as a uniform value
@@ -359,7 +401,7 @@ __device__ __forceinline__ float finish_staging(Cx& c, int n, bool norm, float s
     const float p = wave_sum(ss_thread);
     if (c.lane == 0) c.sm.wsum[c.wave] = p;
   }
-  cta_sync();
+  cta_sync(c);
   ts_mark(c, 2);
   mark_ready(c);
   if (!norm) return 1.0f;
@@ -391,19 +433,22 @@ __device__ __forceinline__ void op_qkv(Cx& c, Ring& ring, const Ins& in) {
   const KParams& kp = *c.kp;
   const int l = in.layer;
   counter_wait(c, in.sync_in, in.n_in, OP_QKV, l);
-  if (!sentinel_mode(c)) cta_sync();
+  if (!sentinel_mode(c)) cta_sync(c);
   const uint16_t* g1 = kp.norms + (int64_t)l * 2 * kp.d;
+  // the (cos, sin) row of this position goes to LDS with the staging, so the
+  // epilogue does not wait on a global load per unit
+  const int hh = kp.hd / 2, nqh = kp.nq * hh, nkh = kp.nkv * hh;
+  float* rope = c.sm.resid;
+  for (int i = c.tid; i < 2 * hh; i += kThreads) rope[i] = *gp(kp.rope + (int64_t)c.pos * hh * 2 + i);
   const float ss = stage_layer_input(c, l, in.kpad, g1, OP_QKV);
   const float scale = finish_staging(c, kp.d, true, ss);
-  const int hh = kp.hd / 2, nqh = kp.nq * hh, nkh = kp.nkv * hh;
-  const float* rope = kp.rope + (int64_t)c.pos * hh * 2;
   gemv_dispatch(c, ring, in, c.sm.vec, scale, [&](int u, float a, float b) {
     int g = in.u0 + u;
     if (g < nqh + nkh) {  // rotary pair (i, i + hd/2) of a q or k head
       const bool isq = g < nqh;
       if (!isq) g -= nqh;
       const int head = g / hh, i = g % hh;
-      const float cs = *gp(rope + 2 * i), sn = *gp(rope + 2 * i + 1);
+      const float cs = rope[2 * i], sn = rope[2 * i + 1];
       const float ra = a * cs - b * sn, rb = a * sn + b * cs;
       if (isq) {
         float* q = buf_at(kp.q, c.e, l, 0) + head * kp.hd + i;
@@ -431,6 +476,118 @@ __device__ __forceinline__ void op_qkv(Cx& c, Ring& ring, const Ins& in) {
 // Split attention for (kv head, split) units: unnormalised partial
 // O = sum_t 2^(s_t - m) v_t, L = sum_t 2^(s_t - m), m = max_t s_t, with
 // scores s_t = q.k_t / sqrt(hd) * log2(e).
+//
+// Query heads [j0, j0 + ng) of the group (ng <= GP) over the positions
+// [t0, t1): each wavefront takes t0 + wave, t0 + wave + kWaves, ... in
+// batches of kBatch whose K/V loads are all issued before any score is
+// computed; lane i holds dims [i*DPL, i*DPL + DPL).  GP * DPL <= 8 keeps the
+// accumulators in 8 registers per lane whatever the head geometry.
+template <int GP, int DPL>
+__device__ __forceinline__ void att_pass(Cx& c, int l, int g, int sp, int j0, int ng, int t0, int t1, int G) {
+  const KParams& kp = *c.kp;
+  const int hd = kp.hd, S = kp.S;
+  constexpr int kBatch = 4;
+  const float* qs = c.sm.vec;            // [G][hd]
+  const float* kcur = c.sm.vec + G * hd; // [hd]
+  const float* vcur = kcur + hd;         // [hd]
+  float m[GP], lsum[GP], o[GP][DPL];
+#pragma unroll
+  for (int j = 0; j < GP; ++j) {
+    m[j] = -INFINITY;
+    lsum[j] = 0.f;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) o[j][k] = 0.f;
+  }
+  const int64_t head_off = ((int64_t)l * kp.nkv + g) * kp.max_seq * hd + c.lane * DPL;
+  const uint16_t* kbase = kp.kc + head_off;
+  const uint16_t* vbase = kp.vc + head_off;
+  for (int tb = t0 + c.wave; tb < t1; tb += kWaves * kBatch) {
+    float kv[kBatch][DPL], vv[kBatch][DPL];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int t = tb + b * kWaves;
+      if (t >= t1) break;
+      if (t == c.pos) {
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) {
+          kv[b][k] = kcur[c.lane * DPL + k];
+          vv[b][k] = vcur[c.lane * DPL + k];
+        }
+      } else {
+        const uint16_t* kr = kbase + (int64_t)t * hd;
+        const uint16_t* vr = vbase + (int64_t)t * hd;
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) {
+          kv[b][k] = (float)__builtin_bit_cast(_Float16, *gp(kr + k));
+          vv[b][k] = (float)__builtin_bit_cast(_Float16, *gp(vr + k));
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int t = tb + b * kWaves;
+      if (t >= t1) break;
+#pragma unroll
+      for (int j = 0; j < GP; ++j) {
+        if (j >= ng) break;
+        float sc = 0.f;
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) sc += qs[(j0 + j) * hd + c.lane * DPL + k] * kv[b][k];
+        sc = wave_sum(sc);
+        const float mn = fmaxf(m[j], sc);
+        const float al = exp2f(m[j] - mn), p = exp2f(sc - mn);
+        lsum[j] = lsum[j] * al + p;
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) o[j][k] = o[j][k] * al + p * vv[b][k];
+        m[j] = mn;
+      }
+    }
+  }
+  // combine the wavefronts: scratch [wave][ng][hd + 2]
+  float* scr = c.sm.scratch;
+  const int rec = hd + 2;
+#pragma unroll
+  for (int j = 0; j < GP; ++j) {
+    if (j >= ng) break;
+    float* r = scr + (c.wave * ng + j) * rec;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) r[2 + c.lane * DPL + k] = o[j][k];
+    if (c.lane == 0) {
+      r[0] = m[j];
+      r[1] = lsum[j];
+    }
+  }
+  cta_sync(c);
+  for (int i = c.tid; i < ng * hd; i += kThreads) {
+    const int j = i / hd, dd = i % hd;
+    float M = -INFINITY;
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, scr[(w * ng + j) * rec]);
+    float Lt = 0.f, Ot = 0.f;
+    if (M != -INFINITY) {
+      for (int w = 0; w < kWaves; ++w) {
+        const float* r = scr + (w * ng + j) * rec;
+        const float al = exp2f(r[0] - M);
+        Lt += al * r[1];
+        Ot += al * r[2 + dd];
+      }
+    }
+    const int qh = g * G + j0 + j;
+    const int64_t po = ((((int64_t)c.e * kp.L + l) * kp.nq + qh) * S + sp);
+    const int64_t po1 = ((((int64_t)c.e1 * kp.L + l) * kp.nq + qh) * S + sp);
+    stcf(kp.att_o + po * hd + dd, Ot);
+    if (sentinel_mode(c)) stc32(kp.att_o + po1 * hd + dd, kSent32);
+    if (dd == 0) {
+      stcf(kp.att_ml + po * 2, M);
+      stcf(kp.att_ml + po * 2 + 1, Lt);
+      if (sentinel_mode(c)) {
+        stc32(kp.att_ml + po1 * 2, kSent32);
+        stc32(kp.att_ml + po1 * 2 + 1, kSent32);
+      }
+    }
+  }
+  cta_sync(c);  // scratch reused by the next pass
+}
+
 __device__ __forceinline__ void op_att(Cx& c, const Ins& in) {
   const KParams& kp = *c.kp;
   const int l = in.layer;
@@ -439,7 +596,7 @@ __device__ __forceinline__ void op_att(Cx& c, const Ins& in) {
   const int chunk = (T + S - 1) / S;
   const float qscale = kLog2e / __builtin_sqrtf((float)hd);
   counter_wait(c, in.sync_in, in.n_in, OP_ATT, l);
-  if (!sentinel_mode(c)) cta_sync();
+  if (!sentinel_mode(c)) cta_sync(c);
   float* qs = c.sm.vec;              // [G][hd]
   float* kcur = c.sm.vec + G * hd;   // [hd]
   float* vcur = kcur + hd;           // [hd]
@@ -447,9 +604,20 @@ __device__ __forceinline__ void op_att(Cx& c, const Ins& in) {
     const int U = in.u0 + ui, g = U / S, sp = U % S;
     const int t0 = sp * chunk, t1 = min(T, t0 + chunk);
     const bool has_cur = t0 <= c.pos && c.pos < t1;
+    // pull this split's cached K/V rows towards the CU before waiting for q:
+    // each thread touches one 4-byte word per 64 bytes of the rows it will read
+    float touch = 0.f;
+    {
+      const int64_t hoff = ((int64_t)l * kp.nkv + g) * kp.max_seq * hd;
+      const int words = (t1 - t0) * hd / 16;  // one per 64 bytes (32 halves) of K and of V
+      for (int i = c.tid; i < words; i += kThreads) {
+        const int64_t e = (int64_t)t0 * hd + (int64_t)(i >> 1) * 32;  // element offset in the head's rows
+        if (e / hd != c.pos) touch += __uint_as_float(*gp((const uint32_t*)(((i & 1) ? kp.vc : kp.kc) + hoff + e)));
+      }
+    }
     // stage q of the group and, for the split holding the current position, its K/V
     const float* qsrc = buf_at(kp.q, c.e, l, 0) + g * G * hd;
-    if (c.tid < G * hd) qs[c.tid] = poll_f32(c, qsrc + c.tid, OP_ATT, l) * qscale;
+    for (int i = c.tid; i < G * hd; i += kThreads) qs[i] = poll_f32(c, qsrc + i, OP_ATT, l) * qscale;
     if (has_cur && c.tid < 2 * hd) {
       const int i = c.tid % hd;
       const uint16_t* src = (c.tid < hd ? kp.kc : kp.vc) + (((int64_t)l * kp.nkv + g) * kp.max_seq + c.pos) * hd + i;
@@ -465,106 +633,20 @@ __device__ __forceinline__ void op_att(Cx& c, const Ins& in) {
       }
       (c.tid < hd ? kcur : vcur)[i] = (float)__builtin_bit_cast(_Float16, v);
     }
-    cta_sync();
+    ts_mark(c, 1);
+    cta_sync(c);
+    ts_mark(c, 2);
     if (ui == 0) mark_ready(c);
-    // each wavefront: positions t0 + wave, t0 + wave + kWaves, ... in batches
-    // of kBatch whose K/V loads are all issued before any score is computed
-    constexpr int kMaxG = 8, kMaxDpl = 4, kBatch = 4;
-    const int dpl = hd / 64;  // dims per lane
-    float m[kMaxG], lsum[kMaxG], o[kMaxG][kMaxDpl];
-#pragma unroll
-    for (int j = 0; j < kMaxG; ++j) {
-      m[j] = -INFINITY;
-      lsum[j] = 0.f;
-#pragma unroll
-      for (int k = 0; k < kMaxDpl; ++k) o[j][k] = 0.f;
+    if (touch == 1.2345e-30f && c.tid == kThreads) c.fail = true;  // keeps the touches; never true
+    const int dpl = hd / 64;
+    const int gp_max = 8 / dpl;
+    for (int j0 = 0; j0 < G; j0 += gp_max) {
+      const int ng = min(gp_max, G - j0);
+      if (dpl == 1) att_pass<8, 1>(c, l, g, sp, j0, ng, t0, t1, G);
+      else if (dpl == 2) att_pass<4, 2>(c, l, g, sp, j0, ng, t0, t1, G);
+      else att_pass<2, 4>(c, l, g, sp, j0, ng, t0, t1, G);
     }
-    const uint16_t* kbase = kp.kc + ((int64_t)l * kp.nkv + g) * kp.max_seq * hd + c.lane * dpl;
-    const uint16_t* vbase = kp.vc + ((int64_t)l * kp.nkv + g) * kp.max_seq * hd + c.lane * dpl;
-    for (int tb = t0 + c.wave; tb < t1; tb += kWaves * kBatch) {
-      float kv[kBatch][kMaxDpl], vv[kBatch][kMaxDpl];
-#pragma unroll
-      for (int b = 0; b < kBatch; ++b) {
-        const int t = tb + b * kWaves;
-        if (t >= t1) break;
-        if (t == c.pos) {
-#pragma unroll
-          for (int k = 0; k < kMaxDpl; ++k)
-            if (k < dpl) { kv[b][k] = kcur[c.lane * dpl + k]; vv[b][k] = vcur[c.lane * dpl + k]; }
-        } else {
-          const uint16_t* kr = kbase + (int64_t)t * hd;
-          const uint16_t* vr = vbase + (int64_t)t * hd;
-#pragma unroll
-          for (int k = 0; k < kMaxDpl; ++k)
-            if (k < dpl) {
-              kv[b][k] = (float)__builtin_bit_cast(_Float16, *gp(kr + k));
-              vv[b][k] = (float)__builtin_bit_cast(_Float16, *gp(vr + k));
-            }
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < kBatch; ++b) {
-        const int t = tb + b * kWaves;
-        if (t >= t1) break;
-#pragma unroll
-        for (int j = 0; j < kMaxG; ++j) {
-          if (j >= G) break;
-          float s = 0.f;
-#pragma unroll
-          for (int k = 0; k < kMaxDpl; ++k)
-            if (k < dpl) s += qs[j * hd + c.lane * dpl + k] * kv[b][k];
-          s = wave_sum(s);
-          const float mn = fmaxf(m[j], s);
-          const float a = exp2f(m[j] - mn), p = exp2f(s - mn);
-          lsum[j] = lsum[j] * a + p;
-#pragma unroll
-          for (int k = 0; k < kMaxDpl; ++k)
-            if (k < dpl) o[j][k] = o[j][k] * a + p * vv[b][k];
-          m[j] = mn;
-        }
-      }
-    }
-    // combine the wavefronts: scratch [wave][G][hd + 2]
-    float* sc = c.sm.scratch;
-    const int rec = hd + 2;
-#pragma unroll
-    for (int j = 0; j < kMaxG; ++j) {
-      if (j >= G) break;
-      float* r = sc + (c.wave * G + j) * rec;
-#pragma unroll
-      for (int k = 0; k < kMaxDpl; ++k)
-        if (k < dpl) r[2 + c.lane * dpl + k] = o[j][k];
-      if (c.lane == 0) { r[0] = m[j]; r[1] = lsum[j]; }
-    }
-    cta_sync();
-    if (c.tid < G * hd) {
-      const int j = c.tid / hd, dd = c.tid % hd;
-      float M = -INFINITY;
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sc[(w * G + j) * rec]);
-      float Lt = 0.f, Ot = 0.f;
-      if (M != -INFINITY) {
-        for (int w = 0; w < kWaves; ++w) {
-          const float* r = sc + (w * G + j) * rec;
-          const float a = exp2f(r[0] - M);
-          Lt += a * r[1];
-          Ot += a * r[2 + dd];
-        }
-      }
-      const int qh = g * G + j;
-      const int64_t po = ((((int64_t)c.e * kp.L + l) * kp.nq + qh) * S + sp);
-      const int64_t po1 = ((((int64_t)c.e1 * kp.L + l) * kp.nq + qh) * S + sp);
-      stcf(kp.att_o + po * hd + dd, Ot);
-      if (sentinel_mode(c)) stc32(kp.att_o + po1 * hd + dd, kSent32);
-      if (dd == 0) {
-        stcf(kp.att_ml + po * 2, M);
-        stcf(kp.att_ml + po * 2 + 1, Lt);
-        if (sentinel_mode(c)) {
-          stc32(kp.att_ml + po1 * 2, kSent32);
-          stc32(kp.att_ml + po1 * 2 + 1, kSent32);
-        }
-      }
-    }
-    cta_sync();  // LDS reused by the next unit
+    ts_mark(c, 6);
   }
   counter_signal(c, in.sync_out);
 }
@@ -574,7 +656,7 @@ __device__ __forceinline__ void op_red(Cx& c, const Ins& in) {
   const KParams& kp = *c.kp;
   const int l = in.layer, hd = kp.hd, S = kp.S, nb = hd / kRedDims;
   counter_wait(c, in.sync_in, in.n_in, OP_RED, l);
-  if (!sentinel_mode(c)) cta_sync();
+  if (!sentinel_mode(c)) cta_sync(c);
   for (int ui = c.wave; ui < in.nu; ui += kWaves) {
     const int U = in.u0 + ui, h = U / nb, b = U % nb;
     const int s = c.lane;
@@ -611,7 +693,10 @@ __device__ __forceinline__ void op_red(Cx& c, const Ins& in) {
 #pragma unroll
       for (int d = 0; d < kRedDims; ++d) os[d] = __uint_as_float(raw[2 + d]);
     }
-    if (ui == 0) mark_ready(c);
+    if (ui == 0) {
+      mark_ready(c);
+      ts_mark(c, 1);
+    }
     const float M = wave_max(ms);
     const float w = (s < S && ms != -INFINITY) ? exp2f(ms - M) : 0.f;
     const float Lt = wave_sum(w * ls);
@@ -621,6 +706,7 @@ __device__ __forceinline__ void op_red(Cx& c, const Ins& in) {
       const float v = wave_sum(w * os[d]) * inv;
       publish(c, kp.o, l, (int64_t)h * hd + b * kRedDims + d, v);
     }
+    if (ui == 0) ts_mark(c, 6);
   }
   counter_signal(c, in.sync_out);
 }
@@ -629,7 +715,7 @@ __device__ __forceinline__ void op_oproj(Cx& c, Ring& ring, const Ins& in) {
   const KParams& kp = *c.kp;
   const int l = in.layer;
   counter_wait(c, in.sync_in, in.n_in, OP_OPROJ, l);
-  if (!sentinel_mode(c)) cta_sync();
+  if (!sentinel_mode(c)) cta_sync(c);
   stage_vec(c, buf_at(kp.o, c.e, l, c.rep), c.sm.vec, kp.nq * kp.hd, in.kpad, nullptr, OP_OPROJ, l);
   stage_resid(c, l == 0 ? nullptr : buf_at(kp.xm, c.e, l - 1, c.rep), l == 0 ? kp.embed + (int64_t)c.tok * kp.d : nullptr,
               in.u0, in.nu, OP_OPROJ, l);
@@ -644,7 +730,7 @@ __device__ __forceinline__ void op_upgate(Cx& c, Ring& ring, const Ins& in) {
   const KParams& kp = *c.kp;
   const int l = in.layer;
   counter_wait(c, in.sync_in, in.n_in, OP_UPGATE, l);
-  if (!sentinel_mode(c)) cta_sync();
+  if (!sentinel_mode(c)) cta_sync(c);
   const uint16_t* g2 = kp.norms + ((int64_t)l * 2 + 1) * kp.d;
   const float ss = stage_vec(c, buf_at(kp.xa, c.e, l, c.rep), c.sm.vec, kp.d, in.kpad, g2, OP_UPGATE, l);
   const float scale = finish_staging(c, kp.d, true, ss);
@@ -659,7 +745,7 @@ __device__ __forceinline__ void op_down(Cx& c, Ring& ring, const Ins& in) {
   const KParams& kp = *c.kp;
   const int l = in.layer;
   counter_wait(c, in.sync_in, in.n_in, OP_DOWN, l);
-  if (!sentinel_mode(c)) cta_sync();
+  if (!sentinel_mode(c)) cta_sync(c);
   stage_vec(c, buf_at(kp.m, c.e, l, c.rep), c.sm.vec, kp.f, in.kpad, nullptr, OP_DOWN, l);
   stage_resid(c, buf_at(kp.xa, c.e, l, c.rep), nullptr, in.u0, in.nu, OP_DOWN, l);
   finish_staging(c, 0, false, 0.f);
@@ -681,7 +767,7 @@ __device__ __forceinline__ void op_lmhead(Cx& c, Ring& ring, const Ins& in) {
   const KParams& kp = *c.kp;
   const int L = kp.L;
   counter_wait(c, in.sync_in, in.n_in, OP_LMHEAD, L);
-  if (!sentinel_mode(c)) cta_sync();
+  if (!sentinel_mode(c)) cta_sync(c);
   uint64_t best = 1;  // below every real key
   if (in.nu > 0) {
     const uint16_t* gf = kp.norms + (int64_t)L * 2 * kp.d;
@@ -699,7 +785,7 @@ __device__ __forceinline__ void op_lmhead(Cx& c, Ring& ring, const Ins& in) {
     });
     if (nan && c.lane == 0) raise_fault(c, -8, OP_LMHEAD, L, c.step);
     if (c.lane == 0) c.sm.keys[c.wave] = bi >= 0 ? argmax_key(bv, bi) : 1;
-    cta_sync();
+    cta_sync(c);
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) best = max(best, c.sm.keys[w]);
   }
@@ -708,17 +794,23 @@ __device__ __forceinline__ void op_lmhead(Cx& c, Ring& ring, const Ins& in) {
   uint64_t* slot = kp.lmp + c.e * kp.lmp_es + in.slot;
   uint64_t* slot1 = kp.lmp + c.e1 * kp.lmp_es + in.slot;
   if (sentinel_mode(c) && c.wave == 0 && c.lane < kp.R) stc64(slot1 + c.lane * kp.lmp_rs, kSent64);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  cta_sync();
-  if (c.wave == 0 && c.lane < kp.R) stc64(slot + c.lane * kp.lmp_rs, best);
-  if (!sentinel_mode(c) && c.tid == 0)
-    __hip_atomic_fetch_add(gp(kp.counters + in.sync_out), 1u, __ATOMIC_RELAXED, MK_SCOPE);
+  stores_acked();
+  cta_sync(c);
+  if (c.wave == 0) {
+    release_stores();
+    if (c.lane < kp.R) stc64(slot + c.lane * kp.lmp_rs, best);
+    if (!sentinel_mode(c)) {
+      // counter mode: the keys themselves must be out before the count says so
+      release_stores();
+      if (c.lane == 0) __hip_atomic_fetch_add(gp(kp.counters + in.sync_out), 1u, __ATOMIC_RELAXED, MK_SCOPE);
+    }
+  }
 }
 
 __device__ __forceinline__ void op_argmax(Cx& c, const Ins& in) {
   const KParams& kp = *c.kp;
   counter_wait(c, in.sync_in, in.n_in, OP_ARGMAX, kp.L);
-  if (!sentinel_mode(c)) cta_sync();
+  if (!sentinel_mode(c)) cta_sync(c);
   const uint64_t* src = kp.lmp + c.e * kp.lmp_es + c.rep * kp.lmp_rs;
   uint64_t k = 0;
   for (int i = c.tid; i < in.nu; i += kThreads) {
@@ -741,12 +833,14 @@ __device__ __forceinline__ void op_argmax(Cx& c, const Ins& in) {
     k = max(k, o);
   }
   if (c.lane == 0) c.sm.keys[c.wave] = k;
-  cta_sync();
+  cta_sync(c);
   mark_ready(c);
+  // one acquire (cache invalidation) for the workgroup, after every wavefront's polls
+  if (c.wave == 0) acquire_polled();
+  cta_sync(c);
   uint64_t best = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) best = max(best, c.sm.keys[w]);
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   int tok = __builtin_amdgcn_readfirstlane((int)(0xFFFFFFFFu - (uint32_t)best));
   if (tok < 0 || tok >= kp.V) tok = 0;  // only on an aborted run
   if (c.cta == 0 && c.tid == 0) *gp(kp.tokens + c.step) = tok;
@@ -757,7 +851,7 @@ __device__ __forceinline__ void op_chain(Cx& c, Ring& ring, const Ins& in) {
   const KParams& kp = *c.kp;
   const int i = in.layer, n = kp.chain_n;
   counter_wait(c, in.sync_in, in.n_in, OP_CHAIN, i);
-  if (!sentinel_mode(c)) cta_sync();
+  if (!sentinel_mode(c)) cta_sync(c);
   if (i == 0) {
     for (int k = c.tid * 4; k < in.kpad; k += kThreads * 4)
       *(f4*)(c.sm.vec + k) = k < n ? *gp((const f4*)(kp.x0 + k)) : f4{0.f, 0.f, 0.f, 0.f};
@@ -774,7 +868,58 @@ __device__ __forceinline__ void op_chain(Cx& c, Ring& ring, const Ins& in) {
 
 }  // namespace
 
-__global__ __launch_bounds__(kThreads, 1) void mk_monokernel(const KParams* __restrict__ kpp) {
+// Loader wavefront `lid`: keeps the free ring slots of compute wavefronts
+// [lid * NW, lid * NW + NW) requested, for all n_steps of the launch, with at
+// most kInFlight DMAs outstanding.  It never waits for a DMA to land (the
+// consumers check the slots' contents), so it re-arms slots as soon as they
+// are released.
+__device__ __forceinline__ void run_loader(const KParams& kp, uint32_t ring_base, uint32_t small, int cta, int lid) {
+  constexpr int NW = kWaves / kLoaders;
+  const int w0 = lid * NW;
+  const uint32_t lane16 = lane_id() * 16;
+  const uint8_t* base[NW];
+  uint32_t n[NW], total[NW], issued[NW], jn[NW], slot[NW];
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int wi = cta * kWaves + w0 + i;
+    n[i] = __builtin_amdgcn_readfirstlane((uint32_t)kp.wave_n[wi]);
+    base[i] = (const uint8_t*)uniform_ptr(kp.stream + kp.wave_off[wi] * 1024);
+    total[i] = n[i] * (uint32_t)kp.n_steps;
+    issued[i] = 0;
+    jn[i] = 0;
+    slot[i] = 0;
+  }
+  // lane i < NW reads the consumed count of wavefront w0 + i
+  const uint32_t cons_lane = small + kOffCons + (uint32_t)(w0 + min(lane_id(), NW - 1)) * 4;
+  const uint32_t exitf = small + kOffExit;
+  for (;;) {
+    const uint32_t cons_v = lds_ld32(cons_lane);
+    bool any = false;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const uint32_t cons = __builtin_amdgcn_readlane(cons_v, i);
+      const uint32_t lim = min(total[i], cons + (uint32_t)kRing);
+      if (issued[i] >= lim) continue;
+      const uint32_t ring = ring_base + (uint32_t)(w0 + i) * kRing * 1024;
+      for (uint32_t k = issued[i]; k < lim; ++k) {
+        dma_chunk(ring + slot[i] * 1024, base[i], jn[i] * 1024 + lane16);
+        jn[i] = (jn[i] + 1 == n[i]) ? 0 : jn[i] + 1;
+        slot[i] = (slot[i] + 1 == kRing) ? 0 : slot[i] + 1;
+      }
+      issued[i] = lim;
+      any = true;
+    }
+    if (any) continue;
+    bool done = true;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) done = done && issued[i] == total[i];
+    if (done || __builtin_amdgcn_readfirstlane(lds_ld32(exitf)) != 0) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("s_waitcnt vmcnt(0)");
+}
+
+__global__ __launch_bounds__(kBlock, 1) void mk_monokernel(const KParams* __restrict__ kpp) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const KParams& kp = *kpp;
   Cx c;
@@ -789,6 +934,7 @@ __global__ __launch_bounds__(kThreads, 1) void mk_monokernel(const KParams* __re
   c.deadline = 0;
   c.poll_iters = 0;
   c.flag_parity = 0;
+  c.gen = 0;
   c.pc = 0;
   // LDS carve-up (must match lds_bytes_for on the host)
   c.sm.base = smem;
@@ -796,26 +942,38 @@ __global__ __launch_bounds__(kThreads, 1) void mk_monokernel(const KParams* __re
   c.sm.vec = (float*)(smem + kWaves * kRing * 1024);
   c.sm.scratch = c.sm.vec + kp.vec_floats;
   c.sm.resid = c.sm.scratch + kScratchFloats;
-  c.sm.flags = (uint32_t*)(c.sm.resid + 1024);
-  c.sm.wsum = (float*)(c.sm.flags + 2 * kWaves);
-  c.sm.keys = (uint64_t*)(c.sm.wsum + kWaves);
-  c.sm.misc = (uint32_t*)(c.sm.keys + kWaves);
+  uint8_t* small = (uint8_t*)(c.sm.resid + 1024);
+  c.sm.flags = (uint32_t*)(small + kOffFlags);
+  c.sm.wsum = (float*)(small + kOffWsum);
+  c.sm.keys = (uint64_t*)(small + kOffKeys);
+  c.sm.misc = (uint32_t*)(small + kOffMisc);
+  c.sm.bar = (uint32_t*)(small + kOffBar);
+  const uint32_t small_addr = (uint32_t)(uintptr_t)small;
+
+  // every ring slot free (sentinel), small fields (barrier counter, exit
+  // flag, consumed counts) zero, before any wavefront looks at them; the only
+  // barrier the loaders join
+  for (int i = c.tid; i < kWaves * kRing * 256; i += kBlock) ((uint32_t*)smem)[i] = kRingSent;
+  for (int i = c.tid; i < kSmallBytes / 4; i += kBlock) ((uint32_t*)small)[i] = 0;
+  __syncthreads();
+  if (c.wave >= kWaves) {
+    run_loader(kp, ring_base, small_addr, c.cta, c.wave - kWaves);
+    return;
+  }
 
   Ring ring;
-  {
-    const int wi = c.cta * kWaves + c.wave;
-    ring.lds = __builtin_amdgcn_readfirstlane(ring_base + c.wave * kRing * 1024);
-    ring.n = (uint32_t)kp.wave_n[wi];
-    ring.g = (const uint8_t*)uniform_ptr(kp.stream + kp.wave_off[wi] * 1024);
-    ring.issue = 0;
-    ring.slot = 0;
-    ring_start(ring);
-  }
+  ring.lds = __builtin_amdgcn_readfirstlane(ring_base + c.wave * kRing * 1024);
+  ring.cons = __builtin_amdgcn_readfirstlane(small_addr + kOffCons + c.wave * 4);
+  ring.seq = 0;
+  ring.slot = 0;
 
   // drop any line an earlier kernel (e.g. the sentinel fill) left in this XCD's L2
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  const int beg = kp.ins_off[c.cta], end = kp.ins_off[c.cta + 1];
-  c.tok = kp.forced ? kp.forced[0] : kp.first_token;
+  // values every lane shares: keep them in scalar registers, or the whole
+  // instruction loop (and the switch on the opcode) becomes divergent code
+  const int beg = __builtin_amdgcn_readfirstlane(kp.ins_off[c.cta]);
+  const int end = __builtin_amdgcn_readfirstlane(kp.ins_off[c.cta + 1]);
+  c.tok = __builtin_amdgcn_readfirstlane(kp.forced ? kp.forced[0] : kp.first_token);
   uint32_t* trace = nullptr;
   for (int step = 0; step < kp.n_steps; ++step) {
     c.step = step;
@@ -826,7 +984,7 @@ __global__ __launch_bounds__(kThreads, 1) void mk_monokernel(const KParams* __re
     if (tr) trace = kp.trace + (((int64_t)c.cta * kp.trace_steps + step) * kp.max_ins) * 8;
     for (int pc = beg; pc < end; ++pc) {
       c.pc = pc - beg;
-      const Ins in = kp.ins[pc];
+      const Ins in = load_ins(kp.ins + pc);
       c.deadline = 0;  // every wait gets its own watchdog budget
       c.poll_iters = 0;
       uint64_t t_wait = 0;
@@ -848,7 +1006,8 @@ __global__ __launch_bounds__(kThreads, 1) void mk_monokernel(const KParams* __re
         default: break;
       }
       ts_mark(c, 3);
-      if (c.tid == 0) *gp(kp.progress + c.cta) = ((uint32_t)step << 16) | (uint32_t)(c.pc + 1);
+      // written through (not left dirty in L2), so the step's release fence finds nothing to write back
+      if (c.tid == 0) stc32(kp.progress + c.cta, ((uint32_t)step << 16) | (uint32_t)(c.pc + 1));
       if (cta_failed(c)) goto done;
       ts_mark(c, 4);
       if (tr && c.tid == 0) {
@@ -864,9 +1023,11 @@ __global__ __launch_bounds__(kThreads, 1) void mk_monokernel(const KParams* __re
         r[7] = (uint32_t)c.xcc;
       }
     }
-    if (kp.forced && step + 1 < kp.n_steps) c.tok = kp.forced[step + 1];
+    if (kp.forced && step + 1 < kp.n_steps) c.tok = __builtin_amdgcn_readfirstlane(kp.forced[step + 1]);
   }
 done:
+  // let the loaders go (they stop early only when the compute wavefronts do)
+  if (c.lane == 0) lds_st32(small_addr + kOffExit, 1u);
   asm volatile("s_waitcnt vmcnt(0)");
 }
 
@@ -935,13 +1096,13 @@ __global__ void mk_count_kv(const uint16_t* kc, const uint16_t* vc, int64_t rows
 extern "C" {
 // kp_dev: the parameters, already copied to device memory.
 MK_INTERNAL hipError_t mk_launch_monokernel(const KParams* kp_dev, int grid, int lds_bytes, hipStream_t s) {
-  hipLaunchKernelGGL(mk_monokernel, dim3(grid), dim3(kThreads), lds_bytes, s, kp_dev);
+  hipLaunchKernelGGL(mk_monokernel, dim3(grid), dim3(kBlock), lds_bytes, s, kp_dev);
   return hipGetLastError();
 }
 MK_INTERNAL hipError_t mk_kernel_attributes(int lds_bytes, int* occupancy) {
   hipError_t e = hipFuncSetAttribute((const void*)mk_monokernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   if (e != hipSuccess) return e;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, mk_monokernel, kThreads, lds_bytes);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, mk_monokernel, kBlock, lds_bytes);
 }
 MK_INTERNAL hipError_t mk_launch_fill32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
   if (n <= 0) return hipSuccess;

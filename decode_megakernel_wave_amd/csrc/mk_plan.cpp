@@ -16,10 +16,10 @@
 
 namespace mk {
 
-// ring | staged vector | scratch | residual rows | 512 B of small fields:
-// failure flags (64 B), wave sums (32), argmax keys (64), misc (64).
+// rings | staged vector | scratch | residual rows | small fields (flags,
+// wave sums, argmax keys, trace scratch, barrier, ring tags and counts).
 int lds_bytes_for(int kpad_max) {
-  return kWaves * kRing * 1024 + kpad_max * 4 + kScratchFloats * 4 + 1024 * 4 + 512;
+  return kWaves * kRing * 1024 + kpad_max * 4 + kScratchFloats * 4 + 1024 * 4 + kSmallBytes;
 }
 
 int choose_splits(int n_cta, int nkv, int max_seq) {
@@ -172,8 +172,9 @@ std::string build_plan(const Dims& dm, int n_cta, int S, int R, int sync_mode, P
     if (dm.d % 4 || dm.f % 4) return "d_model and ffn must be multiples of 4";
     if (dm.d > kMaxK || dm.f > kMaxK || qd > kMaxK) return "d_model, ffn and n_heads*head_dim must be at most 16384";
     const int G = dm.nq / dm.nkv;
-    if (G * dm.hd > kThreads) return "query heads per kv head times head_dim must be at most 512";
-    if (kWaves * G * (dm.hd + 2) > kScratchFloats) return "attention combine does not fit the LDS scratch";
+    // attention combines at most 8 / (hd / 64) query heads per pass through the scratch
+    if (kWaves * std::min(G, 8 / (dm.hd / 64)) * (dm.hd + 2) > kScratchFloats)
+      return "attention combine does not fit the LDS scratch";
     p.S = S > 0 ? S : choose_splits(n_cta, dm.nkv, dm.max_seq);
     if (p.S < 1 || p.S > 64) return "attn_splits must be in [1, 64]";
     const int hh = dm.hd / 2;

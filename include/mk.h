@@ -175,6 +175,15 @@ int mk_debug_progress(mk_ctx* ctx, uint32_t* host, int32_t capacity);
  * offsets [grid * 8] (int64) and chunk counts [grid * 8] (int32). */
 int mk_debug_streams(const mk_ctx* ctx, const void** base, const void** wave_off, const void** wave_n);
 
+/* Fine timestamps of step 0 of the last launch (recorded only when the
+ * environment variable MK_DEBUG_TS is set at run time): per workgroup and
+ * instruction, 8 uint64 device-clock (100 MHz) marks {0 instruction start,
+ * 1 inputs polled, 2 inputs staged (after the barrier), 3 op end, 4 failure
+ * check done, 5 activations in registers, 6 dot products / attention done,
+ * 7 unused}; zero where not recorded.  capacity is in uint64 and must be at
+ * least grid * max_ins_per_cta * 8. */
+int mk_debug_ts(mk_ctx* ctx, uint64_t* host, int64_t capacity);
+
 const char* mk_last_error(const mk_ctx* ctx);
 void mk_destroy(mk_ctx* ctx);
 
@@ -191,12 +200,7 @@ int mk_chain_run(mk_chain* ch, const float* x0, float* y);
 int mk_chain_stats(const mk_chain* ch, mk_stats* out);
 /* Time journal of the last chain run (same record format as mk_read_trace). */
 int mk_chain_read_trace(mk_chain* ch, uint32_t* host_buf, int64_t capacity_records, int64_t* n_records);
-/* Fine timestamps of step 0 of the last chain run, recorded only when the
- * environment variable MK_DEBUG_TS is set at run time: per workgroup and
- * instruction, 8 uint64 device-clock (100 MHz) marks {0 instruction start, 1 inputs
- * polled, 2 inputs staged (after the barrier), 3 op end, 4 failure check
- * done, 5 activations in registers, 6 dot products done, 7 unused}; zero where not recorded.  capacity is in
- * uint64 and must be at least grid * max_ins_per_cta * 8. */
+/* Fine timestamps of step 0 of the last chain run (layout of mk_debug_ts). */
 int mk_chain_debug_ts(mk_chain* ch, uint64_t* host, int64_t capacity);
 const char* mk_chain_last_error(const mk_chain* ch);
 void mk_chain_destroy(mk_chain* ch);

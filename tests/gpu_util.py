@@ -9,11 +9,27 @@ MARGIN = 2e-2         # tokens must agree where the oracle's top-2 margin exceed
 
 
 def oracle_run(model, w, ids, n):
-    """Free-running oracle: (t0, tokens[n], logits[n, V], prompt logits)."""
+    """Free-running oracle: (t0, tokens[n], logits[n, V], decoder, top-2 margin of the prompt logits)."""
     dec = od.Decoder(w, model.n_heads, model.n_kv_heads, model.rms_eps, model.rope_theta,
                      max_seq=len(ids) + n + 1)
-    t0, toks, logs = dec.greedy(ids, n)
-    return t0, toks, logs, dec
+    l0 = dec.prefill(ids)
+    t = int(np.argmax(l0))
+    t0, toks, logs = t, [], []
+    for s in range(n):
+        lg = dec.step(t, len(ids) + s)
+        t = int(np.argmax(lg))
+        toks.append(t)
+        logs.append(lg)
+    return t0, np.array(toks, dtype=np.int32), np.array(logs), dec, float(od.top2_margin(l0[None])[0])
+
+
+def check_free_run(free, ref, margins):
+    """Greedy tokens must agree until the first step whose oracle top-2 margin is a close call
+    (<= MARGIN): there either token is acceptable and the sequences may part."""
+    for s in range(len(ref)):
+        if margins[s] <= MARGIN:
+            break
+        assert free[s] == ref[s], f"free-running token {s}: {free[s]} != {ref[s]}"
 
 
 def check_step_logits(gpu_logits, ref_logits, gpu_tokens, ref_tokens, tol=LOGIT_TOL):
@@ -36,4 +52,4 @@ def load(mk, model, w, max_seq, **opts):
     return ctx
 
 
-__all__ = ["inputs", "oracle_run", "check_step_logits", "load", "LOGIT_TOL", "MARGIN"]
+__all__ = ["inputs", "oracle_run", "check_step_logits", "check_free_run", "load", "LOGIT_TOL", "MARGIN"]

@@ -10,7 +10,7 @@ import pytest
 
 import decode_megakernel_wave_amd as mk
 from decode_megakernel_wave_amd import inputs
-from gpu_util import check_step_logits, load, oracle_run
+from gpu_util import MARGIN, check_free_run, check_step_logits, load, oracle_run
 
 pytestmark = pytest.mark.gpu
 
@@ -22,9 +22,8 @@ P, N = 32, 16
 def tiny():
     w = inputs.make_weights(CFG, seed=0)
     ids = inputs.make_prompt(CFG, P, seed=1)
-    t0, toks, logs, dec = oracle_run(CFG, w, ids, N)
-    l0 = dec.prefill(ids)
-    return w, ids, t0, toks, logs, l0
+    t0, toks, logs, dec, m0 = oracle_run(CFG, w, ids, N)
+    return w, ids, t0, toks, logs, m0
 
 
 def _forced_run(tiny, **opts):
@@ -42,30 +41,24 @@ def _forced_run(tiny, **opts):
 
 
 def test_tiny_teacher_forced_parity(tiny):
-    w, ids, t0_ref, toks_ref, logs_ref, l0 = tiny
+    w, ids, t0_ref, toks_ref, logs_ref, m0 = tiny
     t0, toks, logits, sent, stats = _forced_run(tiny)
     print("tiny forced: max |dlogit| %.3e" % check_step_logits(logits, logs_ref, toks, toks_ref))
-    from oracle.decoder import top2_margin
-    if top2_margin(l0) > 2e-2:
+    if m0 > MARGIN:
         assert t0 == t0_ref
     assert sent == 0
     assert stats["fault"]["code"] == 0
 
 
 def test_tiny_greedy_matches_oracle_until_first_close_call(tiny):
-    w, ids, t0_ref, toks_ref, logs_ref, _ = tiny
+    w, ids, t0_ref, toks_ref, logs_ref, m0 = tiny
     from oracle.decoder import top2_margin
     ctx = load(mk, CFG, w, P + N + 1)
     try:
         out = mk.mk_generate(ctx, ids, N)
     finally:
         mk.mk_destroy(ctx)
-    ref = np.concatenate([[t0_ref], toks_ref])
-    margins = np.concatenate([[2.0], top2_margin(logs_ref)])  # t0 checked in the forced test
-    for s in range(N + 1):
-        assert out[s] == ref[s], f"step {s}"
-        if margins[s] <= 2e-2:
-            break
+    check_free_run(out, np.concatenate([[t0_ref], toks_ref]), np.concatenate([[m0], top2_margin(logs_ref)]))
 
 
 def test_tiny_counter_mode_is_bitwise_identical(tiny):
