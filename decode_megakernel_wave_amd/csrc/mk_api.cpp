@@ -245,7 +245,7 @@ int launch(Engine& g, KParams& k, int n_steps) {
   g.last.gpu_ms = ms;
   g.last.steps = n_steps;
   g.last.grid = g.grid;
-  g.last.block = kBlock;
+  g.last.block = kThreads;
   g.last.lds_bytes = g.plan.lds_bytes;
   g.last.ring_depth = kRing;
   g.last.stream_bytes = g.plan.stream_bytes();

@@ -1,7 +1,6 @@
 // mk_device.h -- gfx950 device primitives of the monokernel: coherent
-// loads/stores for cross-workgroup sync, an LDS barrier for the compute
-// wavefronts, wavefront DPP reductions, and the LDS weight rings that loader
-// wavefronts fill with nontemporal global->LDS loads.
+// loads/stores for cross-workgroup sync, wavefront DPP reductions, and the
+// per-wavefront LDS weight ring fed by nontemporal global->LDS loads.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -84,39 +83,14 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
   return (const void*)(((uint64_t)hi << 32) | lo);
 }
 
-// Barrier of the kWaves compute wavefronts, through an LDS counter.  The
-// loader wavefronts never reach a barrier (they run their own loop), so the
-// hardware s_barrier, which waits for every wavefront of the workgroup, is
-// used only once, before the roles split.  Each wavefront adds 1 to the
-// counter and waits until it reaches kWaves times the number of barriers it
-// has entered (gen, a per-wavefront count kept by the caller).  The fences
-// name the "local" address space only: global loads and stores in flight
-// stay in flight across the barrier.
-#define MK_LDS __attribute__((address_space(3)))
-template <typename T>
-__device__ __forceinline__ MK_LDS T* lp(T* p) { return (MK_LDS T*)p; }
-
-// Returns false if the barrier did not complete within `ticks` of the device
-// clock or the abort word became non-zero (the caller reports the fault).
-__device__ __forceinline__ bool lds_barrier(uint32_t* bar, uint32_t& gen, uint64_t ticks, const uint32_t* abort) {
+// Workgroup barrier ordering LDS traffic only: the fences name the "local"
+// address space, so outstanding global loads (the weight ring) and stores
+// stay in flight across it, and the compiler may keep values it loaded from
+// global memory in registers (no blanket memory clobber).
+__device__ __forceinline__ void cta_sync_hw() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  gen += kWaves;
-  if (lane_id() == 0) __hip_atomic_fetch_add(lp(bar), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  uint32_t spins = 0;
-  uint64_t deadline = 0;
-  bool ok = true;
-  while ((int32_t)(__hip_atomic_load(lp(bar), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) - gen) < 0) {
-    if ((++spins & 255) == 0) {
-      const uint64_t now = __builtin_amdgcn_s_memrealtime();
-      if (deadline == 0) deadline = now + ticks;
-      if (now > deadline || ldc32(abort) != 0) {
-        ok = false;
-        break;
-      }
-    }
-  }
+  __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  return ok;
 }
 
 __device__ __forceinline__ int xcc_id() {
@@ -150,65 +124,68 @@ __device__ __forceinline__ float wave_max(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
 }
 
-// ---------------------------------------------------------------- weight rings
-// Each compute wavefront consumes one stream of 1 KB chunks (built by the
-// host in consumption order, repeating every step) through a ring of kRing
-// LDS slots.  A free slot holds the ring sentinel in every word.  A loader
-// wavefront DMAs chunk i of the stream into slot i % kRing once the consumer
-// has released the chunk that used the slot before (cons, the consumer's
-// count of finished chunks, exceeds i - kRing).  The consumer reads a chunk
-// until none of its words is the sentinel (the DMA has landed), then refills
-// the slot with the sentinel and advances cons.  The loader therefore never
-// waits for its DMAs to land; it only throttles how many are outstanding.
-//
-// The rings are touched only through inline asm (the DMA, the reads, the
-// refills and the cons words), and volatile asm statements keep their
-// program order, so none of them needs a "memory" clobber (which would make
-// the compiler reload every value it keeps in memory after each chunk).
+// ---------------------------------------------------------------- weight ring
+struct Ring {
+  uint32_t lds;          // LDS byte address of this wavefront's ring
+  const uint8_t* g;      // stream base
+  uint32_t n;            // chunks per step
+  uint32_t issue;        // next chunk (mod n) to request
+  uint32_t slot;         // ring slot holding the next chunk to consume
+};
 
-// Two fp16 NaNs with a full payload: no finite weight pair has this bit pattern.
-constexpr uint32_t kRingSent = 0xFFFFFFFFu;
-
-// LDS word access in program order with the ring asm (address = LDS byte offset).
-__device__ __forceinline__ uint32_t lds_ld32(uint32_t addr) {
-  uint32_t v;
-  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr));
-  return v;
-}
-__device__ __forceinline__ void lds_st32(uint32_t addr, uint32_t v) {
-  asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v));
-}
-
-// Loader side: DMA one chunk (64 lanes x 16 bytes) to LDS byte address
-// lds_addr; lane i's bytes land at lds_addr + 16 i.  At most kInFlight DMAs
-// of this wavefront stay outstanding (loads complete in order).
+// The ring is touched only through inline asm (the DMA that fills a slot and
+// the ds_read that drains it), so none of these statements needs a "memory"
+// clobber: a clobber would make the compiler reload every value it keeps in
+// memory (kernel parameters, LDS pointers) after each chunk, and the next
+// lgkmcnt wait would then stall on those scalar loads.  Volatile asm
+// statements keep their program order relative to each other.
 __device__ __forceinline__ void dma_chunk(uint32_t lds_addr, const uint8_t* g, uint32_t voff) {
   uint32_t save;
   lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
   g = (const uint8_t*)uniform_ptr(g);
   asm volatile(
-      "s_waitcnt vmcnt(%4)\n\t"
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
       "global_load_lds_dwordx4 %2, %3 nt\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(save)
-      : "s"(lds_addr), "v"(voff), "s"(g), "n"(kInFlight - 1));
+      : "s"(lds_addr), "v"(voff), "s"(g));
 }
 
-// Consumer side.
-struct Ring {
-  uint32_t lds;    // LDS byte address of this wavefront's ring
-  uint32_t cons;   // LDS byte address of its consumed-count word
-  uint32_t seq;    // chunks consumed so far in this launch
-  uint32_t slot;   // seq % kRing
-};
+__device__ __forceinline__ void ring_start(Ring& r) {
+  if (r.n == 0) return;
+  const uint32_t lane16 = lane_id() * 16;
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) {
+    dma_chunk(r.lds + i * 1024, r.g, r.issue * 1024 + lane16);
+    r.issue = (r.issue + 1 == r.n) ? 0 : r.issue + 1;
+  }
+  r.slot = 0;
+}
 
-// Read the next N (1..4) chunks (16 bytes per lane each); true when every
-// word of every lane has landed.
+// Next chunk of this wavefront's stream (16 bytes per lane), then refill its
+// slot.  vmcnt(kRing-1): the oldest of the kRing outstanding DMAs (this slot)
+// has landed; lgkmcnt(0): the slot has been read before it is refilled.
+__device__ __forceinline__ u4 ring_next(Ring& r) {
+  const uint32_t addr = r.lds + r.slot * 1024 + lane_id() * 16;
+  u4 v;
+  asm volatile(
+      "s_waitcnt vmcnt(%1)\n\t"
+      "ds_read_b128 %0, %2\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(v)
+      : "n"(kRing - 1), "v"(addr));
+  dma_chunk(r.lds + r.slot * 1024, r.g, r.issue * 1024 + lane_id() * 16);
+  r.issue = (r.issue + 1 == r.n) ? 0 : r.issue + 1;
+  r.slot = (r.slot + 1 == kRing) ? 0 : r.slot + 1;
+  return v;
+}
+
+// Next N chunks (N <= 4) with one LDS wait: vmcnt(kRing-N) means the N
+// oldest DMAs (these slots) have landed.
 template <int N>
-__device__ __forceinline__ bool ring_load(const Ring& r, u4 (&v)[4]) {
-  static_assert(N >= 1 && N <= 4 && N <= kRing, "ring_load reads 1..4 chunks");
+__device__ __forceinline__ void ring_read(Ring& r, u4 (&v)[4]) {
+  static_assert(N >= 1 && N <= 4 && N <= kRing, "ring_read reads 1..4 chunks");
   uint32_t a[4];
   uint32_t slot = r.slot;
 #pragma unroll
@@ -217,40 +194,27 @@ __device__ __forceinline__ bool ring_load(const Ring& r, u4 (&v)[4]) {
     slot = (slot + 1 == kRing) ? 0 : slot + 1;
   }
   if constexpr (N == 1) {
-    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v[0]) : "v"(a[0]));
+    asm volatile("s_waitcnt vmcnt(%1)\n\tds_read_b128 %0, %2\n\ts_waitcnt lgkmcnt(0)"
+                 : "=v"(v[0]) : "n"(kRing - 1), "v"(a[0]));
   } else if constexpr (N == 2) {
-    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
-                 : "=&v"(v[0]), "=&v"(v[1]) : "v"(a[0]), "v"(a[1]));
+    asm volatile("s_waitcnt vmcnt(%2)\n\tds_read_b128 %0, %3\n\tds_read_b128 %1, %4\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]) : "n"(kRing - 2), "v"(a[0]), "v"(a[1]));
   } else if constexpr (N == 3) {
-    asm volatile("ds_read_b128 %0, %3\n\tds_read_b128 %1, %4\n\tds_read_b128 %2, %5\n\t"
+    asm volatile("s_waitcnt vmcnt(%3)\n\tds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\t"
                  "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]) : "v"(a[0]), "v"(a[1]), "v"(a[2]));
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]) : "n"(kRing - 3), "v"(a[0]), "v"(a[1]), "v"(a[2]));
   } else {
-    asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\t"
-                 "ds_read_b128 %3, %7\n\ts_waitcnt lgkmcnt(0)"
+    asm volatile("s_waitcnt vmcnt(%4)\n\tds_read_b128 %0, %5\n\tds_read_b128 %1, %6\n\tds_read_b128 %2, %7\n\t"
+                 "ds_read_b128 %3, %8\n\ts_waitcnt lgkmcnt(0)"
                  : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
-                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+                 : "n"(kRing - 4), "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
   }
-  bool pending = false;
-#pragma unroll
-  for (int k = 0; k < N; ++k)
-    pending |= (v[k][0] == kRingSent) | (v[k][1] == kRingSent) | (v[k][2] == kRingSent) | (v[k][3] == kRingSent);
-  return __ballot(pending) == 0;
-}
-
-// Release the N chunks just read: refill their slots with the sentinel, then
-// advance cons (LDS executes a wavefront's accesses in order, so the loader
-// never sees the new count before the refill).
-template <int N>
-__device__ __forceinline__ void ring_release(Ring& r) {
-  const u4 s = {kRingSent, kRingSent, kRingSent, kRingSent};
 #pragma unroll
   for (int k = 0; k < N; ++k) {
-    asm volatile("ds_write_b128 %0, %1" ::"v"(r.lds + r.slot * 1024 + lane_id() * 16), "v"(s));
+    dma_chunk(r.lds + r.slot * 1024, r.g, r.issue * 1024 + lane_id() * 16);
+    r.issue = (r.issue + 1 == r.n) ? 0 : r.issue + 1;
     r.slot = (r.slot + 1 == kRing) ? 0 : r.slot + 1;
   }
-  r.seq += N;
-  lds_st32(r.cons, r.seq);
 }
 
 __device__ __forceinline__ float dot8(u4 w, const float* a) {

@@ -52,7 +52,6 @@ struct Smem {
   float* wsum;       // [kWaves] partial sums of squares
   uint64_t* keys;    // [kWaves]
   uint32_t* misc;    // [16]
-  uint32_t* bar;     // compute-wavefront barrier counter
 };
 
 struct Cx {
@@ -61,7 +60,6 @@ struct Cx {
   int cta, wave, lane, tid, rep, xcc;
   int step, pos, e, e1, tok, pc;
   int flag_parity;
-  uint32_t gen;       // barrier generation (kWaves per barrier entered)
   bool fail;          // this thread saw a timeout or abort
   uint64_t deadline;
   int poll_iters;
@@ -115,15 +113,8 @@ __device__ __forceinline__ Ins load_ins(const Ins* p) {
   return __builtin_bit_cast(Ins, raw);
 }
 
-// Barrier of the compute wavefronts (the loaders run on their own).  A
-// barrier that times out (a wavefront never arrived) is a fault; after any
-// fault every barrier returns at once, so the workgroup drains.
-__device__ __forceinline__ void cta_sync(Cx& c) {
-  if (!lds_barrier(c.sm.bar, c.gen, c.kp->watchdog_ticks, c.kp->abort_flag)) {
-    raise_fault(c, -7, OP_END, -1, -2);
-    c.fail = true;
-  }
-}
+// Workgroup barrier.
+__device__ __forceinline__ void cta_sync(Cx&) { cta_sync_hw(); }
 
 // Workgroup-wide OR of the per-thread failure flags (also a barrier).
 __device__ __forceinline__ bool cta_failed(Cx& c) {
@@ -304,20 +295,6 @@ __device__ __forceinline__ void publish(const Cx& c, const Buf& b, int l, int64_
 }
 
 // ---------------------------------------------------------------- GEMV core
-// Next N chunks of this wavefront's weight stream: wait until they have
-// landed, then release their slots.
-template <int N>
-__device__ __forceinline__ void ring_read(Cx& c, Ring& r, u4 (&w)[4], const Ins& in) {
-  while (!ring_load<N>(r, w)) {
-    if (c.fail || expired(c, in.op, in.layer, (int)r.seq)) {
-      c.fail = true;
-      break;
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
-  ring_release<N>(r);
-}
-
 template <int CPS, typename Epi>
 __device__ __forceinline__ void gemv(Cx& c, Ring& ring, const Ins& in, const float* vec, float scale, Epi epi) {
   const int ks = in.ks, rg = kWaves / ks, ki = c.wave % ks, gi = c.wave / ks;
@@ -337,12 +314,12 @@ __device__ __forceinline__ void gemv(Cx& c, Ring& ring, const Ins& in, const flo
   for (int u = gi; u < in.nu; u += rg) {
     float r0 = 0.f, r1 = 0.f;
     u4 w[4];
-    ring_read<CPS>(c, ring, w, in);
+    ring_read<CPS>(ring, w);
     if (u == gi) ts_mark(c, 7);
 #pragma unroll
     for (int k = 0; k < CPS; ++k) r0 += dot8(w[k], act[k]);
     if (upr == 2) {
-      ring_read<CPS>(c, ring, w, in);
+      ring_read<CPS>(ring, w);
 #pragma unroll
       for (int k = 0; k < CPS; ++k) r1 += dot8(w[k], act[k]);
     }
@@ -868,58 +845,7 @@ __device__ __forceinline__ void op_chain(Cx& c, Ring& ring, const Ins& in) {
 
 }  // namespace
 
-// Loader wavefront `lid`: keeps the free ring slots of compute wavefronts
-// [lid * NW, lid * NW + NW) requested, for all n_steps of the launch, with at
-// most kInFlight DMAs outstanding.  It never waits for a DMA to land (the
-// consumers check the slots' contents), so it re-arms slots as soon as they
-// are released.
-__device__ __forceinline__ void run_loader(const KParams& kp, uint32_t ring_base, uint32_t small, int cta, int lid) {
-  constexpr int NW = kWaves / kLoaders;
-  const int w0 = lid * NW;
-  const uint32_t lane16 = lane_id() * 16;
-  const uint8_t* base[NW];
-  uint32_t n[NW], total[NW], issued[NW], jn[NW], slot[NW];
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const int wi = cta * kWaves + w0 + i;
-    n[i] = __builtin_amdgcn_readfirstlane((uint32_t)kp.wave_n[wi]);
-    base[i] = (const uint8_t*)uniform_ptr(kp.stream + kp.wave_off[wi] * 1024);
-    total[i] = n[i] * (uint32_t)kp.n_steps;
-    issued[i] = 0;
-    jn[i] = 0;
-    slot[i] = 0;
-  }
-  // lane i < NW reads the consumed count of wavefront w0 + i
-  const uint32_t cons_lane = small + kOffCons + (uint32_t)(w0 + min(lane_id(), NW - 1)) * 4;
-  const uint32_t exitf = small + kOffExit;
-  for (;;) {
-    const uint32_t cons_v = lds_ld32(cons_lane);
-    bool any = false;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      const uint32_t cons = __builtin_amdgcn_readlane(cons_v, i);
-      const uint32_t lim = min(total[i], cons + (uint32_t)kRing);
-      if (issued[i] >= lim) continue;
-      const uint32_t ring = ring_base + (uint32_t)(w0 + i) * kRing * 1024;
-      for (uint32_t k = issued[i]; k < lim; ++k) {
-        dma_chunk(ring + slot[i] * 1024, base[i], jn[i] * 1024 + lane16);
-        jn[i] = (jn[i] + 1 == n[i]) ? 0 : jn[i] + 1;
-        slot[i] = (slot[i] + 1 == kRing) ? 0 : slot[i] + 1;
-      }
-      issued[i] = lim;
-      any = true;
-    }
-    if (any) continue;
-    bool done = true;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) done = done && issued[i] == total[i];
-    if (done || __builtin_amdgcn_readfirstlane(lds_ld32(exitf)) != 0) break;
-    __builtin_amdgcn_s_sleep(1);
-  }
-  asm volatile("s_waitcnt vmcnt(0)");
-}
-
-__global__ __launch_bounds__(kBlock, 1) void mk_monokernel(const KParams* __restrict__ kpp) {
+__global__ __launch_bounds__(kThreads, 1) void mk_monokernel(const KParams* __restrict__ kpp) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const KParams& kp = *kpp;
   Cx c;
@@ -934,7 +860,6 @@ __global__ __launch_bounds__(kBlock, 1) void mk_monokernel(const KParams* __rest
   c.deadline = 0;
   c.poll_iters = 0;
   c.flag_parity = 0;
-  c.gen = 0;
   c.pc = 0;
   // LDS carve-up (must match lds_bytes_for on the host)
   c.sm.base = smem;
@@ -947,25 +872,17 @@ __global__ __launch_bounds__(kBlock, 1) void mk_monokernel(const KParams* __rest
   c.sm.wsum = (float*)(small + kOffWsum);
   c.sm.keys = (uint64_t*)(small + kOffKeys);
   c.sm.misc = (uint32_t*)(small + kOffMisc);
-  c.sm.bar = (uint32_t*)(small + kOffBar);
-  const uint32_t small_addr = (uint32_t)(uintptr_t)small;
-
-  // every ring slot free (sentinel), small fields (barrier counter, exit
-  // flag, consumed counts) zero, before any wavefront looks at them; the only
-  // barrier the loaders join
-  for (int i = c.tid; i < kWaves * kRing * 256; i += kBlock) ((uint32_t*)smem)[i] = kRingSent;
-  for (int i = c.tid; i < kSmallBytes / 4; i += kBlock) ((uint32_t*)small)[i] = 0;
-  __syncthreads();
-  if (c.wave >= kWaves) {
-    run_loader(kp, ring_base, small_addr, c.cta, c.wave - kWaves);
-    return;
-  }
 
   Ring ring;
-  ring.lds = __builtin_amdgcn_readfirstlane(ring_base + c.wave * kRing * 1024);
-  ring.cons = __builtin_amdgcn_readfirstlane(small_addr + kOffCons + c.wave * 4);
-  ring.seq = 0;
-  ring.slot = 0;
+  {
+    const int wi = c.cta * kWaves + c.wave;
+    ring.lds = __builtin_amdgcn_readfirstlane(ring_base + c.wave * kRing * 1024);
+    ring.n = __builtin_amdgcn_readfirstlane((uint32_t)kp.wave_n[wi]);
+    ring.g = (const uint8_t*)uniform_ptr(kp.stream + kp.wave_off[wi] * 1024);
+    ring.issue = 0;
+    ring.slot = 0;
+    ring_start(ring);
+  }
 
   // drop any line an earlier kernel (e.g. the sentinel fill) left in this XCD's L2
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -1026,8 +943,6 @@ __global__ __launch_bounds__(kBlock, 1) void mk_monokernel(const KParams* __rest
     if (kp.forced && step + 1 < kp.n_steps) c.tok = __builtin_amdgcn_readfirstlane(kp.forced[step + 1]);
   }
 done:
-  // let the loaders go (they stop early only when the compute wavefronts do)
-  if (c.lane == 0) lds_st32(small_addr + kOffExit, 1u);
   asm volatile("s_waitcnt vmcnt(0)");
 }
 
@@ -1096,13 +1011,13 @@ __global__ void mk_count_kv(const uint16_t* kc, const uint16_t* vc, int64_t rows
 extern "C" {
 // kp_dev: the parameters, already copied to device memory.
 MK_INTERNAL hipError_t mk_launch_monokernel(const KParams* kp_dev, int grid, int lds_bytes, hipStream_t s) {
-  hipLaunchKernelGGL(mk_monokernel, dim3(grid), dim3(kBlock), lds_bytes, s, kp_dev);
+  hipLaunchKernelGGL(mk_monokernel, dim3(grid), dim3(kThreads), lds_bytes, s, kp_dev);
   return hipGetLastError();
 }
 MK_INTERNAL hipError_t mk_kernel_attributes(int lds_bytes, int* occupancy) {
   hipError_t e = hipFuncSetAttribute((const void*)mk_monokernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   if (e != hipSuccess) return e;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, mk_monokernel, kBlock, lds_bytes);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, mk_monokernel, kThreads, lds_bytes);
 }
 MK_INTERNAL hipError_t mk_launch_fill32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
   if (n <= 0) return hipSuccess;

@@ -12,20 +12,9 @@
 
 namespace mk {
 
-constexpr int kWaves = 8;                 // compute wavefronts per workgroup
-constexpr int kThreads = kWaves * 64;     // 512 compute threads
-#ifndef MK_LOADERS
-#define MK_LOADERS 2
-#endif
-constexpr int kLoaders = MK_LOADERS;      // loader wavefronts (weight DMA only), after the compute ones
-constexpr int kBlock = kThreads + kLoaders * 64;
-static_assert(kWaves % kLoaders == 0, "each loader serves the same number of compute wavefronts");
-constexpr int kRing = 12;                 // 1 KB weight chunks per compute wavefront (LDS ring)
-#ifndef MK_INFLIGHT
-#define MK_INFLIGHT 16
-#endif
-constexpr int kInFlight = MK_INFLIGHT;    // 1 KB DMAs a loader keeps outstanding (<= 63, the vmcnt field)
-static_assert(kInFlight >= 1 && kInFlight <= 63, "kInFlight must fit the vmcnt field");
+constexpr int kWaves = 8;                 // wavefronts per workgroup
+constexpr int kThreads = kWaves * 64;     // 512 threads
+constexpr int kRing = 12;                 // 1 KB weight chunks in flight per wavefront (LDS ring)
 constexpr int kChunkHalfs = 512;          // fp16 values per chunk = 64 lanes x 8
 constexpr int kMaxK = 16384;              // longest GEMV row
 constexpr int kRedDims = 8;               // output dims per attention-reduce unit
@@ -37,10 +26,7 @@ constexpr int kOffFlags = 0;              // u32 [2][kWaves] failure flags (doub
 constexpr int kOffWsum = 64;              // f32 [kWaves] partial sums of squares
 constexpr int kOffKeys = 96;              // u64 [kWaves] argmax keys
 constexpr int kOffMisc = 160;             // u32 [16] trace scratch
-constexpr int kOffBar = 224;              // u32 compute-wavefront barrier counter
-constexpr int kOffExit = 228;             // u32 set when the compute wavefronts leave
-constexpr int kOffCons = 256;             // u32 [kWaves] chunks consumed per stream
-static_assert(kOffCons + kWaves * 4 <= kSmallBytes, "small LDS fields overflow");
+static_assert(kOffMisc + 64 <= kSmallBytes, "small LDS fields overflow");
 
 // Sentinels: bit patterns no computed value takes.  A quiet NaN whose low
 // payload bits can come neither from arithmetic (default NaN 0x7FC00000) nor
