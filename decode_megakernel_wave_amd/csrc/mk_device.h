@@ -60,18 +60,25 @@ __device__ __forceinline__ void stcf(float* p, float v) { stc32(p, __float_as_ui
 
 // Release / acquire between workgroups for data whose arrival the reader
 // cannot see in the data itself (the KV cache and the sentinel re-arms at a
-// step boundary; every stage in counter mode).  A system-scope store is
-// acknowledged by the XCD's L2 before its write-through reaches memory, so
-// waiting for the acknowledgements is not enough: the release also writes
-// the L2 back (agent-scope release fence), and the acquire invalidates the
-// reader's caches.  Measured: without the write-back, counter-mode consumers
-// read values of the previous launch.
-__device__ __forceinline__ void release_stores() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-// The wavefront's stores have reached the L2 (acknowledged).  A workgroup
-// releases with: every wavefront waits for this, a barrier, then one
-// wavefront's release fence writes the (shared) L2 back for all of them.
+// step boundary; every stage in counter mode).  Everything the kernel shares
+// between workgroups is written with the system-scope stores above, which
+// the L2 writes through and acknowledges once they are visible at the
+// coherence point, and read with system-scope loads or, for the KV cache of
+// earlier positions, with plain loads of lines no cache can hold stale (a
+// line is never read before it is written in a launch, and every launch
+// starts by invalidating its caches).  So a release only has to wait for the
+// wavefront's stores to be acknowledged, and an acquire only has to keep the
+// compiler from moving later loads above the poll.  Building with
+// MK_FULL_FENCES selects the agent-scope fences instead (L2 write-back and
+// invalidation), the conservative reading of the memory model.
 __device__ __forceinline__ void stores_acked() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+#ifdef MK_FULL_FENCES
+__device__ __forceinline__ void release_stores() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
 __device__ __forceinline__ void acquire_polled() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+#else
+__device__ __forceinline__ void release_stores() { stores_acked(); }
+__device__ __forceinline__ void acquire_polled() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
+#endif
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
