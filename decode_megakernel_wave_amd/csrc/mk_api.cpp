@@ -297,6 +297,7 @@ struct mk_ctx {
   Buf xa{}, xm{}, q{}, o{}, m{};
   float* att_o = nullptr;
   float* att_ml = nullptr;
+  uint32_t* att_cnt = nullptr;
   uint64_t* lmp = nullptr;
   int64_t lmp_es = 0, lmp_rs = 0;
   int64_t layout[16] = {0};
@@ -338,9 +339,11 @@ int ctx_alloc_arena(mk_ctx* c) {
   c->lmp_rs = p.lm_slots;
   c->lmp_es = (int64_t)p.lm_slots * R;
   off += ((3 * c->lmp_es * 2 + 63) / 64) * 64;
+  const int64_t ocnt = off;  // attention merge counters [L][n_kv_heads], zero at launch
+  off += (((int64_t)L * k.n_kv_heads + 63) / 64) * 64;
   g.arena_words = off;
-  const int64_t lay[9] = {oxa, oxm, oq, oo, om, oao, oml, g.lmp_word_off, off};
-  for (int i = 0; i < 9; ++i) c->layout[i] = lay[i];
+  const int64_t lay[10] = {oxa, oxm, oq, oo, om, oao, oml, g.lmp_word_off, off, ocnt};
+  for (int i = 0; i < 10; ++i) c->layout[i] = lay[i];
   CHK(g.alloc(&g.d_arena, off * 4));
   float* a = g.d_arena;
   c->xa.p = a + oxa;
@@ -351,6 +354,7 @@ int ctx_alloc_arena(mk_ctx* c) {
   c->att_o = a + oao;
   c->att_ml = a + oml;
   c->lmp = (uint64_t*)(a + g.lmp_word_off);
+  c->att_cnt = (uint32_t*)(a + ocnt);
   return MK_OK;
 }
 
@@ -402,6 +406,7 @@ int ctx_run(mk_ctx* c, int n, int first_token, const int32_t* forced, int32_t* t
   kp.m = c->m;
   kp.att_o = c->att_o;
   kp.att_ml = c->att_ml;
+  kp.att_cnt = c->att_cnt;
   kp.lmp = c->lmp;
   kp.lmp_es = c->lmp_es;
   kp.lmp_rs = c->lmp_rs;

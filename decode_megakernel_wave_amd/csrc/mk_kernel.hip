@@ -450,6 +450,56 @@ __device__ __forceinline__ void op_qkv(Cx& c, Ring& ring, const Ins& in) {
   counter_signal(c, in.sync_out);
 }
 
+// Merge the S splits of query head h for output dims [b * kRedDims, +kRedDims):
+// one wavefront, lane s holds split s; publishes o (every replica).
+__device__ __forceinline__ void red_unit(Cx& c, int l, int h, int b) {
+  const KParams& kp = *c.kp;
+  const int hd = kp.hd, S = kp.S;
+  const int s = c.lane;
+  const int64_t base = (((int64_t)c.e * kp.L + l) * kp.nq + h) * S + s;
+  float ms = -INFINITY, ls = 0.f, os[kRedDims];
+#pragma unroll
+  for (int d = 0; d < kRedDims; ++d) os[d] = 0.f;
+  if (s < S) {
+    uint32_t raw[2 + kRedDims];
+    const float* ml = kp.att_ml + base * 2;
+    const float* ov = kp.att_o + base * hd + b * kRedDims;
+    raw[0] = ldc32(ml);
+    raw[1] = ldc32(ml + 1);
+#pragma unroll
+    for (int d = 0; d < kRedDims; ++d) raw[2 + d] = ldc32(ov + d);
+    if (sentinel_mode(c)) {
+      for (;;) {
+        bool pending = false;
+#pragma unroll
+        for (int k = 0; k < 2 + kRedDims; ++k) pending |= raw[k] == kSent32;
+        if (!pending || c.fail) break;
+        if (expired(c, OP_ATT, l, h)) {
+          c.fail = true;
+          break;
+        }
+        poll_pause(c);
+#pragma unroll
+        for (int k = 0; k < 2 + kRedDims; ++k)
+          if (raw[k] == kSent32) raw[k] = ldc32(k < 2 ? ml + k : ov + (k - 2));
+      }
+    }
+    ms = __uint_as_float(raw[0]);
+    ls = __uint_as_float(raw[1]);
+#pragma unroll
+    for (int d = 0; d < kRedDims; ++d) os[d] = __uint_as_float(raw[2 + d]);
+  }
+  const float M = wave_max(ms);
+  const float w = (s < S && ms != -INFINITY) ? exp2f(ms - M) : 0.f;
+  const float Lt = wave_sum(w * ls);
+  const float inv = 1.0f / Lt;
+#pragma unroll
+  for (int d = 0; d < kRedDims; ++d) {
+    const float v = wave_sum(w * os[d]) * inv;
+    publish(c, kp.o, l, (int64_t)h * hd + b * kRedDims + d, v);
+  }
+}
+
 // Split attention for (kv head, split) units: unnormalised partial
 // O = sum_t 2^(s_t - m) v_t, L = sum_t 2^(s_t - m), m = max_t s_t, with
 // scores s_t = q.k_t / sqrt(hd) * log2(e).
@@ -624,66 +674,35 @@ __device__ __forceinline__ void op_att(Cx& c, const Ins& in) {
       else att_pass<2, 4>(c, l, g, sp, j0, ng, t0, t1, G);
     }
     ts_mark(c, 6);
-  }
-  counter_signal(c, in.sync_out);
-}
-
-// Merge the S splits of one query head for kRedDims output dims.
-__device__ __forceinline__ void op_red(Cx& c, const Ins& in) {
-  const KParams& kp = *c.kp;
-  const int l = in.layer, hd = kp.hd, S = kp.S, nb = hd / kRedDims;
-  counter_wait(c, in.sync_in, in.n_in, OP_RED, l);
-  if (!sentinel_mode(c)) cta_sync(c);
-  for (int ui = c.wave; ui < in.nu; ui += kWaves) {
-    const int U = in.u0 + ui, h = U / nb, b = U % nb;
-    const int s = c.lane;
-    const int64_t base = (((int64_t)c.e * kp.L + l) * kp.nq + h) * S + s;
-    float ms = -INFINITY, ls = 0.f, os[kRedDims];
-#pragma unroll
-    for (int d = 0; d < kRedDims; ++d) os[d] = 0.f;
-    if (s < S) {
-      uint32_t raw[2 + kRedDims];
-      const float* ml = kp.att_ml + base * 2;
-      const float* ov = kp.att_o + base * hd + b * kRedDims;
-      raw[0] = ldc32(ml);
-      raw[1] = ldc32(ml + 1);
-#pragma unroll
-      for (int d = 0; d < kRedDims; ++d) raw[2 + d] = ldc32(ov + d);
-      if (sentinel_mode(c)) {
-        for (;;) {
-          bool pending = false;
-#pragma unroll
-          for (int k = 0; k < 2 + kRedDims; ++k) pending |= raw[k] == kSent32;
-          if (!pending || c.fail) break;
-          if (expired(c, OP_RED, l, U)) {
+    // Merge right here, without a reduction stage: the splits of this kv
+    // head share its reduce units (query head, kRedDims dims) -- split sp
+    // takes units sp, sp + S, ... -- and each waits for the S partials it
+    // needs.  Sentinel mode polls the partials themselves; counter mode
+    // counts finished splits per kv head (release before the count).
+    if (!sentinel_mode(c)) {
+      stores_acked();
+      cta_sync(c);
+      if (c.tid == 0) {
+        release_stores();
+        uint32_t* cnt = kp.att_cnt + l * kp.nkv + g;
+        __hip_atomic_fetch_add(gp(cnt), 1u, __ATOMIC_RELAXED, MK_SCOPE);
+        const uint32_t target = (uint32_t)S * (uint32_t)(c.step + 1);
+        while (__hip_atomic_load(gp(cnt), __ATOMIC_RELAXED, MK_SCOPE) < target) {
+          if (expired(c, OP_ATT, l, g)) {
             c.fail = true;
             break;
           }
-          poll_pause(c);
-#pragma unroll
-          for (int k = 0; k < 2 + kRedDims; ++k)
-            if (raw[k] == kSent32) raw[k] = ldc32(k < 2 ? ml + k : ov + (k - 2));
+          __builtin_amdgcn_s_sleep(2);
         }
+        acquire_polled();
       }
-      ms = __uint_as_float(raw[0]);
-      ls = __uint_as_float(raw[1]);
-#pragma unroll
-      for (int d = 0; d < kRedDims; ++d) os[d] = __uint_as_float(raw[2 + d]);
+      cta_sync(c);
     }
-    if (ui == 0) {
-      mark_ready(c);
-      ts_mark(c, 1);
+    {
+      const int nb = hd / kRedDims, units = G * nb;
+      for (int v = sp + c.wave * S; v < units; v += S * kWaves) red_unit(c, l, g * G + v / nb, v % nb);
     }
-    const float M = wave_max(ms);
-    const float w = (s < S && ms != -INFINITY) ? exp2f(ms - M) : 0.f;
-    const float Lt = wave_sum(w * ls);
-    const float inv = 1.0f / Lt;
-#pragma unroll
-    for (int d = 0; d < kRedDims; ++d) {
-      const float v = wave_sum(w * os[d]) * inv;
-      publish(c, kp.o, l, (int64_t)h * hd + b * kRedDims + d, v);
-    }
-    if (ui == 0) ts_mark(c, 6);
+    cta_sync(c);  // the scratch is reused by the next unit
   }
   counter_signal(c, in.sync_out);
 }
@@ -913,7 +932,6 @@ __global__ __launch_bounds__(kThreads, 1) void mk_monokernel(const KParams* __re
       switch (in.op) {
         case OP_QKV: op_qkv(c, ring, in); break;
         case OP_ATT: op_att(c, in); break;
-        case OP_RED: op_red(c, in); break;
         case OP_OPROJ: op_oproj(c, ring, in); break;
         case OP_UPGATE: op_upgate(c, ring, in); break;
         case OP_DOWN: op_down(c, ring, in); break;

@@ -39,7 +39,7 @@ enum Op : uint8_t {
   OP_END = 0,
   OP_QKV = 1,     // RMSNorm + fused QKV GEMV + RoPE, K/V into the cache
   OP_ATT = 2,     // split attention partials (m, l, o) per (kv head, split)
-  OP_RED = 3,     // log-sum-exp merge of the splits -> o
+  OP_RED = 3,     // (unused: the last split of each kv head merges them inside OP_ATT)
   OP_OPROJ = 4,   // x += Wo o
   OP_UPGATE = 5,  // RMSNorm + gate/up GEMV + silu(g) * u
   OP_DOWN = 6,    // x += Wd m
@@ -101,6 +101,7 @@ struct KParams {
   Buf xa, xm, q, o, m, y;
   float* att_o;               // [3][L][nq][S][hd]
   float* att_ml;              // [3][L][nq][S][2]
+  uint32_t* att_cnt;          // [L][nkv] splits finished (zero at launch, monotonic)
   uint64_t* lmp;              // [3][R][lm_slots]
   int64_t lmp_es, lmp_rs;
   const float* x0;            // chain input

@@ -52,13 +52,12 @@ int Plan::mat_rows(int mat) const {
 
 namespace {
 
-// Stage ids within one step.
-int sid_qkv(int l) { return 6 * l + 0; }
-int sid_att(int l) { return 6 * l + 1; }
-int sid_red(int l) { return 6 * l + 2; }
-int sid_o(int l) { return 6 * l + 3; }
-int sid_up(int l) { return 6 * l + 4; }
-int sid_dn(int l) { return 6 * l + 5; }
+// Stage ids within one step (the attention stage also merges its splits).
+int sid_qkv(int l) { return 5 * l + 0; }
+int sid_att(int l) { return 5 * l + 1; }
+int sid_o(int l) { return 5 * l + 2; }
+int sid_up(int l) { return 5 * l + 3; }
+int sid_dn(int l) { return 5 * l + 4; }
 
 // Units of a stage dealt to workgroups: contiguous balanced ranges when there
 // are at least as many units as workgroups, else one unit for each of the
@@ -181,14 +180,13 @@ std::string build_plan(const Dims& dm, int n_cta, int S, int R, int sync_mode, P
     for (int l = 0; l < dm.L; ++l) {
       stages.push_back({OP_QKV, l, (dm.nq + 2 * dm.nkv) * hh, 2, dm.d, l == 0 ? -1 : sid_dn(l - 1), sid_qkv(l)});
       stages.push_back({OP_ATT, l, dm.nkv * p.S, 0, 0, sid_qkv(l), sid_att(l)});
-      stages.push_back({OP_RED, l, dm.nq * (dm.hd / kRedDims), 0, 0, sid_att(l), sid_red(l)});
-      stages.push_back({OP_OPROJ, l, dm.d, 1, qd, sid_red(l), sid_o(l)});
+      stages.push_back({OP_OPROJ, l, dm.d, 1, qd, sid_att(l), sid_o(l)});
       stages.push_back({OP_UPGATE, l, dm.f, 2, dm.d, sid_o(l), sid_up(l)});
       stages.push_back({OP_DOWN, l, dm.d, 1, dm.f, sid_up(l), sid_dn(l)});
     }
-    stages.push_back({OP_LMHEAD, dm.L, dm.V, 1, dm.d, sid_dn(dm.L - 1), 6 * dm.L});
-    stages.push_back({OP_ARGMAX, dm.L, 1, 0, 0, 6 * dm.L, -1});
-    p.n_sync = 6 * dm.L + 1;
+    stages.push_back({OP_LMHEAD, dm.L, dm.V, 1, dm.d, sid_dn(dm.L - 1), 5 * dm.L});
+    stages.push_back({OP_ARGMAX, dm.L, 1, 0, 0, 5 * dm.L, -1});
+    p.n_sync = 5 * dm.L + 1;
     kpad_max = std::max({kpad(dm.d), kpad(qd), kpad(dm.f), (G + 2) * dm.hd});
     const int64_t per_layer = (int64_t)(qd + 2 * dm.nkv * dm.hd) * dm.d + (int64_t)dm.d * qd + 3LL * dm.f * dm.d;
     p.weight_bytes = 2 * (per_layer * dm.L + (int64_t)dm.V * dm.d + (int64_t)dm.d * (2 * dm.L + 1) + dm.d);
@@ -327,13 +325,12 @@ std::string check_plan(const Plan& p) {
   if (!dm.chain) {
     const int hh = dm.hd / 2;
     for (int l = 0; l < dm.L; ++l) {
-      if ((int)cover[6 * l + 0].size() != (dm.nq + 2 * dm.nkv) * hh) return "QKV units incomplete";
-      if ((int)cover[6 * l + 1].size() != dm.nkv * p.S) return "attention units incomplete";
-      if ((int)cover[6 * l + 2].size() != dm.nq * dm.hd / kRedDims) return "reduce units incomplete";
-      if ((int)cover[6 * l + 3].size() != dm.d || (int)cover[6 * l + 5].size() != dm.d) return "residual rows incomplete";
-      if ((int)cover[6 * l + 4].size() != dm.f) return "MLP units incomplete";
+      if ((int)cover[sid_qkv(l)].size() != (dm.nq + 2 * dm.nkv) * hh) return "QKV units incomplete";
+      if ((int)cover[sid_att(l)].size() != dm.nkv * p.S) return "attention units incomplete";
+      if ((int)cover[sid_o(l)].size() != dm.d || (int)cover[sid_dn(l)].size() != dm.d) return "residual rows incomplete";
+      if ((int)cover[sid_up(l)].size() != dm.f) return "MLP units incomplete";
     }
-    if ((int)cover[6 * dm.L].size() != dm.V) return "LM-head rows incomplete";
+    if ((int)cover[5 * dm.L].size() != dm.V) return "LM-head rows incomplete";
   } else {
     for (int i = 0; i < dm.chain_stages; ++i)
       if ((int)cover[i].size() != dm.chain_n) return "chain rows incomplete";

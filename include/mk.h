@@ -163,8 +163,8 @@ int mk_read_trace(mk_ctx* ctx, uint32_t* host_buf, int64_t capacity_records, int
 /* Diagnostics.  Copy n_words 32-bit words of the sync-buffer arena starting
  * at word_off into host memory.  mk_debug_layout gives the word offsets of
  * its regions: [0] xa, [1] xm, [2] q, [3] o, [4] m, [5] att_o, [6] att_ml,
- * [7] argmax keys (uint64), [8] arena size; and [9] per-workgroup progress
- * words follow in mk_debug_progress. */
+ * [7] argmax keys (uint64), [8] arena size, [9] attention merge counters
+ * (uint32 [n_layers][n_kv_heads]). */
 int mk_debug_layout(const mk_ctx* ctx, int64_t* offsets /* [16] */);
 int mk_debug_arena(mk_ctx* ctx, int64_t word_off, int64_t n_words, uint32_t* host);
 /* (step << 16) | (pc + 1) of the last instruction each workgroup finished in

@@ -105,9 +105,9 @@ def test_plan_accepts_workloads(name, grid):
     assert info["stream_bytes"] == 2 * _padded_params(m) == info["stream_chunks"] * 1024
     # algorithmic bytes: the matrices, the 2L+1 norm gains and one embedding row
     assert info["weight_bytes"] == 2 * (_matrix_params(m) + (2 * m.n_layers + 1) * m.d_model + m.d_model)
-    # stages with outputs: per layer QKV, attention, reduce, O, up/gate, down; then the LM head
+    # stages with outputs: per layer QKV, attention (with the split merge), O, up/gate, down; then the LM head
     # (its argmax keys are the last stage's output; the argmax produces only the token)
-    assert info["n_sync_ids"] == 6 * m.n_layers + 1
+    assert info["n_sync_ids"] == 5 * m.n_layers + 1
     mean = info["stream_chunks"] / (grid * 8)
     assert info["min_wave_chunks"] <= mean <= info["max_wave_chunks"]
     if grid == 256 and m is inputs.M2B:
