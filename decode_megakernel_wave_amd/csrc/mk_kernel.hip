@@ -505,12 +505,21 @@ __device__ __forceinline__ void red_unit(Cx& c, int l, int h, int b) {
 // scores s_t = q.k_t / sqrt(hd) * log2(e).
 //
 // Query heads [j0, j0 + ng) of the group (ng <= GP) over the positions
-// [t0, t1): each wavefront takes t0 + wave, t0 + wave + kWaves, ... in
+// [t0, t1), for head_dim HD.  A K or V row is HD fp16 = HD / 8 lanes of 16
+// bytes, so one 16-byte load per lane covers PPI = 512 / HD positions: lane
+// `lane` holds dims [dl * 8, dl * 8 + 8) of position slot `sub`.  Each
+// wavefront takes position groups wave, wave + kWaves, ... and keeps up to
+// 8 groups of K and V loads in flight before computing; every lane
+// keeps its own online-softmax state (m, l, o) for its slot, the slots are
+// merged with cross-lane shuffles, then the wavefronts through the scratch.
+
+// Short splits: query heads [j0, j0 + ng) of the group (ng <= GP) over the
+// positions [t0, t1), one position per wavefront at a time: each wavefront takes t0 + wave, t0 + wave + kWaves, ... in
 // batches of kBatch whose K/V loads are all issued before any score is
 // computed; lane i holds dims [i*DPL, i*DPL + DPL).  GP * DPL <= 8 keeps the
 // accumulators in 8 registers per lane whatever the head geometry.
 template <int GP, int DPL>
-__device__ __forceinline__ void att_pass(Cx& c, int l, int g, int sp, int j0, int ng, int t0, int t1, int G) {
+__device__ __forceinline__ void att_pass_pos(Cx& c, int l, int g, int sp, int j0, int ng, int t0, int t1, int G) {
   const KParams& kp = *c.kp;
   const int hd = kp.hd, S = kp.S;
   constexpr int kBatch = 4;
@@ -615,6 +624,161 @@ __device__ __forceinline__ void att_pass(Cx& c, int l, int g, int sp, int j0, in
   cta_sync(c);  // scratch reused by the next pass
 }
 
+// Sum over each aligned group of LPP lanes (8, 16 or 32), in every lane of
+// the group: DPP within 16-lane rows, one permute across rows for 32.
+template <int LPP>
+__device__ __forceinline__ float slot_sum(float v) {
+  v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);   // row_half_mirror: 8-lane sums
+  if constexpr (LPP >= 16) v += dpp<0x140>(v);  // row_mirror: 16-lane sums
+  if constexpr (LPP >= 32) v += __shfl_xor(v, 16);
+  return v;
+}
+
+template <int HD, int GP>
+__device__ __forceinline__ void att_pass(Cx& c, int l, int g, int sp, int j0, int ng, int t0, int t1, int G) {
+  const KParams& kp = *c.kp;
+  const int S = kp.S;
+  constexpr int LPP = HD / 8, PPI = 64 / LPP;
+  constexpr int kAttBatch = GP >= 4 ? 4 : 8;  // position groups in flight (registers: 8 per group)
+  const int sub = c.lane / LPP, dl = c.lane % LPP;
+  const float* qs = c.sm.vec;            // [G][HD]
+  const float* kcur = c.sm.vec + G * HD; // [HD]
+  const float* vcur = kcur + HD;         // [HD]
+  float q[GP][8], m[GP], lsum[GP], o[GP][8];
+#pragma unroll
+  for (int j = 0; j < GP; ++j) {
+    m[j] = -INFINITY;
+    lsum[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      o[j][e] = 0.f;
+      q[j][e] = j < ng ? qs[(j0 + j) * HD + dl * 8 + e] : 0.f;
+    }
+  }
+  const int64_t head_off = ((int64_t)l * kp.nkv + g) * kp.max_seq * HD + dl * 8;
+  const uint16_t* kbase = kp.kc + head_off;
+  const uint16_t* vbase = kp.vc + head_off;
+  const int ngroups = (t1 - t0 + PPI - 1) / PPI;
+  for (int gb = c.wave; gb < ngroups; gb += kWaves * kAttBatch) {
+    u4 kb[kAttBatch], vb[kAttBatch];
+#pragma unroll
+    for (int b = 0; b < kAttBatch; ++b) {
+      const int t = t0 + (gb + b * kWaves) * PPI + sub;
+      if (t < t1 && t != c.pos) {
+        kb[b] = *gp((const u4*)(kbase + (int64_t)t * HD));
+        vb[b] = *gp((const u4*)(vbase + (int64_t)t * HD));
+      } else {
+        kb[b] = u4{0u, 0u, 0u, 0u};
+        vb[b] = u4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kAttBatch; ++b) {
+      const int t = t0 + (gb + b * kWaves) * PPI + sub;
+      const bool valid = t < t1;
+      if (__ballot(valid) == 0) break;
+      float kf[8], vf[8];
+      const h8 kh = __builtin_bit_cast(h8, kb[b]), vh = __builtin_bit_cast(h8, vb[b]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        kf[e] = t == c.pos ? kcur[dl * 8 + e] : (float)kh[e];
+        vf[e] = t == c.pos ? vcur[dl * 8 + e] : (float)vh[e];
+      }
+#pragma unroll
+      for (int j = 0; j < GP; ++j) {
+        if (j >= ng) break;
+        float sc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sc = fmaf(q[j][e], kf[e], sc);
+        sc = slot_sum<LPP>(sc);
+        const float mn = valid ? fmaxf(m[j], sc) : m[j];
+        const float al = mn == -INFINITY ? 0.f : exp2f(m[j] - mn);
+        const float pv = valid ? exp2f(sc - mn) : 0.f;
+        lsum[j] = lsum[j] * al + pv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[j][e] = o[j][e] * al + pv * vf[e];
+        m[j] = mn;
+      }
+    }
+  }
+  // merge the PPI position slots of the wavefront (lanes dl, dl + LPP, ...)
+#pragma unroll
+  for (int x = LPP; x < 64; x <<= 1) {
+#pragma unroll
+    for (int j = 0; j < GP; ++j) {
+      const float m2 = __shfl_xor(m[j], x), l2 = __shfl_xor(lsum[j], x);
+      const float mn = fmaxf(m[j], m2);
+      const float a1 = m[j] == -INFINITY ? 0.f : exp2f(m[j] - mn);
+      const float a2 = m2 == -INFINITY ? 0.f : exp2f(m2 - mn);
+      lsum[j] = lsum[j] * a1 + l2 * a2;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[j][e] = o[j][e] * a1 + __shfl_xor(o[j][e], x) * a2;
+      m[j] = mn;
+    }
+  }
+  // combine the wavefronts: scratch [wave][ng][HD + 2]
+  float* scr = c.sm.scratch;
+  const int rec = HD + 2;
+  if (sub == 0) {
+#pragma unroll
+    for (int j = 0; j < GP; ++j) {
+      if (j >= ng) break;
+      float* r = scr + (c.wave * ng + j) * rec;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r[2 + dl * 8 + e] = o[j][e];
+      if (dl == 0) {
+        r[0] = m[j];
+        r[1] = lsum[j];
+      }
+    }
+  }
+  cta_sync(c);
+  for (int i = c.tid; i < ng * HD; i += kThreads) {
+    const int j = i / HD, dd = i % HD;
+    float M = -INFINITY;
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, scr[(w * ng + j) * rec]);
+    float Lt = 0.f, Ot = 0.f;
+    if (M != -INFINITY) {
+      for (int w = 0; w < kWaves; ++w) {
+        const float* r = scr + (w * ng + j) * rec;
+        const float al = exp2f(r[0] - M);
+        Lt += al * r[1];
+        Ot += al * r[2 + dd];
+      }
+    }
+    const int qh = g * G + j0 + j;
+    const int64_t po = ((((int64_t)c.e * kp.L + l) * kp.nq + qh) * S + sp);
+    const int64_t po1 = ((((int64_t)c.e1 * kp.L + l) * kp.nq + qh) * S + sp);
+    stcf(kp.att_o + po * HD + dd, Ot);
+    if (sentinel_mode(c)) stc32(kp.att_o + po1 * HD + dd, kSent32);
+    if (dd == 0) {
+      stcf(kp.att_ml + po * 2, M);
+      stcf(kp.att_ml + po * 2 + 1, Lt);
+      if (sentinel_mode(c)) {
+        stc32(kp.att_ml + po1 * 2, kSent32);
+        stc32(kp.att_ml + po1 * 2 + 1, kSent32);
+      }
+    }
+  }
+  cta_sync(c);  // scratch reused by the next pass
+}
+
+// Query heads per pass: at most 4 (2 for head_dim 256), so the combine fits
+// the scratch: kWaves * heads * (HD + 2) floats.
+template <int HD>
+__device__ __forceinline__ void att_heads(Cx& c, int l, int g, int sp, int t0, int t1, int G) {
+  constexpr int kMaxPass = HD == 256 ? 2 : 4;
+  if (G == 1) {
+    att_pass<HD, 1>(c, l, g, sp, 0, 1, t0, t1, G);
+  } else if (G == 2 || kMaxPass == 2) {
+    for (int j0 = 0; j0 < G; j0 += 2) att_pass<HD, 2>(c, l, g, sp, j0, min(2, G - j0), t0, t1, G);
+  } else {
+    for (int j0 = 0; j0 < G; j0 += 4) att_pass<HD, 4>(c, l, g, sp, j0, min(4, G - j0), t0, t1, G);
+  }
+}
+
 __device__ __forceinline__ void op_att(Cx& c, const Ins& in) {
   const KParams& kp = *c.kp;
   const int l = in.layer;
@@ -665,13 +829,21 @@ __device__ __forceinline__ void op_att(Cx& c, const Ins& in) {
     ts_mark(c, 2);
     if (ui == 0) mark_ready(c);
     if (touch == 1.2345e-30f && c.tid == kThreads) c.fail = true;  // keeps the touches; never true
-    const int dpl = hd / 64;
-    const int gp_max = 8 / dpl;
-    for (int j0 = 0; j0 < G; j0 += gp_max) {
-      const int ng = min(gp_max, G - j0);
-      if (dpl == 1) att_pass<8, 1>(c, l, g, sp, j0, ng, t0, t1, G);
-      else if (dpl == 2) att_pass<4, 2>(c, l, g, sp, j0, ng, t0, t1, G);
-      else att_pass<2, 4>(c, l, g, sp, j0, ng, t0, t1, G);
+    if (t1 - t0 <= 4 * kWaves) {
+      // short split (a few positions per wavefront): one position per wavefront per step
+      const int dpl = hd / 64, gp_max = 8 / dpl;
+      for (int j0 = 0; j0 < G; j0 += gp_max) {
+        const int ng = min(gp_max, G - j0);
+        if (dpl == 1) att_pass_pos<8, 1>(c, l, g, sp, j0, ng, t0, t1, G);
+        else if (dpl == 2) att_pass_pos<4, 2>(c, l, g, sp, j0, ng, t0, t1, G);
+        else att_pass_pos<2, 4>(c, l, g, sp, j0, ng, t0, t1, G);
+      }
+    } else if (hd == 64) {
+      att_heads<64>(c, l, g, sp, t0, t1, G);
+    } else if (hd == 128) {
+      att_heads<128>(c, l, g, sp, t0, t1, G);
+    } else {
+      att_heads<256>(c, l, g, sp, t0, t1, G);
     }
     ts_mark(c, 6);
     // Merge right here, without a reduction stage: the splits of this kv
