@@ -846,18 +846,29 @@ __device__ __forceinline__ void op_att(Cx& c, const Ins& in) {
       att_heads<256>(c, l, g, sp, t0, t1, G);
     }
     ts_mark(c, 6);
-    // Merge right here, without a reduction stage: the splits of this kv
-    // head share its reduce units (query head, kRedDims dims) -- split sp
-    // takes units sp, sp + S, ... -- and each waits for the S partials it
-    // needs.  Sentinel mode polls the partials themselves; counter mode
-    // counts finished splits per kv head (release before the count).
     if (!sentinel_mode(c)) {
+      // counter mode: count this finished split of kv head g (release before the count)
       stores_acked();
       cta_sync(c);
       if (c.tid == 0) {
         release_stores();
-        uint32_t* cnt = kp.att_cnt + l * kp.nkv + g;
-        __hip_atomic_fetch_add(gp(cnt), 1u, __ATOMIC_RELAXED, MK_SCOPE);
+        __hip_atomic_fetch_add(gp(kp.att_cnt + l * kp.nkv + g), 1u, __ATOMIC_RELAXED, MK_SCOPE);
+      }
+    }
+    if (ui + 1 < in.nu) cta_sync(c);  // the staging and the scratch are reused by the next unit
+  }
+  // Merge right here, without a reduction stage: the splits of a kv head
+  // share its reduce units (query head, kRedDims dims) -- split sp takes
+  // units sp, sp + S, ... -- and each waits for the S partials it needs.
+  // Every partial of this workgroup is published before it waits for any
+  // other, so a workgroup holding several splits of one head cannot wait on
+  // itself.  Sentinel mode polls the partials themselves; counter mode waits
+  // until all S splits of the head are counted.
+  for (int ui = 0; ui < in.nu; ++ui) {
+    const int U = in.u0 + ui, g = U / S, sp = U % S;
+    if (!sentinel_mode(c) && (ui == 0 || sp == 0)) {
+      if (c.tid == 0) {
+        const uint32_t* cnt = kp.att_cnt + l * kp.nkv + g;
         const uint32_t target = (uint32_t)S * (uint32_t)(c.step + 1);
         while (__hip_atomic_load(gp(cnt), __ATOMIC_RELAXED, MK_SCOPE) < target) {
           if (expired(c, OP_ATT, l, g)) {
@@ -870,12 +881,10 @@ __device__ __forceinline__ void op_att(Cx& c, const Ins& in) {
       }
       cta_sync(c);
     }
-    {
-      const int nb = hd / kRedDims, units = G * nb;
-      for (int v = sp + c.wave * S; v < units; v += S * kWaves) red_unit(c, l, g * G + v / nb, v % nb);
-    }
-    cta_sync(c);  // the scratch is reused by the next unit
+    const int nb = hd / kRedDims, units = G * nb;
+    for (int v = sp + c.wave * S; v < units; v += S * kWaves) red_unit(c, l, g * G + v / nb, v % nb);
   }
+  cta_sync(c);  // the next instruction restages the vector the partials read
   counter_signal(c, in.sync_out);
 }
 

@@ -113,3 +113,17 @@ def test_tiny_small_grids(tiny):
         assert st["grid"] == g
         check_step_logits(logits, logs_ref, toks, toks_ref)
         assert sent == 0
+
+
+def test_tiny_several_splits_per_workgroup(tiny):
+    """More attention units (kv head x split) than workgroups: one workgroup
+    holds several splits of the same kv head and merges them only after all
+    its partials are published; both synchronisation modes."""
+    w, ids, t0_ref, toks_ref, logs_ref, _ = tiny
+    for g, s in ((1, 3), (8, 16), (61, 16)):
+        for mode in (mk.MK_SYNC_SENTINEL, mk.MK_SYNC_COUNTER):
+            _, toks, logits, sent, st = _forced_run(tiny, grid=g, attn_splits=s, sync_mode=mode)
+            assert st["grid"] == g and st["fault"]["code"] == 0
+            err = check_step_logits(logits, logs_ref, toks, toks_ref)
+            print(f"grid {g} splits {s} mode {mode}: max |dlogit| {err:.2e}")
+            assert sent == 0
