@@ -138,6 +138,7 @@ struct Ring {
   uint32_t n;            // chunks per step
   uint32_t issue;        // next chunk (mod n) to request
   uint32_t slot;         // ring slot holding the next chunk to consume
+  uint32_t deferred;     // slots read but not yet refilled (the refill waits for ring_flush)
 };
 
 // The ring is touched only through inline asm (the DMA that fills a slot and
@@ -168,28 +169,34 @@ __device__ __forceinline__ void ring_start(Ring& r) {
     r.issue = (r.issue + 1 == r.n) ? 0 : r.issue + 1;
   }
   r.slot = 0;
+  r.deferred = 0;
 }
 
-// Next chunk of this wavefront's stream (16 bytes per lane), then refill its
-// slot.  vmcnt(kRing-1): the oldest of the kRing outstanding DMAs (this slot)
-// has landed; lgkmcnt(0): the slot has been read before it is refilled.
-__device__ __forceinline__ u4 ring_next(Ring& r) {
-  const uint32_t addr = r.lds + r.slot * 1024 + lane_id() * 16;
-  u4 v;
-  asm volatile(
-      "s_waitcnt vmcnt(%1)\n\t"
-      "ds_read_b128 %0, %2\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=v"(v)
-      : "n"(kRing - 1), "v"(addr));
-  dma_chunk(r.lds + r.slot * 1024, r.g, r.issue * 1024 + lane_id() * 16);
-  r.issue = (r.issue + 1 == r.n) ? 0 : r.issue + 1;
-  r.slot = (r.slot + 1 == kRing) ? 0 : r.slot + 1;
-  return v;
+// Read N ring chunks (N <= 4) at LDS addresses a[] after waiting for
+// vmcnt(W), with one LDS wait; one asm block, so no use of v[] can be
+// scheduled before the data is there.
+template <int N, int W>
+__device__ __forceinline__ void ring_load(const uint32_t (&a)[4], u4 (&v)[4]) {
+  if constexpr (N == 1) {
+    asm volatile("s_waitcnt vmcnt(%1)\n\tds_read_b128 %0, %2\n\ts_waitcnt lgkmcnt(0)"
+                 : "=v"(v[0]) : "n"(W), "v"(a[0]));
+  } else if constexpr (N == 2) {
+    asm volatile("s_waitcnt vmcnt(%2)\n\tds_read_b128 %0, %3\n\tds_read_b128 %1, %4\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]) : "n"(W), "v"(a[0]), "v"(a[1]));
+  } else if constexpr (N == 3) {
+    asm volatile("s_waitcnt vmcnt(%3)\n\tds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]) : "n"(W), "v"(a[0]), "v"(a[1]), "v"(a[2]));
+  } else {
+    asm volatile("s_waitcnt vmcnt(%4)\n\tds_read_b128 %0, %5\n\tds_read_b128 %1, %6\n\tds_read_b128 %2, %7\n\t"
+                 "ds_read_b128 %3, %8\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+                 : "n"(W), "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+  }
 }
 
 // Next N chunks (N <= 4) with one LDS wait: vmcnt(kRing-N) means the N
-// oldest DMAs (these slots) have landed.
+// oldest DMAs (these slots) have landed.  Then refill the N slots.
 template <int N>
 __device__ __forceinline__ void ring_read(Ring& r, u4 (&v)[4]) {
   static_assert(N >= 1 && N <= 4 && N <= kRing, "ring_read reads 1..4 chunks");
@@ -200,28 +207,44 @@ __device__ __forceinline__ void ring_read(Ring& r, u4 (&v)[4]) {
     a[k] = r.lds + slot * 1024 + lane_id() * 16;
     slot = (slot + 1 == kRing) ? 0 : slot + 1;
   }
-  if constexpr (N == 1) {
-    asm volatile("s_waitcnt vmcnt(%1)\n\tds_read_b128 %0, %2\n\ts_waitcnt lgkmcnt(0)"
-                 : "=v"(v[0]) : "n"(kRing - 1), "v"(a[0]));
-  } else if constexpr (N == 2) {
-    asm volatile("s_waitcnt vmcnt(%2)\n\tds_read_b128 %0, %3\n\tds_read_b128 %1, %4\n\ts_waitcnt lgkmcnt(0)"
-                 : "=&v"(v[0]), "=&v"(v[1]) : "n"(kRing - 2), "v"(a[0]), "v"(a[1]));
-  } else if constexpr (N == 3) {
-    asm volatile("s_waitcnt vmcnt(%3)\n\tds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\t"
-                 "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]) : "n"(kRing - 3), "v"(a[0]), "v"(a[1]), "v"(a[2]));
-  } else {
-    asm volatile("s_waitcnt vmcnt(%4)\n\tds_read_b128 %0, %5\n\tds_read_b128 %1, %6\n\tds_read_b128 %2, %7\n\t"
-                 "ds_read_b128 %3, %8\n\ts_waitcnt lgkmcnt(0)"
-                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
-                 : "n"(kRing - 4), "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
-  }
+  ring_load<N, kRing - N>(a, v);
 #pragma unroll
   for (int k = 0; k < N; ++k) {
     dma_chunk(r.lds + r.slot * 1024, r.g, r.issue * 1024 + lane_id() * 16);
     r.issue = (r.issue + 1 == r.n) ? 0 : r.issue + 1;
     r.slot = (r.slot + 1 == kRing) ? 0 : r.slot + 1;
   }
+}
+
+// Next N chunks without refilling their slots: W must be kRing - N -
+// r.deferred, the vmcnt that leaves the N oldest outstanding DMAs landed.
+// The refills are issued later by ring_flush, so loads issued in between
+// (the next instruction's input polls) do not return behind them.
+template <int N, int W>
+__device__ __forceinline__ void ring_read_tail(Ring& r, u4 (&v)[4]) {
+  static_assert(N >= 1 && N <= 4 && W >= 0, "ring_read_tail reads 1..4 chunks");
+  uint32_t a[4];
+  uint32_t slot = r.slot;
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    a[k] = r.lds + slot * 1024 + lane_id() * 16;
+    slot = (slot + 1 == kRing) ? 0 : slot + 1;
+  }
+  ring_load<N, W>(a, v);
+  r.slot = slot;
+  r.deferred += N;
+}
+
+// Issue the refills that ring_read_tail held back, in slot order.
+__device__ __forceinline__ void ring_flush(Ring& r) {
+  const uint32_t lane16 = lane_id() * 16;
+  uint32_t s = (r.slot + kRing - r.deferred) % kRing;
+  for (uint32_t k = 0; k < r.deferred; ++k) {
+    dma_chunk(r.lds + s * 1024, r.g, r.issue * 1024 + lane16);
+    r.issue = (r.issue + 1 == r.n) ? 0 : r.issue + 1;
+    s = (s + 1 == kRing) ? 0 : s + 1;
+  }
+  r.deferred = 0;
 }
 
 __device__ __forceinline__ float dot8(u4 w, const float* a) {

@@ -57,6 +57,7 @@ struct Smem {
 struct Cx {
   const KParams* kp;
   Smem sm;
+  Ring* ring;
   int cta, wave, lane, tid, rep, xcc;
   int step, pos, e, e1, tok, pc;
   int flag_parity;
@@ -294,6 +295,36 @@ __device__ __forceinline__ void publish(const Cx& c, const Buf& b, int l, int64_
   else if (c.lane < 2 * R && sentinel_mode(c)) stc32(buf_at(b, c.e1, l, c.lane - R) + idx, kSent32);
 }
 
+// Rows [u0, u0 + nu) of b (epoch e) from LDS src to every replica, with
+// stores that are contiguous across the lanes of a wavefront, then (when
+// `rearm`) the same rows of epoch e1 back to the sentinel.  A GEMV that owns
+// a contiguous range of output rows writes them this way after its last row,
+// so the memory system sees a few full-line writes per replica instead of
+// one partial-line write per element and replica.
+__device__ __forceinline__ void publish_rows(const Cx& c, const Buf& b, int e, int l, int u0, int nu, const float* src, bool rearm) {
+  const int R = c.kp->R, n = nu * R;
+  for (int i = c.tid; i < n; i += kThreads) {
+    const int r = i / nu, k = i - r * nu;
+    stcf(buf_at(b, e, l, r) + u0 + k, src[k]);
+  }
+  if (rearm && sentinel_mode(c)) {
+    for (int i = c.tid; i < n; i += kThreads) {
+      const int r = i / nu, k = i - r * nu;
+      stc32(buf_at(b, c.e1, l, r) + u0 + k, kSent32);
+    }
+  }
+}
+
+// Output rows a GEMV instruction can stage in LDS (sm.resid) before
+// publish_rows; longer ranges (very small grids) publish row by row.
+__device__ __forceinline__ bool staged_rows(const Ins& in) {
+#ifdef MK_DIRECT_PUBLISH
+  return false;
+#else
+  return in.nu <= kResidRows;
+#endif
+}
+
 // ---------------------------------------------------------------- GEMV core
 template <int CPS, typename Epi>
 __device__ __forceinline__ void gemv(Cx& c, Ring& ring, const Ins& in, const float* vec, float scale, Epi epi) {
@@ -314,12 +345,21 @@ __device__ __forceinline__ void gemv(Cx& c, Ring& ring, const Ins& in, const flo
   for (int u = gi; u < in.nu; u += rg) {
     float r0 = 0.f, r1 = 0.f;
     u4 w[4];
-    ring_read<CPS>(ring, w);
+#ifdef MK_DEFER
+    // the wavefront's last unit: hold its refills back until the next
+    // instruction's inputs have been polled
+    const bool tail = u + rg >= in.nu;
+#else
+    constexpr bool tail = false;
+#endif
+    if (tail) ring_read_tail<CPS, kRing - CPS>(ring, w);
+    else ring_read<CPS>(ring, w);
     if (u == gi) ts_mark(c, 7);
 #pragma unroll
     for (int k = 0; k < CPS; ++k) r0 += dot8(w[k], act[k]);
     if (upr == 2) {
-      ring_read<CPS>(ring, w);
+      if (tail) ring_read_tail<CPS, kRing - 2 * CPS>(ring, w);
+      else ring_read<CPS>(ring, w);
 #pragma unroll
       for (int k = 0; k < CPS; ++k) r1 += dot8(w[k], act[k]);
     }
@@ -379,6 +419,7 @@ __device__ __forceinline__ float finish_staging(Cx& c, int n, bool norm, float s
     if (c.lane == 0) c.sm.wsum[c.wave] = p;
   }
   cta_sync(c);
+  ring_flush(*c.ring);
   ts_mark(c, 2);
   mark_ready(c);
   if (!norm) return 1.0f;
@@ -419,39 +460,52 @@ __device__ __forceinline__ void op_qkv(Cx& c, Ring& ring, const Ins& in) {
   for (int i = c.tid; i < 2 * hh; i += kThreads) rope[i] = *gp(kp.rope + (int64_t)c.pos * hh * 2 + i);
   const float ss = stage_layer_input(c, l, in.kpad, g1, OP_QKV);
   const float scale = finish_staging(c, kp.d, true, ss);
+  // Output element `half` (0: row i, 1: row i + hd/2) of global unit g: a
+  // rotary pair of a q head (fp32, one copy, the other epoch re-armed) or a
+  // k head (fp16 into the cache) after RoPE, or a pair of value rows.
+  auto store_out = [&](int g, int half, float v) {
+    if (g < nqh) {
+      const int64_t idx = (int64_t)(g / hh) * kp.hd + g % hh + half * hh;
+      stcf(buf_at(kp.q, c.e, l, 0) + idx, v);
+      if (sentinel_mode(c)) stc32(buf_at(kp.q, c.e1, l, 0) + idx, kSent32);
+    } else {
+      const bool isk = g < nqh + nkh;
+      g -= isk ? nqh : nqh + nkh;
+      const int64_t idx = (((int64_t)l * kp.nkv + g / hh) * kp.max_seq + c.pos) * kp.hd + g % hh + half * hh;
+      stc16((isk ? kp.kc : kp.vc) + idx, __builtin_bit_cast(uint16_t, (_Float16)v));
+    }
+  };
+  // outputs are staged after the RoPE row and written together at the end
+  float* outs = rope + 2 * hh;  // [2][nu]
+  const bool staged = staged_rows(in) && 2 * hh + 2 * in.nu <= kResidRows;
   gemv_dispatch(c, ring, in, c.sm.vec, scale, [&](int u, float a, float b) {
-    int g = in.u0 + u;
+    const int g = in.u0 + u;
     if (g < nqh + nkh) {  // rotary pair (i, i + hd/2) of a q or k head
-      const bool isq = g < nqh;
-      if (!isq) g -= nqh;
-      const int head = g / hh, i = g % hh;
+      const int i = (g < nqh ? g : g - nqh) % hh;
       const float cs = rope[2 * i], sn = rope[2 * i + 1];
       const float ra = a * cs - b * sn, rb = a * sn + b * cs;
-      if (isq) {
-        float* q = buf_at(kp.q, c.e, l, 0) + head * kp.hd + i;
-        float* q1 = buf_at(kp.q, c.e1, l, 0) + head * kp.hd + i;
-        if (c.lane == 0) stcf(q, ra);
-        else if (c.lane == 1) stcf(q + hh, rb);
-        else if (c.lane == 2 && sentinel_mode(c)) stc32(q1, kSent32);
-        else if (c.lane == 3 && sentinel_mode(c)) stc32(q1 + hh, kSent32);
-      } else {
-        uint16_t* k = kp.kc + (((int64_t)l * kp.nkv + head) * kp.max_seq + c.pos) * kp.hd + i;
-        if (c.lane == 0) stc16(k, __builtin_bit_cast(uint16_t, (_Float16)ra));
-        else if (c.lane == 1) stc16(k + hh, __builtin_bit_cast(uint16_t, (_Float16)rb));
+      a = ra;
+      b = rb;
+    }
+    if (staged) {
+      if (c.lane == 0) {
+        outs[u] = a;
+        outs[in.nu + u] = b;
       }
-    } else {  // value rows
-      g -= nqh + nkh;
-      const int head = g / hh, i = g % hh;
-      uint16_t* v = kp.vc + (((int64_t)l * kp.nkv + head) * kp.max_seq + c.pos) * kp.hd + i;
-      if (c.lane == 0) stc16(v, __builtin_bit_cast(uint16_t, (_Float16)a));
-      else if (c.lane == 1) stc16(v + hh, __builtin_bit_cast(uint16_t, (_Float16)b));
+    } else if (c.lane < 2) {
+      store_out(g, c.lane, c.lane == 0 ? a : b);
     }
   });
+  if (staged) {
+    cta_sync(c);
+    for (int t = c.tid; t < 2 * in.nu; t += kThreads) store_out(in.u0 + t % in.nu, t / in.nu, outs[t]);
+  }
   counter_signal(c, in.sync_out);
 }
 
 // Merge the S splits of query head h for output dims [b * kRedDims, +kRedDims):
 // one wavefront, lane s holds split s; publishes o (every replica).
+static_assert(kRedDims * 8 <= 64, "red_unit stores kRedDims dims to up to 8 replicas from one wavefront");
 __device__ __forceinline__ void red_unit(Cx& c, int l, int h, int b) {
   const KParams& kp = *c.kp;
   const int hd = kp.hd, S = kp.S;
@@ -493,10 +547,19 @@ __device__ __forceinline__ void red_unit(Cx& c, int l, int h, int b) {
   const float w = (s < S && ms != -INFINITY) ? exp2f(ms - M) : 0.f;
   const float Lt = wave_sum(w * ls);
   const float inv = 1.0f / Lt;
+  // lane r * kRedDims + d stores dim d to replica r: one contiguous
+  // kRedDims-float write per replica (and one re-arm write per replica)
+  const int rr = c.lane / kRedDims, dl = c.lane % kRedDims;
+  float mine = 0.f;
 #pragma unroll
   for (int d = 0; d < kRedDims; ++d) {
     const float v = wave_sum(w * os[d]) * inv;
-    publish(c, kp.o, l, (int64_t)h * hd + b * kRedDims + d, v);
+    if (dl == d) mine = v;
+  }
+  if (rr < kp.R) {
+    const int64_t idx = (int64_t)h * hd + b * kRedDims + dl;
+    stcf(buf_at(kp.o, c.e, l, rr) + idx, mine);
+    if (sentinel_mode(c)) stc32(buf_at(kp.o, c.e1, l, rr) + idx, kSent32);
   }
 }
 
@@ -826,6 +889,7 @@ __device__ __forceinline__ void op_att(Cx& c, const Ins& in) {
     }
     ts_mark(c, 1);
     cta_sync(c);
+    ring_flush(*c.ring);
     ts_mark(c, 2);
     if (ui == 0) mark_ready(c);
     if (touch == 1.2345e-30f && c.tid == kThreads) c.fail = true;  // keeps the touches; never true
@@ -897,9 +961,16 @@ __device__ __forceinline__ void op_oproj(Cx& c, Ring& ring, const Ins& in) {
   stage_resid(c, l == 0 ? nullptr : buf_at(kp.xm, c.e, l - 1, c.rep), l == 0 ? kp.embed + (int64_t)c.tok * kp.d : nullptr,
               in.u0, in.nu, OP_OPROJ, l);
   finish_staging(c, 0, false, 0.f);
+  const bool staged = staged_rows(in);
   gemv_dispatch(c, ring, in, c.sm.vec, 1.f, [&](int u, float y, float) {
-    publish(c, kp.xa, l, in.u0 + u, c.sm.resid[u] + y);
+    const float v = c.sm.resid[u] + y;
+    if (!staged) publish(c, kp.xa, l, in.u0 + u, v);
+    else if (c.lane == 0) c.sm.resid[u] = v;
   });
+  if (staged) {
+    cta_sync(c);
+    publish_rows(c, kp.xa, c.e, l, in.u0, in.nu, c.sm.resid, true);
+  }
   counter_signal(c, in.sync_out);
 }
 
@@ -911,10 +982,16 @@ __device__ __forceinline__ void op_upgate(Cx& c, Ring& ring, const Ins& in) {
   const uint16_t* g2 = kp.norms + ((int64_t)l * 2 + 1) * kp.d;
   const float ss = stage_vec(c, buf_at(kp.xa, c.e, l, c.rep), c.sm.vec, kp.d, in.kpad, g2, OP_UPGATE, l);
   const float scale = finish_staging(c, kp.d, true, ss);
+  const bool staged = staged_rows(in);
   gemv_dispatch(c, ring, in, c.sm.vec, scale, [&](int u, float gt, float up) {
     const float silu = gt / (1.0f + __expf(-gt));
-    publish(c, kp.m, l, in.u0 + u, silu * up);
+    if (!staged) publish(c, kp.m, l, in.u0 + u, silu * up);
+    else if (c.lane == 0) c.sm.resid[u] = silu * up;
   });
+  if (staged) {
+    cta_sync(c);
+    publish_rows(c, kp.m, c.e, l, in.u0, in.nu, c.sm.resid, true);
+  }
   counter_signal(c, in.sync_out);
 }
 
@@ -926,9 +1003,16 @@ __device__ __forceinline__ void op_down(Cx& c, Ring& ring, const Ins& in) {
   stage_vec(c, buf_at(kp.m, c.e, l, c.rep), c.sm.vec, kp.f, in.kpad, nullptr, OP_DOWN, l);
   stage_resid(c, buf_at(kp.xa, c.e, l, c.rep), nullptr, in.u0, in.nu, OP_DOWN, l);
   finish_staging(c, 0, false, 0.f);
+  const bool staged = staged_rows(in);
   gemv_dispatch(c, ring, in, c.sm.vec, 1.f, [&](int u, float y, float) {
-    publish(c, kp.xm, l, in.u0 + u, c.sm.resid[u] + y);
+    const float v = c.sm.resid[u] + y;
+    if (!staged) publish(c, kp.xm, l, in.u0 + u, v);
+    else if (c.lane == 0) c.sm.resid[u] = v;
   });
+  if (staged) {
+    cta_sync(c);
+    publish_rows(c, kp.xm, c.e, l, in.u0, in.nu, c.sm.resid, true);
+  }
   counter_signal(c, in.sync_out);
 }
 
@@ -1011,6 +1095,7 @@ __device__ __forceinline__ void op_argmax(Cx& c, const Ins& in) {
   }
   if (c.lane == 0) c.sm.keys[c.wave] = k;
   cta_sync(c);
+  ring_flush(*c.ring);
   mark_ready(c);
   // one acquire (cache invalidation) for the workgroup, after every wavefront's polls
   if (c.wave == 0) acquire_polled();
@@ -1036,10 +1121,19 @@ __device__ __forceinline__ void op_chain(Cx& c, Ring& ring, const Ins& in) {
     stage_vec(c, buf_at(kp.y, 0, i - 1, c.rep), c.sm.vec, n, in.kpad, nullptr, OP_CHAIN, i);
   }
   finish_staging(c, 0, false, 0.f);
+  const bool staged = staged_rows(in);
   gemv_dispatch(c, ring, in, c.sm.vec, 1.f, [&](int u, float y, float) {
     const float t = tanhf(y);
-    if (c.lane < kp.R) stcf(buf_at(kp.y, 0, i, c.lane) + in.u0 + u, t);
+    if (!staged) {
+      if (c.lane < kp.R) stcf(buf_at(kp.y, 0, i, c.lane) + in.u0 + u, t);
+    } else if (c.lane == 0) {
+      c.sm.resid[u] = t;
+    }
   });
+  if (staged) {
+    cta_sync(c);
+    publish_rows(c, kp.y, 0, i, in.u0, in.nu, c.sm.resid, false);
+  }
   counter_signal(c, in.sync_out);
 }
 
@@ -1067,7 +1161,7 @@ __global__ __launch_bounds__(kThreads, 1) void mk_monokernel(const KParams* __re
   c.sm.vec = (float*)(smem + kWaves * kRing * 1024);
   c.sm.scratch = c.sm.vec + kp.vec_floats;
   c.sm.resid = c.sm.scratch + kScratchFloats;
-  uint8_t* small = (uint8_t*)(c.sm.resid + 1024);
+  uint8_t* small = (uint8_t*)(c.sm.resid + kResidRows);
   c.sm.flags = (uint32_t*)(small + kOffFlags);
   c.sm.wsum = (float*)(small + kOffWsum);
   c.sm.keys = (uint64_t*)(small + kOffKeys);
@@ -1083,6 +1177,7 @@ __global__ __launch_bounds__(kThreads, 1) void mk_monokernel(const KParams* __re
     ring.slot = 0;
     ring_start(ring);
   }
+  c.ring = &ring;
 
   // drop any line an earlier kernel (e.g. the sentinel fill) left in this XCD's L2
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");

@@ -14,11 +14,15 @@ namespace mk {
 
 constexpr int kWaves = 8;                 // wavefronts per workgroup
 constexpr int kThreads = kWaves * 64;     // 512 threads
-constexpr int kRing = 12;                 // 1 KB weight chunks in flight per wavefront (LDS ring)
+#ifndef MK_RING
+#define MK_RING 12
+#endif
+constexpr int kRing = MK_RING;            // 1 KB weight chunks in flight per wavefront (LDS ring)
 constexpr int kChunkHalfs = 512;          // fp16 values per chunk = 64 lanes x 8
 constexpr int kMaxK = 16384;              // longest GEMV row
 constexpr int kRedDims = 8;               // output dims per attention-reduce unit
 constexpr int kScratchFloats = 4352;      // LDS scratch for cross-wave reductions (17 KB)
+constexpr int kResidRows = 1024;          // LDS rows for residual inputs / staged GEMV outputs
 
 // Small LDS fields after the residual rows (byte offsets within a 1 KB block).
 constexpr int kSmallBytes = 1024;

@@ -19,7 +19,7 @@ namespace mk {
 // rings | staged vector | scratch | residual rows | small fields (flags,
 // wave sums, argmax keys, trace scratch, barrier, ring tags and counts).
 int lds_bytes_for(int kpad_max) {
-  return kWaves * kRing * 1024 + kpad_max * 4 + kScratchFloats * 4 + 1024 * 4 + kSmallBytes;
+  return kWaves * kRing * 1024 + kpad_max * 4 + kScratchFloats * 4 + kResidRows * 4 + kSmallBytes;
 }
 
 int choose_splits(int n_cta, int nkv, int max_seq) {
@@ -309,7 +309,7 @@ std::string check_plan(const Plan& p) {
         if (in.cps < 1 || in.cps > 4) return "chunks per slice must be in [1, 4]";
         if (in.kpad > kMaxK) return "row too long";
         if (in.ks > 1 && in.nu * in.upr * in.ks > kScratchFloats) return "K-slice partials do not fit the LDS scratch";
-        if ((in.op == OP_OPROJ || in.op == OP_DOWN) && in.nu > 1024) return "residual rows do not fit the LDS";
+        if ((in.op == OP_OPROJ || in.op == OP_DOWN) && in.nu > kResidRows) return "residual rows do not fit the LDS";
       }
       if (in.op == OP_LMHEAD && (in.slot < 0 || in.slot >= p.lm_slots)) return "bad argmax slot";
     }
