@@ -138,7 +138,6 @@ struct Ring {
   uint32_t n;            // chunks per step
   uint32_t issue;        // next chunk (mod n) to request
   uint32_t slot;         // ring slot holding the next chunk to consume
-  uint32_t deferred;     // slots read but not yet refilled (the refill waits for ring_flush)
 };
 
 // The ring is touched only through inline asm (the DMA that fills a slot and
@@ -169,7 +168,6 @@ __device__ __forceinline__ void ring_start(Ring& r) {
     r.issue = (r.issue + 1 == r.n) ? 0 : r.issue + 1;
   }
   r.slot = 0;
-  r.deferred = 0;
 }
 
 // Read N ring chunks (N <= 4) at LDS addresses a[] after waiting for
@@ -216,36 +214,6 @@ __device__ __forceinline__ void ring_read(Ring& r, u4 (&v)[4]) {
   }
 }
 
-// Next N chunks without refilling their slots: W must be kRing - N -
-// r.deferred, the vmcnt that leaves the N oldest outstanding DMAs landed.
-// The refills are issued later by ring_flush, so loads issued in between
-// (the next instruction's input polls) do not return behind them.
-template <int N, int W>
-__device__ __forceinline__ void ring_read_tail(Ring& r, u4 (&v)[4]) {
-  static_assert(N >= 1 && N <= 4 && W >= 0, "ring_read_tail reads 1..4 chunks");
-  uint32_t a[4];
-  uint32_t slot = r.slot;
-#pragma unroll
-  for (int k = 0; k < N; ++k) {
-    a[k] = r.lds + slot * 1024 + lane_id() * 16;
-    slot = (slot + 1 == kRing) ? 0 : slot + 1;
-  }
-  ring_load<N, W>(a, v);
-  r.slot = slot;
-  r.deferred += N;
-}
-
-// Issue the refills that ring_read_tail held back, in slot order.
-__device__ __forceinline__ void ring_flush(Ring& r) {
-  const uint32_t lane16 = lane_id() * 16;
-  uint32_t s = (r.slot + kRing - r.deferred) % kRing;
-  for (uint32_t k = 0; k < r.deferred; ++k) {
-    dma_chunk(r.lds + s * 1024, r.g, r.issue * 1024 + lane16);
-    r.issue = (r.issue + 1 == r.n) ? 0 : r.issue + 1;
-    s = (s + 1 == kRing) ? 0 : s + 1;
-  }
-  r.deferred = 0;
-}
 
 __device__ __forceinline__ float dot8(u4 w, const float* a) {
   const h8 h = __builtin_bit_cast(h8, w);

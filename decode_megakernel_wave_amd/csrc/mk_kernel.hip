@@ -57,7 +57,6 @@ struct Smem {
 struct Cx {
   const KParams* kp;
   Smem sm;
-  Ring* ring;
   int cta, wave, lane, tid, rep, xcc;
   int step, pos, e, e1, tok, pc;
   int flag_parity;
@@ -133,9 +132,20 @@ __device__ __forceinline__ bool cta_failed(Cx& c) {
 }
 
 // Diagnostics: fine timestamp k of the current instruction (step 0, thread 0).
+// With MK_TSW the record instead holds, per wavefront w, the time its GEMV
+// rows were done (slot w).
 __device__ __forceinline__ void ts_mark(const Cx& c, int k) {
+#ifndef MK_TSW
   if (c.kp->ts && c.step == 0 && c.tid == 0)
     *gp(c.kp->ts + ((int64_t)c.cta * c.kp->max_ins + c.pc) * 8 + k) = __builtin_amdgcn_s_memrealtime();
+#endif
+}
+
+__device__ __forceinline__ void ts_wave_done(const Cx& c) {
+#ifdef MK_TSW
+  if (c.kp->ts && c.step == 0 && c.lane == 0)
+    *gp(c.kp->ts + ((int64_t)c.cta * c.kp->max_ins + c.pc) * 8 + c.wave) = __builtin_amdgcn_s_memrealtime();
+#endif
 }
 
 // Trace: time at which an instruction's inputs were staged.
@@ -345,21 +355,12 @@ __device__ __forceinline__ void gemv(Cx& c, Ring& ring, const Ins& in, const flo
   for (int u = gi; u < in.nu; u += rg) {
     float r0 = 0.f, r1 = 0.f;
     u4 w[4];
-#ifdef MK_DEFER
-    // the wavefront's last unit: hold its refills back until the next
-    // instruction's inputs have been polled
-    const bool tail = u + rg >= in.nu;
-#else
-    constexpr bool tail = false;
-#endif
-    if (tail) ring_read_tail<CPS, kRing - CPS>(ring, w);
-    else ring_read<CPS>(ring, w);
+    ring_read<CPS>(ring, w);
     if (u == gi) ts_mark(c, 7);
 #pragma unroll
     for (int k = 0; k < CPS; ++k) r0 += dot8(w[k], act[k]);
     if (upr == 2) {
-      if (tail) ring_read_tail<CPS, kRing - 2 * CPS>(ring, w);
-      else ring_read<CPS>(ring, w);
+      ring_read<CPS>(ring, w);
 #pragma unroll
       for (int k = 0; k < CPS; ++k) r1 += dot8(w[k], act[k]);
     }
@@ -373,6 +374,7 @@ __device__ __forceinline__ void gemv(Cx& c, Ring& ring, const Ins& in, const flo
     }
   }
   ts_mark(c, 6);
+  ts_wave_done(c);
   if (ks > 1) {
     cta_sync(c);
     if (ki == 0) {
@@ -419,7 +421,6 @@ __device__ __forceinline__ float finish_staging(Cx& c, int n, bool norm, float s
     if (c.lane == 0) c.sm.wsum[c.wave] = p;
   }
   cta_sync(c);
-  ring_flush(*c.ring);
   ts_mark(c, 2);
   mark_ready(c);
   if (!norm) return 1.0f;
@@ -889,8 +890,7 @@ __device__ __forceinline__ void op_att(Cx& c, const Ins& in) {
     }
     ts_mark(c, 1);
     cta_sync(c);
-    ring_flush(*c.ring);
-    ts_mark(c, 2);
+      ts_mark(c, 2);
     if (ui == 0) mark_ready(c);
     if (touch == 1.2345e-30f && c.tid == kThreads) c.fail = true;  // keeps the touches; never true
     if (t1 - t0 <= 4 * kWaves) {
@@ -1095,7 +1095,6 @@ __device__ __forceinline__ void op_argmax(Cx& c, const Ins& in) {
   }
   if (c.lane == 0) c.sm.keys[c.wave] = k;
   cta_sync(c);
-  ring_flush(*c.ring);
   mark_ready(c);
   // one acquire (cache invalidation) for the workgroup, after every wavefront's polls
   if (c.wave == 0) acquire_polled();
@@ -1177,7 +1176,6 @@ __global__ __launch_bounds__(kThreads, 1) void mk_monokernel(const KParams* __re
     ring.slot = 0;
     ring_start(ring);
   }
-  c.ring = &ring;
 
   // drop any line an earlier kernel (e.g. the sentinel fill) left in this XCD's L2
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
