@@ -12,7 +12,10 @@
 
 namespace mk {
 
-constexpr int kWaves = 8;                 // wavefronts per workgroup
+#ifndef MK_WAVES
+#define MK_WAVES 8
+#endif
+constexpr int kWaves = MK_WAVES;          // wavefronts per workgroup
 constexpr int kThreads = kWaves * 64;     // 512 threads
 #ifndef MK_RING
 #define MK_RING 12

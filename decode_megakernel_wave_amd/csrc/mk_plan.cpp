@@ -106,8 +106,10 @@ void row_source(const Plan& p, const Stage& st, int g, int r, int* mat, int* row
 // two ks (dividing the wavefront count) that minimises the busiest
 // wavefront's chunk count, with at most 4 chunks per slice (the activation
 // slice lives in registers).  Rows are zero-padded to a multiple of ks chunks.
+// ks = 0 when no split fits (rows too long for the registers and too many
+// rows for the merge scratch).
 void choose_split(int nu, int upr, int kc_raw, int* ks_out, int* cps_out) {
-  int best = -1, best_ks = 8, best_cps = 1;
+  int best = -1, best_ks = 0, best_cps = 1;
   for (int ks = 1; ks <= kWaves; ks *= 2) {
     const int kc = (kc_raw + ks - 1) / ks * ks, cps = kc / ks;
     if (cps > 4) continue;
@@ -239,6 +241,7 @@ std::string build_plan(const Dims& dm, int n_cta, int S, int R, int sync_mode, P
       if (is_gemv(st.op)) {
         int ks, cps;
         choose_split(std::max(nu, 1), st.upr, (st.K + kChunkHalfs - 1) / kChunkHalfs, &ks, &cps);
+        if (ks == 0) return "no K split fits: too many GEMV rows per workgroup for this row length (use a larger grid)";
         in.upr = (uint8_t)st.upr;
         in.ks = (uint8_t)ks;
         in.cps = (uint8_t)cps;

@@ -156,7 +156,8 @@ def _cfg(**kw):
     (_cfg(vocab=1), 64, 64, {}, "positive"),
     (_cfg(), 1, 64, {}, "positive"),
     (_cfg(), 64, 0, {}, "at least one workgroup"),
-    (inputs.M2B, 1025, 1, {}, "residual rows"),
+    (_cfg(d_model=2048, ffn=512), 64, 1, {}, "residual rows"),
+    (inputs.M2B, 1025, 1, {}, "no K split fits"),
 ])
 def test_plan_rejects(model, max_seq, grid, opts, reason):
     with pytest.raises(mk.MkError) as e:
