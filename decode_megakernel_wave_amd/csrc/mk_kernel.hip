@@ -577,19 +577,19 @@ __device__ __forceinline__ void red_unit(Cx& c, int l, int h, int b) {
 // keeps its own online-softmax state (m, l, o) for its slot, the slots are
 // merged with cross-lane shuffles, then the wavefronts through the scratch.
 
-// Short splits: query heads [j0, j0 + ng) of the group (ng <= GP) over the
-// positions [t0, t1), one position per wavefront at a time: each wavefront takes t0 + wave, t0 + wave + kWaves, ... in
-// batches of kBatch whose K/V loads are all issued before any score is
-// computed; lane i holds dims [i*DPL, i*DPL + DPL).  GP * DPL <= 8 keeps the
-// accumulators in 8 registers per lane whatever the head geometry.
+// Short splits (at most kPosBatch positions per wavefront): query heads
+// [j0, j0 + ng) of the group (ng <= GP) over the positions [t0, t1); wavefront
+// w holds positions t0 + w + b * kWaves (b < kPosBatch) in kv / vv, lane i
+// dims [i*DPL, i*DPL + DPL).  GP * DPL <= 8 keeps the accumulators in 8
+// registers per lane whatever the head geometry.
+constexpr int kPosBatch = 4;
+
 template <int GP, int DPL>
-__device__ __forceinline__ void att_pass_pos(Cx& c, int l, int g, int sp, int j0, int ng, int t0, int t1, int G) {
+__device__ __forceinline__ void att_pos_core(Cx& c, int l, int g, int sp, int j0, int ng, int t0, int t1, int G,
+                                             const float (&kv)[kPosBatch][DPL], const float (&vv)[kPosBatch][DPL]) {
   const KParams& kp = *c.kp;
   const int hd = kp.hd, S = kp.S;
-  constexpr int kBatch = 4;
-  const float* qs = c.sm.vec;            // [G][hd]
-  const float* kcur = c.sm.vec + G * hd; // [hd]
-  const float* vcur = kcur + hd;         // [hd]
+  const float* qs = c.sm.vec;  // [G][hd]
   float m[GP], lsum[GP], o[GP][DPL];
 #pragma unroll
   for (int j = 0; j < GP; ++j) {
@@ -598,33 +598,10 @@ __device__ __forceinline__ void att_pass_pos(Cx& c, int l, int g, int sp, int j0
 #pragma unroll
     for (int k = 0; k < DPL; ++k) o[j][k] = 0.f;
   }
-  const int64_t head_off = ((int64_t)l * kp.nkv + g) * kp.max_seq * hd + c.lane * DPL;
-  const uint16_t* kbase = kp.kc + head_off;
-  const uint16_t* vbase = kp.vc + head_off;
-  for (int tb = t0 + c.wave; tb < t1; tb += kWaves * kBatch) {
-    float kv[kBatch][DPL], vv[kBatch][DPL];
+  {
+    const int tb = t0 + c.wave;
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int t = tb + b * kWaves;
-      if (t >= t1) break;
-      if (t == c.pos) {
-#pragma unroll
-        for (int k = 0; k < DPL; ++k) {
-          kv[b][k] = kcur[c.lane * DPL + k];
-          vv[b][k] = vcur[c.lane * DPL + k];
-        }
-      } else {
-        const uint16_t* kr = kbase + (int64_t)t * hd;
-        const uint16_t* vr = vbase + (int64_t)t * hd;
-#pragma unroll
-        for (int k = 0; k < DPL; ++k) {
-          kv[b][k] = (float)__builtin_bit_cast(_Float16, *gp(kr + k));
-          vv[b][k] = (float)__builtin_bit_cast(_Float16, *gp(vr + k));
-        }
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
+    for (int b = 0; b < kPosBatch; ++b) {
       const int t = tb + b * kWaves;
       if (t >= t1) break;
 #pragma unroll
@@ -843,71 +820,129 @@ __device__ __forceinline__ void att_heads(Cx& c, int l, int g, int sp, int t0, i
   }
 }
 
+// Stage q of kv head g's query group (times log2(e)/sqrt(hd)) and, for the
+// split holding the current position, that position's K/V rows (polled: the
+// QKV stage writes them) into LDS; ends with a workgroup barrier.
+__device__ __forceinline__ void att_stage(Cx& c, int l, int g, bool has_cur, bool first) {
+  const KParams& kp = *c.kp;
+  const int G = kp.nq / kp.nkv, hd = kp.hd;
+  const float qscale = kLog2e / __builtin_sqrtf((float)hd);
+  float* qs = c.sm.vec;              // [G][hd]
+  float* kcur = c.sm.vec + G * hd;   // [hd]
+  float* vcur = kcur + hd;           // [hd]
+  const float* qsrc = buf_at(kp.q, c.e, l, 0) + g * G * hd;
+  for (int i = c.tid; i < G * hd; i += kThreads) qs[i] = poll_f32(c, qsrc + i, OP_ATT, l) * qscale;
+  if (has_cur && c.tid < 2 * hd) {
+    const int i = c.tid % hd;
+    const uint16_t* src = (c.tid < hd ? kp.kc : kp.vc) + (((int64_t)l * kp.nkv + g) * kp.max_seq + c.pos) * hd + i;
+    uint16_t v = ldc16(src);
+    if (sentinel_mode(c)) {
+      while (v == kSent16 && !c.fail) {
+        if (expired(c, OP_ATT, l, i)) {
+          c.fail = true;
+          break;
+        }
+        v = ldc16(src);
+      }
+    }
+    (c.tid < hd ? kcur : vcur)[i] = (float)__builtin_bit_cast(_Float16, v);
+  }
+  ts_mark(c, 1);
+  cta_sync(c);
+  ts_mark(c, 2);
+  if (first) mark_ready(c);
+}
+
+// DPL fp16 values of one cached K or V row slice, kept as loaded (the
+// conversion waits for the load, so it happens after q has been staged).
+template <int DPL> struct RawHalves { typedef uint32_t T; };
+template <> struct RawHalves<4> { typedef u2 T; };
+
+template <int DPL>
+__device__ __forceinline__ typename RawHalves<DPL>::T load_halves(const uint16_t* p) {
+  if constexpr (DPL == 1) return (uint32_t)*gp(p);
+  else if constexpr (DPL == 2) return *gp((const uint32_t*)p);
+  else return *gp((const u2*)p);
+}
+
+template <int DPL>
+__device__ __forceinline__ float half_at(const typename RawHalves<DPL>::T& r, int k) {
+  uint32_t w;
+  if constexpr (DPL == 4) w = r[k >> 1];
+  else w = r;
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> (16 * (k & 1))));
+}
+
+// Short split: this wavefront's cached K/V rows are loaded before q is
+// polled, so their latency hides behind the wait for the QKV stage.
+template <int GP, int DPL>
+__device__ __forceinline__ void att_short(Cx& c, int l, int g, int sp, int t0, int t1, int G, bool has_cur, bool first) {
+  const KParams& kp = *c.kp;
+  const int hd = kp.hd;
+  typedef typename RawHalves<DPL>::T Raw;
+  Raw kr[kPosBatch], vr[kPosBatch];
+  const int64_t head_off = ((int64_t)l * kp.nkv + g) * kp.max_seq * hd + c.lane * DPL;
+#pragma unroll
+  for (int b = 0; b < kPosBatch; ++b) {
+    const int t = t0 + c.wave + b * kWaves;
+    kr[b] = Raw{};
+    vr[b] = Raw{};
+    if (t < t1 && t != c.pos) {
+      kr[b] = load_halves<DPL>(kp.kc + head_off + (int64_t)t * hd);
+      vr[b] = load_halves<DPL>(kp.vc + head_off + (int64_t)t * hd);
+    }
+  }
+  att_stage(c, l, g, has_cur, first);
+  const float* kcur = c.sm.vec + G * hd;
+  const float* vcur = kcur + hd;
+  float kv[kPosBatch][DPL], vv[kPosBatch][DPL];
+#pragma unroll
+  for (int b = 0; b < kPosBatch; ++b) {
+    const bool cur = t0 + c.wave + b * kWaves == c.pos;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) {
+      kv[b][k] = cur ? kcur[c.lane * DPL + k] : half_at<DPL>(kr[b], k);
+      vv[b][k] = cur ? vcur[c.lane * DPL + k] : half_at<DPL>(vr[b], k);
+    }
+  }
+  for (int j0 = 0; j0 < G; j0 += GP) att_pos_core<GP, DPL>(c, l, g, sp, j0, min(GP, G - j0), t0, t1, G, kv, vv);
+}
+
 __device__ __forceinline__ void op_att(Cx& c, const Ins& in) {
   const KParams& kp = *c.kp;
   const int l = in.layer;
   const int G = kp.nq / kp.nkv, hd = kp.hd, S = kp.S;
   const int T = c.pos + 1;
   const int chunk = (T + S - 1) / S;
-  const float qscale = kLog2e / __builtin_sqrtf((float)hd);
   counter_wait(c, in.sync_in, in.n_in, OP_ATT, l);
   if (!sentinel_mode(c)) cta_sync(c);
-  float* qs = c.sm.vec;              // [G][hd]
-  float* kcur = c.sm.vec + G * hd;   // [hd]
-  float* vcur = kcur + hd;           // [hd]
   for (int ui = 0; ui < in.nu; ++ui) {
     const int U = in.u0 + ui, g = U / S, sp = U % S;
     const int t0 = sp * chunk, t1 = min(T, t0 + chunk);
     const bool has_cur = t0 <= c.pos && c.pos < t1;
-    // pull this split's cached K/V rows towards the CU before waiting for q:
-    // each thread touches one 4-byte word per 64 bytes of the rows it will read
-    float touch = 0.f;
-    {
-      const int64_t hoff = ((int64_t)l * kp.nkv + g) * kp.max_seq * hd;
-      const int words = (t1 - t0) * hd / 16;  // one per 64 bytes (32 halves) of K and of V
-      for (int i = c.tid; i < words; i += kThreads) {
-        const int64_t e = (int64_t)t0 * hd + (int64_t)(i >> 1) * 32;  // element offset in the head's rows
-        if (e / hd != c.pos) touch += __uint_as_float(*gp((const uint32_t*)(((i & 1) ? kp.vc : kp.kc) + hoff + e)));
-      }
-    }
-    // stage q of the group and, for the split holding the current position, its K/V
-    const float* qsrc = buf_at(kp.q, c.e, l, 0) + g * G * hd;
-    for (int i = c.tid; i < G * hd; i += kThreads) qs[i] = poll_f32(c, qsrc + i, OP_ATT, l) * qscale;
-    if (has_cur && c.tid < 2 * hd) {
-      const int i = c.tid % hd;
-      const uint16_t* src = (c.tid < hd ? kp.kc : kp.vc) + (((int64_t)l * kp.nkv + g) * kp.max_seq + c.pos) * hd + i;
-      uint16_t v = ldc16(src);
-      if (sentinel_mode(c)) {
-        while (v == kSent16 && !c.fail) {
-          if (expired(c, OP_ATT, l, i)) {
-            c.fail = true;
-            break;
-          }
-          v = ldc16(src);
+    if (t1 - t0 <= kPosBatch * kWaves) {
+      // short split (a few positions per wavefront): one position per wavefront per step
+      const int dpl = hd / 64;
+      if (dpl == 1) att_short<8, 1>(c, l, g, sp, t0, t1, G, has_cur, ui == 0);
+      else if (dpl == 2) att_short<4, 2>(c, l, g, sp, t0, t1, G, has_cur, ui == 0);
+      else att_short<2, 4>(c, l, g, sp, t0, t1, G, has_cur, ui == 0);
+    } else {
+      // pull this split's cached K/V rows towards the CU before waiting for q:
+      // each thread touches one 4-byte word per 64 bytes of the rows it will read
+      float touch = 0.f;
+      {
+        const int64_t hoff = ((int64_t)l * kp.nkv + g) * kp.max_seq * hd;
+        const int words = (t1 - t0) * hd / 16;  // one per 64 bytes (32 halves) of K and of V
+        for (int i = c.tid; i < words; i += kThreads) {
+          const int64_t e = (int64_t)t0 * hd + (int64_t)(i >> 1) * 32;  // element offset in the head's rows
+          if (e / hd != c.pos) touch += __uint_as_float(*gp((const uint32_t*)(((i & 1) ? kp.vc : kp.kc) + hoff + e)));
         }
       }
-      (c.tid < hd ? kcur : vcur)[i] = (float)__builtin_bit_cast(_Float16, v);
-    }
-    ts_mark(c, 1);
-    cta_sync(c);
-      ts_mark(c, 2);
-    if (ui == 0) mark_ready(c);
-    if (touch == 1.2345e-30f && c.tid == kThreads) c.fail = true;  // keeps the touches; never true
-    if (t1 - t0 <= 4 * kWaves) {
-      // short split (a few positions per wavefront): one position per wavefront per step
-      const int dpl = hd / 64, gp_max = 8 / dpl;
-      for (int j0 = 0; j0 < G; j0 += gp_max) {
-        const int ng = min(gp_max, G - j0);
-        if (dpl == 1) att_pass_pos<8, 1>(c, l, g, sp, j0, ng, t0, t1, G);
-        else if (dpl == 2) att_pass_pos<4, 2>(c, l, g, sp, j0, ng, t0, t1, G);
-        else att_pass_pos<2, 4>(c, l, g, sp, j0, ng, t0, t1, G);
-      }
-    } else if (hd == 64) {
-      att_heads<64>(c, l, g, sp, t0, t1, G);
-    } else if (hd == 128) {
-      att_heads<128>(c, l, g, sp, t0, t1, G);
-    } else {
-      att_heads<256>(c, l, g, sp, t0, t1, G);
+      att_stage(c, l, g, has_cur, ui == 0);
+      if (touch == 1.2345e-30f && c.tid == kThreads) c.fail = true;  // keeps the touches; never true
+      if (hd == 64) att_heads<64>(c, l, g, sp, t0, t1, G);
+      else if (hd == 128) att_heads<128>(c, l, g, sp, t0, t1, G);
+      else att_heads<256>(c, l, g, sp, t0, t1, G);
     }
     ts_mark(c, 6);
     if (!sentinel_mode(c)) {
