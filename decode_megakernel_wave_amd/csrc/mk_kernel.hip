@@ -437,12 +437,29 @@ __device__ __forceinline__ float stage_layer_input(Cx& c, int l, int npad, const
   return stage_vec(c, buf_at(kp.xm, c.e, l - 1, c.rep), c.sm.vec, kp.d, npad, gain, op, l);
 }
 
-// Residual rows [u0, u0+nu) of x_l (embedding for layer 0) into sm.resid.
-__device__ __forceinline__ void stage_resid(Cx& c, const float* src, const uint16_t* emb, int u0, int nu, int op, int layer) {
+// Residual rows [u0, u0+nu) of x_l (embedding for layer 0) into sm.resid, in
+// two halves around the staging of the instruction's main input: the rows
+// were published a stage or more earlier, so resid_issue loads this thread's
+// first row before the main input is polled (its value is then back when the
+// polls are), and resid_finish stores it, re-polling only if it was still
+// the sentinel, plus any rows beyond the first kThreads.
+__device__ __forceinline__ uint32_t resid_issue(Cx& c, const float* src, const uint16_t* emb, int u0, int nu) {
+  if (c.tid >= nu) return 0u;
+  if (emb) return (uint32_t)*gp(emb + u0 + c.tid);
+  return ldc32(src + u0 + c.tid);
+}
+
+__device__ __forceinline__ void resid_finish(Cx& c, uint32_t first, const float* src, const uint16_t* emb, int u0, int nu, int op,
+                                             int layer) {
   for (int i = c.tid; i < nu; i += kThreads) {
     float v;
-    if (emb) v = (float)__builtin_bit_cast(_Float16, *gp(emb + u0 + i));
-    else v = poll_f32(c, src + u0 + i, op, layer);
+    if (emb) {
+      v = (float)__builtin_bit_cast(_Float16, (uint16_t)(i == c.tid ? first : (uint32_t)*gp(emb + u0 + i)));
+    } else if (i == c.tid && (!sentinel_mode(c) || first != kSent32)) {
+      v = __uint_as_float(first);
+    } else {
+      v = poll_f32(c, src + u0 + i, op, layer);
+    }
     c.sm.resid[i] = v;
   }
 }
@@ -992,9 +1009,11 @@ __device__ __forceinline__ void op_oproj(Cx& c, Ring& ring, const Ins& in) {
   const int l = in.layer;
   counter_wait(c, in.sync_in, in.n_in, OP_OPROJ, l);
   if (!sentinel_mode(c)) cta_sync(c);
+  const float* rsrc = l == 0 ? nullptr : buf_at(kp.xm, c.e, l - 1, c.rep);
+  const uint16_t* remb = l == 0 ? kp.embed + (int64_t)c.tok * kp.d : nullptr;
+  const uint32_t r0 = resid_issue(c, rsrc, remb, in.u0, in.nu);
   stage_vec(c, buf_at(kp.o, c.e, l, c.rep), c.sm.vec, kp.nq * kp.hd, in.kpad, nullptr, OP_OPROJ, l);
-  stage_resid(c, l == 0 ? nullptr : buf_at(kp.xm, c.e, l - 1, c.rep), l == 0 ? kp.embed + (int64_t)c.tok * kp.d : nullptr,
-              in.u0, in.nu, OP_OPROJ, l);
+  resid_finish(c, r0, rsrc, remb, in.u0, in.nu, OP_OPROJ, l);
   finish_staging(c, 0, false, 0.f);
   const bool staged = staged_rows(in);
   gemv_dispatch(c, ring, in, c.sm.vec, 1.f, [&](int u, float y, float) {
@@ -1035,8 +1054,10 @@ __device__ __forceinline__ void op_down(Cx& c, Ring& ring, const Ins& in) {
   const int l = in.layer;
   counter_wait(c, in.sync_in, in.n_in, OP_DOWN, l);
   if (!sentinel_mode(c)) cta_sync(c);
+  const float* rsrc = buf_at(kp.xa, c.e, l, c.rep);
+  const uint32_t r0 = resid_issue(c, rsrc, nullptr, in.u0, in.nu);
   stage_vec(c, buf_at(kp.m, c.e, l, c.rep), c.sm.vec, kp.f, in.kpad, nullptr, OP_DOWN, l);
-  stage_resid(c, buf_at(kp.xa, c.e, l, c.rep), nullptr, in.u0, in.nu, OP_DOWN, l);
+  resid_finish(c, r0, rsrc, nullptr, in.u0, in.nu, OP_DOWN, l);
   finish_staging(c, 0, false, 0.f);
   const bool staged = staged_rows(in);
   gemv_dispatch(c, ring, in, c.sm.vec, 1.f, [&](int u, float y, float) {
