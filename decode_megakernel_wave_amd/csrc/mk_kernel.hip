@@ -944,19 +944,9 @@ __device__ __forceinline__ void op_att(Cx& c, const Ins& in) {
       else if (dpl == 2) att_short<4, 2>(c, l, g, sp, t0, t1, G, has_cur, ui == 0);
       else att_short<2, 4>(c, l, g, sp, t0, t1, G, has_cur, ui == 0);
     } else {
-      // pull this split's cached K/V rows towards the CU before waiting for q:
-      // each thread touches one 4-byte word per 64 bytes of the rows it will read
-      float touch = 0.f;
-      {
-        const int64_t hoff = ((int64_t)l * kp.nkv + g) * kp.max_seq * hd;
-        const int words = (t1 - t0) * hd / 16;  // one per 64 bytes (32 halves) of K and of V
-        for (int i = c.tid; i < words; i += kThreads) {
-          const int64_t e = (int64_t)t0 * hd + (int64_t)(i >> 1) * 32;  // element offset in the head's rows
-          if (e / hd != c.pos) touch += __uint_as_float(*gp((const uint32_t*)(((i & 1) ? kp.vc : kp.kc) + hoff + e)));
-        }
-      }
+      // (no prefetch of the split's K/V rows before the wait: pulling them
+      // towards L2 first was measured slower at 2048 and 8192 positions)
       att_stage(c, l, g, has_cur, ui == 0);
-      if (touch == 1.2345e-30f && c.tid == kThreads) c.fail = true;  // keeps the touches; never true
       if (hd == 64) att_heads<64>(c, l, g, sp, t0, t1, G);
       else if (hd == 128) att_heads<128>(c, l, g, sp, t0, t1, G);
       else att_heads<256>(c, l, g, sp, t0, t1, G);
