@@ -89,16 +89,102 @@ def measured_traffic(workload: str, n: int, launch: dict):
     return rec
 
 
+def traced_decode(model, w, ids, P: int, n: int, opts, trace_steps: int) -> dict:
+    """One extra launch (not timed) with the time journal on for its first steps: handoff latency per op."""
+    import torch
+    import decode_megakernel_wave_amd as mk
+    from decode_megakernel_wave_amd import synclat
+
+    opts.trace_steps = trace_steps
+    ctx = mk.mk_create(model, max_seq=P + n + 1, opts=opts)
+    try:
+        wd = mk.to_device(w)
+        mk.mk_load_weights(ctx, wd)
+        del wd
+        torch.cuda.empty_cache()
+        mk.mk_prefill(ctx, ids)
+        mk.mk_decode(ctx, min(n, max(trace_steps, 8)))
+        rec = mk.mk_read_trace(ctx)
+    finally:
+        mk.mk_destroy(ctx)
+    res = synclat.handoffs(rec)
+    log(f"[bench] handoff latency over {trace_steps} traced steps (us): "
+        + ", ".join(f"{k} {v['median_us']:.2f}/{v['p99_us']:.2f}" for k, v in res.items() if v["median_us"] is not None))
+    return {"traced_steps": trace_steps, "definition": "last producer's publish -> a waiting consumer's inputs "
+            "staged, device wall clock (10 ns ticks); median / p99 over (stage, consumer) pairs; critical = last "
+            "consumer ready - last producer done, per stage", "per_op": res}
+
+
+def chain_bench(args) -> int:
+    """GEMV-tanh chain y_i = tanh(W_i y_{i-1}), 256 dependent stages in one persistent launch, run with
+    NaN-sentinel and with atomic-counter inter-stage sync: microseconds per stage, GB/s, handoff latency."""
+    import numpy as np
+    import torch
+    import decode_megakernel_wave_amd as mk
+    from decode_megakernel_wave_amd import inputs, synclat
+
+    n = 2048 if args.workload == "chain" else 256
+    stages = 256
+    W = inputs.make_chain_weights(n=n, stages=stages)
+    x0 = inputs.make_chain_x0(n)
+    Wd = torch.from_numpy(W).cuda()
+    xd = torch.from_numpy(x0).cuda()
+    y = torch.empty((stages, n), dtype=torch.float32, device="cuda")
+    results, outs = {}, {}
+    for name, mode in (("sentinel", mk.MK_SYNC_SENTINEL), ("counter", mk.MK_SYNC_COUNTER)):
+        ch = mk.mk_chain_create(n, stages, Wd, mk.mk_default_options(sync_mode=mode, xcd_replicas=args.replicas))
+        try:
+            for _ in range(args.warmup):
+                mk.mk_chain_run(ch, xd, y)
+            ms = []
+            for _ in range(args.steps):
+                mk.mk_chain_run(ch, xd, y)
+                ms.append(mk.mk_chain_stats(ch)["gpu_ms"])
+            st = mk.mk_chain_stats(ch)
+            outs[name] = y.cpu().numpy().copy()
+        finally:
+            mk.mk_chain_destroy(ch)
+        ch = mk.mk_chain_create(n, stages, Wd, mk.mk_default_options(sync_mode=mode, xcd_replicas=args.replicas,
+                                                                      trace_steps=1))
+        try:
+            mk.mk_chain_run(ch, xd, y)
+            lat = synclat.handoffs(mk.mk_chain_read_trace(ch)).get("chain")
+        finally:
+            mk.mk_chain_destroy(ch)
+        mean_ms = float(np.mean(ms))
+        results[name] = {"us_per_stage": mean_ms * 1e3 / stages, "launch_ms": mean_ms,
+                         "GB_per_s": st["weight_bytes"] / (mean_ms * 1e-3) / 1e9, "handoff_latency": lat}
+        log(f"[bench] chain {n}x{n} {name}: {results[name]['us_per_stage']:.3f} us/stage, "
+            f"{results[name]['GB_per_s']:.0f} GB/s, handoff median {lat['median_us']:.2f} us")
+    same = bool(np.array_equal(outs["sentinel"].view(np.uint32), outs["counter"].view(np.uint32)))
+    stream_us = stages * n * n * 2 / (HBM_PEAK_GBS * 1e3) / stages
+    out = {"metric": f"GEMV-tanh chain, {stages} dependent stages of {n}x{n} fp16 in one launch: us per stage",
+           "value": results["sentinel"]["us_per_stage"], "unit": "us/stage", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": False, "vs_baseline": None, "dtype": "f16 weights, f32 accumulate",
+           "data": "synthetic: W_i ~ N(0,0.02^2) fp16, x0 ~ N(0,1) fp32",
+           "config": {"workload": f"chain {stages} x {n}x{n}", "xcd_replicas": args.replicas},
+           "sentinel": results["sentinel"], "counter": results["counter"],
+           "counter_over_sentinel": results["counter"]["us_per_stage"] / results["sentinel"]["us_per_stage"],
+           "bitwise_equal_modes": same, "streaming_floor_us_per_stage": stream_us}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", default="2b", choices=["2b", "2b-long", "0.5b", "tiny"])
+    ap.add_argument("--workload", default="2b", choices=["2b", "2b-long", "0.5b", "tiny", "chain", "chain-s"],
+                    help="decoder workloads, or the GEMV-tanh chain microbenchmark (chain: 256 stages of "
+                         "2048x2048; chain-s: 256 stages of 256x256, cache-resident, to isolate sync latency)")
     ap.add_argument("--decode-steps", type=int, default=0, help="tokens per launch (default: the workload's)")
     ap.add_argument("--sync", default="sentinel", choices=["sentinel", "counter"])
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--trace-steps", type=int, default=0,
+                    help="after the timed launches, run one more launch that records the per-instruction time "
+                         "journal of its first N steps and report the inter-stage handoff latency")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (torch) and exit: the reference "
                          "kernel for scaling the HBM byte counters")
@@ -124,6 +210,9 @@ def main() -> int:
 
     import decode_megakernel_wave_amd as mk
     from decode_megakernel_wave_amd import inputs
+
+    if args.workload.startswith("chain"):
+        return chain_bench(args)
 
     wl = inputs.WORKLOADS[args.workload]
     model, P = wl.model, wl.prompt_len
@@ -167,6 +256,9 @@ def main() -> int:
     sent = mk.mk_count_sentinels(ctx)
     stats = mk.mk_get_stats(ctx)
     mk.mk_destroy(ctx)
+    sync_latency = None
+    if args.trace_steps > 0:
+        sync_latency = traced_decode(model, w, ids, P, n, opts, args.trace_steps)
 
     mean_ms = float(np.mean(kernel_ms))
     achieved = float(np.mean(algo)) / (mean_ms * 1e-3) / 1e9
@@ -204,6 +296,8 @@ def main() -> int:
                     "same monokernel, one teacher-forced step per token"},
         "residual_sentinels": sent,
     }
+    if sync_latency is not None:
+        out["sync_latency"] = sync_latency
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle (bounded sample)")
         try:

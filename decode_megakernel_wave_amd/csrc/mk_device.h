@@ -58,6 +58,26 @@ __device__ __forceinline__ void stc64(void* p, uint64_t v) {
 }
 __device__ __forceinline__ void stcf(float* p, float v) { stc32(p, __float_as_uint(v)); }
 
+// 16 bytes of sync words per request: a buffer load with the same cache-policy
+// bits as the system-scope loads above (sc0 sc1), marked volatile (bit 31 of
+// the policy operand) so the compiler re-issues it in every poll round.  Each
+// aligned 4-byte word of the result is read whole, so a reader checks every
+// word for the sentinel, as it would after four single loads; the gain is a
+// quarter of the requests in flight while hundreds of workgroups poll.  The
+// buffer resource bounds the access: bytes beyond `bytes` read as zero.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+#if MK_SYNC_SCOPE == __HIP_MEMORY_SCOPE_SYSTEM
+constexpr int kPolicySync = (int)(0x80000000u | 1u | 16u);  // volatile | sc0 | sc1
+#else
+constexpr int kPolicySync = (int)(0x80000000u | 16u);       // volatile | sc1
+#endif
+__device__ __forceinline__ Rsrc sync_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u4 ldc128(Rsrc r, uint32_t byte_off) {
+  return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kPolicySync));
+}
+
 // Release / acquire between workgroups for data whose arrival the reader
 // cannot see in the data itself (the KV cache and the sentinel re-arms at a
 // step boundary; every stage in counter mode).  Everything the kernel shares

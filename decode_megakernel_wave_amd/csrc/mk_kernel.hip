@@ -204,39 +204,41 @@ __device__ __forceinline__ float poll_f32(Cx& c, const float* p, int op, int lay
 }
 
 // Stage n fp32 values of a sync buffer into LDS dst[0..npad) (zero padded),
-// multiplied by the fp16 gain when one is given.  All loads of a thread are
-// issued before any is checked.  Returns this thread's sum of squares of the
-// raw values (for RMSNorm).
+// multiplied by the fp16 gain when one is given.  n is a multiple of 4 and src
+// 16-byte aligned (every sync buffer is), so a thread reads 4 consecutive
+// values per 16-byte request; all requests of a thread are issued before any
+// is checked.  Returns this thread's sum of squares of the raw values (for
+// RMSNorm).
 __device__ __forceinline__ float stage_vec(Cx& c, const float* src, float* dst, int n, int npad, const uint16_t* gain, int op, int layer) {
-  constexpr int kPer = 16;  // floats a thread stages per round
+  constexpr int kGroups = 4;  // 16-byte groups a thread stages per round
+  const Rsrc rs = sync_rsrc(src, (uint32_t)n * 4u);
   float ss = 0.f;
-  for (int base = c.tid * 4; base < npad; base += kThreads * kPer) {
-    uint32_t v[kPer];
-    float g[kPer];
+  for (int base = c.tid * 4; base < npad; base += kThreads * 4 * kGroups) {
+    u4 v[kGroups];
+    float g[kGroups][4];
 #pragma unroll
-    for (int k = 0; k < kPer / 4; ++k) {
+    for (int k = 0; k < kGroups; ++k) {
       const int i = base + k * kThreads * 4;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[k * 4 + j] = (i + j < n) ? ldc32(src + i + j) : 0u;
+      v[k] = i < n ? ldc128(rs, (uint32_t)i * 4u) : u4{0u, 0u, 0u, 0u};
       if (gain && i < n) {
         const u2 w = *gp((const u2*)(gain + i));
         const _Float16* h = (const _Float16*)&w;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) g[k * 4 + j] = (float)h[j];
+        for (int j = 0; j < 4; ++j) g[k][j] = (float)h[j];
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) g[k * 4 + j] = 1.f;
+        for (int j = 0; j < 4; ++j) g[k][j] = 1.f;
       }
     }
     if (sentinel_mode(c)) {
-      // re-poll every element still holding the sentinel in one batch, so a
-      // late producer costs one more round trip, not one per element
+      // re-poll every group still holding a sentinel in one batch, so a late
+      // producer costs one more round trip, not one per element
       for (;;) {
         bool pending = false;
 #pragma unroll
-        for (int k = 0; k < kPer; ++k) {
-          const int i = base + (k / 4) * kThreads * 4 + (k % 4);
-          pending |= i < n && v[k] == kSent32;
+        for (int k = 0; k < kGroups; ++k) {
+          const int i = base + k * kThreads * 4;
+          pending |= i < n && (v[k][0] == kSent32 || v[k][1] == kSent32 || v[k][2] == kSent32 || v[k][3] == kSent32);
         }
         if (!pending || c.fail) break;
         if (expired(c, op, layer, base)) {
@@ -245,22 +247,23 @@ __device__ __forceinline__ float stage_vec(Cx& c, const float* src, float* dst, 
         }
         poll_pause(c);
 #pragma unroll
-        for (int k = 0; k < kPer; ++k) {
-          const int i = base + (k / 4) * kThreads * 4 + (k % 4);
-          if (i < n && v[k] == kSent32) v[k] = ldc32(src + i);
+        for (int k = 0; k < kGroups; ++k) {
+          const int i = base + k * kThreads * 4;
+          if (i < n && (v[k][0] == kSent32 || v[k][1] == kSent32 || v[k][2] == kSent32 || v[k][3] == kSent32))
+            v[k] = ldc128(rs, (uint32_t)i * 4u);
         }
       }
     }
 #pragma unroll
-    for (int k = 0; k < kPer / 4; ++k) {
+    for (int k = 0; k < kGroups; ++k) {
       const int i = base + k * kThreads * 4;
       if (i < npad) {
         f4 x;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float f = __uint_as_float(v[k * 4 + j]);
+          const float f = __uint_as_float(v[k][j]);
           ss += f * f;
-          x[j] = f * g[k * 4 + j];
+          x[j] = f * g[k][j];
         }
         *(f4*)(dst + i) = x;
       }

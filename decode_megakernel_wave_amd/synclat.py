@@ -1,0 +1,89 @@
+"""Inter-stage handoff latency from the monokernel's time journal.
+
+The journal (``mk_read_trace`` / ``mk_chain_read_trace``) holds one record of
+8 uint32 per (workgroup, step, instruction): {cta, step, pc, op | layer << 8,
+t_wait (low 32 bits of the 100 MHz device clock), t_ready - t_wait,
+t_done - t_wait, xcc}.  Every workgroup runs the same instruction sequence and
+each instruction consumes what the one before it produced (the first QKV
+instruction of a step consumes the token every workgroup computed itself).
+
+Handoff latency is measured the way "7 - AMD et le monokernel" (section 7.3)
+frames the cost of a synchronisation: from the moment the last producer of a
+stage has published (its ``t_done``) to the moment a consumer that was
+already waiting has its inputs staged (``t_ready``).  Per stage the
+critical-path handoff is the last consumer's ready time minus the last
+producer's done time.  Consumers that started waiting after the data was
+complete only pay a load round trip; they are reported apart.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+TICK_US = 0.01  # the device wall clock runs at 100 MHz
+
+OP_NAMES = {1: "qkv", 2: "attention", 4: "o_proj", 5: "up_gate", 6: "down", 7: "lm_head", 8: "argmax",
+            9: "chain"}
+
+
+def _relative_ticks(t: np.ndarray) -> np.ndarray:
+    """Unwrap 32-bit clock samples of one launch into signed ticks relative to the first."""
+    t = t.astype(np.int64)
+    return ((t - t[0] + (1 << 31)) % (1 << 32)) - (1 << 31)
+
+
+def handoffs(records: np.ndarray) -> dict:
+    """Per-op handoff statistics (microseconds) of a time journal.
+
+    Returns {op_name: {"stages", "waiting_consumers", "median_us", "p99_us",
+    "critical_median_us", "critical_p99_us", "late_staging_median_us"}} plus an
+    "all" entry pooling every op.
+    """
+    r = np.asarray(records, dtype=np.uint32).reshape(-1, 8)
+    r = r[r[:, 6] != 0]
+    if len(r) == 0:
+        return {}
+    tw = _relative_ticks(r[:, 4])
+    ready_rel = r[:, 5].astype(np.int64)
+    done = tw + r[:, 6].astype(np.int64)
+    ready = tw + ready_rel
+    step = r[:, 1].astype(np.int64)
+    pc = r[:, 2].astype(np.int64)
+    op = (r[:, 3] & 0xFF).astype(np.int64)
+    key = step * (1 << 20) + pc
+    order = np.unique(key)
+    groups = {k: np.nonzero(key == k)[0] for k in order}
+    per_op: dict[str, dict[str, list]] = {}
+    for prev_k, k in zip(order[:-1], order[1:]):
+        prod = groups[prev_k]
+        cons = groups[k]
+        cons = cons[ready_rel[cons] != 0]  # instructions without a staging mark have no handoff
+        if len(cons) == 0:
+            continue
+        last_done = done[prod].max()
+        waiting = cons[tw[cons] <= last_done]
+        late = cons[tw[cons] > last_done]
+        name = OP_NAMES.get(int(op[cons[0]]), str(int(op[cons[0]])))
+        d = per_op.setdefault(name, {"lat": [], "crit": [], "late": []})
+        d["lat"].extend((ready[waiting] - last_done).tolist())
+        d["late"].extend(ready_rel[late].tolist())
+        if len(waiting):
+            d["crit"].append(int(ready[cons].max() - last_done))
+    out = {}
+    pooled = {"lat": [], "crit": [], "late": []}
+    for name, d in per_op.items():
+        for k in pooled:
+            pooled[k].extend(d[k])
+        out[name] = _summary(d)
+    if per_op:
+        out["all"] = _summary(pooled)
+    return out
+
+
+def _summary(d: dict) -> dict:
+    def q(v, p):
+        return float(np.percentile(np.asarray(v, dtype=np.float64) * TICK_US, p)) if len(v) else None
+
+    return {"stages": len(d["crit"]), "waiting_consumers": len(d["lat"]),
+            "median_us": q(d["lat"], 50), "p99_us": q(d["lat"], 99),
+            "critical_median_us": q(d["crit"], 50), "critical_p99_us": q(d["crit"], 99),
+            "late_staging_median_us": q(d["late"], 50)}

@@ -1,0 +1,43 @@
+"""Handoff-latency analysis of the time journal on hand-built records (host logic, no GPU)."""
+import numpy as np
+import pytest
+
+from decode_megakernel_wave_amd import synclat
+
+
+def rec(cta, step, pc, op, t_wait, ready_rel, done_rel, xcc=0):
+    return [cta, step, pc, op, t_wait & 0xFFFFFFFF, ready_rel, done_rel, xcc]
+
+
+def test_handoff_latency_of_waiting_and_late_consumers():
+    base = 0xFFFFFF00  # the 32-bit clock wraps inside the journal
+    r = [
+        # stage pc 0 (up_gate, op 5): three producers, the last one done at base + 100
+        rec(0, 0, 0, 5, base, 5, 60),
+        rec(1, 0, 0, 5, base, 5, 100),
+        rec(2, 0, 0, 5, base, 5, 80),
+        # stage pc 1 (down, op 6): two consumers waiting since before base + 100, one arriving late
+        rec(0, 0, 1, 6, base + 60, 70, 200),    # ready at +130: latency 30 ticks
+        rec(1, 0, 1, 6, base + 100, 50, 200),   # waits from +100 (== last done): ready +150, latency 50
+        rec(2, 0, 1, 6, base + 120, 8, 200),    # started after the data was complete: 8 ticks of staging
+        [0] * 8,                                # unused record
+    ]
+    res = synclat.handoffs(np.array(r, dtype=np.uint32))
+    d = res["down"]
+    assert d["waiting_consumers"] == 2 and d["stages"] == 1
+    assert d["median_us"] == pytest.approx(0.40)           # median of 30 and 50 ticks
+    assert d["critical_median_us"] == pytest.approx(0.50)  # last ready (+150) - last done (+100)
+    assert d["late_staging_median_us"] == pytest.approx(0.08)
+    assert "up_gate" not in res  # the first stage of the journal has no producer in it
+    assert res["all"]["waiting_consumers"] == 2
+
+
+def test_records_without_a_staging_mark_are_skipped():
+    r = [rec(0, 0, 0, 7, 1000, 5, 50), rec(0, 0, 1, 8, 1050, 0, 20), rec(0, 1, 0, 1, 1075, 10, 40)]
+    res = synclat.handoffs(np.array(r, dtype=np.uint32))
+    assert "argmax" not in res
+    assert res["qkv"]["waiting_consumers"] == 0 and res["qkv"]["late_staging_median_us"] == pytest.approx(0.10)
+
+
+def test_empty_journal():
+    assert synclat.handoffs(np.zeros((4, 8), dtype=np.uint32)) == {}
