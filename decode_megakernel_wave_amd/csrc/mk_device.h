@@ -77,6 +77,9 @@ __device__ __forceinline__ Rsrc sync_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ u4 ldc128(Rsrc r, uint32_t byte_off) {
   return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kPolicySync));
 }
+__device__ __forceinline__ u2 ldc64v(Rsrc r, uint32_t byte_off) {
+  return __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, kPolicySync));
+}
 
 // Release / acquire between workgroups for data whose arrival the reader
 // cannot see in the data itself (the KV cache and the sentinel re-arms at a

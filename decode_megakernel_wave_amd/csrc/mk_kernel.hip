@@ -203,6 +203,27 @@ __device__ __forceinline__ float poll_f32(Cx& c, const float* p, int op, int lay
   return __uint_as_float(v);
 }
 
+__device__ __forceinline__ bool any_sent(u4 v) {
+  return v[0] == kSent32 || v[1] == kSent32 || v[2] == kSent32 || v[3] == kSent32;
+}
+
+// Poll four consecutive fp32 sync words (16-byte aligned) until none is the
+// sentinel (sentinel mode) or read them once (counter mode).
+__device__ __forceinline__ u4 poll_f32x4(Cx& c, Rsrc rs, uint32_t byte_off, int op, int layer) {
+  u4 v = ldc128(rs, byte_off);
+  if (sentinel_mode(c)) {
+    while (any_sent(v) && !c.fail) {
+      if (expired(c, op, layer, -1)) {
+        c.fail = true;
+        break;
+      }
+      poll_pause(c);
+      v = ldc128(rs, byte_off);
+    }
+  }
+  return v;
+}
+
 // Stage n fp32 values of a sync buffer into LDS dst[0..npad) (zero padded),
 // multiplied by the fp16 gain when one is given.  n is a multiple of 4 and src
 // 16-byte aligned (every sync buffer is), so a thread reads 4 consecutive
@@ -238,7 +259,7 @@ __device__ __forceinline__ float stage_vec(Cx& c, const float* src, float* dst, 
 #pragma unroll
         for (int k = 0; k < kGroups; ++k) {
           const int i = base + k * kThreads * 4;
-          pending |= i < n && (v[k][0] == kSent32 || v[k][1] == kSent32 || v[k][2] == kSent32 || v[k][3] == kSent32);
+          pending |= i < n && any_sent(v[k]);
         }
         if (!pending || c.fail) break;
         if (expired(c, op, layer, base)) {
@@ -249,8 +270,7 @@ __device__ __forceinline__ float stage_vec(Cx& c, const float* src, float* dst, 
 #pragma unroll
         for (int k = 0; k < kGroups; ++k) {
           const int i = base + k * kThreads * 4;
-          if (i < n && (v[k][0] == kSent32 || v[k][1] == kSent32 || v[k][2] == kSent32 || v[k][3] == kSent32))
-            v[k] = ldc128(rs, (uint32_t)i * 4u);
+          if (i < n && any_sent(v[k])) v[k] = ldc128(rs, (uint32_t)i * 4u);
         }
       }
     }
@@ -536,33 +556,36 @@ __device__ __forceinline__ void red_unit(Cx& c, int l, int h, int b) {
 #pragma unroll
   for (int d = 0; d < kRedDims; ++d) os[d] = 0.f;
   if (s < S) {
-    uint32_t raw[2 + kRedDims];
-    const float* ml = kp.att_ml + base * 2;
-    const float* ov = kp.att_o + base * hd + b * kRedDims;
-    raw[0] = ldc32(ml);
-    raw[1] = ldc32(ml + 1);
-#pragma unroll
-    for (int d = 0; d < kRedDims; ++d) raw[2 + d] = ldc32(ov + d);
+    // (m, l) is 8-byte aligned, the kRedDims output dims 32-byte aligned:
+    // one 8-byte and two 16-byte system-scope loads per split, re-issued
+    // together while any word is still the sentinel
+    static_assert(kRedDims == 8, "red_unit loads its dims as two 16-byte groups");
+    // the resources start at split 0 (uniform); lane s reads at its own offset
+    const int64_t base0 = base - s;
+    const Rsrc rml = sync_rsrc(kp.att_ml + base0 * 2, (uint32_t)S * 8u);
+    const Rsrc rov = sync_rsrc(kp.att_o + base0 * hd, (uint32_t)(S * hd) * 4u);
+    const uint32_t oml = (uint32_t)s * 8u, oov = (uint32_t)(s * hd + b * kRedDims) * 4u;
+    u2 ml = ldc64v(rml, oml);
+    u4 o0 = ldc128(rov, oov), o1 = ldc128(rov, oov + 16u);
     if (sentinel_mode(c)) {
-      for (;;) {
-        bool pending = false;
-#pragma unroll
-        for (int k = 0; k < 2 + kRedDims; ++k) pending |= raw[k] == kSent32;
-        if (!pending || c.fail) break;
+      while ((ml[0] == kSent32 || ml[1] == kSent32 || any_sent(o0) || any_sent(o1)) && !c.fail) {
         if (expired(c, OP_ATT, l, h)) {
           c.fail = true;
           break;
         }
         poll_pause(c);
-#pragma unroll
-        for (int k = 0; k < 2 + kRedDims; ++k)
-          if (raw[k] == kSent32) raw[k] = ldc32(k < 2 ? ml + k : ov + (k - 2));
+        ml = ldc64v(rml, oml);
+        o0 = ldc128(rov, oov);
+        o1 = ldc128(rov, oov + 16u);
       }
     }
-    ms = __uint_as_float(raw[0]);
-    ls = __uint_as_float(raw[1]);
+    ms = __uint_as_float(ml[0]);
+    ls = __uint_as_float(ml[1]);
 #pragma unroll
-    for (int d = 0; d < kRedDims; ++d) os[d] = __uint_as_float(raw[2 + d]);
+    for (int d = 0; d < 4; ++d) {
+      os[d] = __uint_as_float(o0[d]);
+      os[4 + d] = __uint_as_float(o1[d]);
+    }
   }
   const float M = wave_max(ms);
   const float w = (s < S && ms != -INFINITY) ? exp2f(ms - M) : 0.f;
@@ -851,7 +874,14 @@ __device__ __forceinline__ void att_stage(Cx& c, int l, int g, bool has_cur, boo
   float* kcur = c.sm.vec + G * hd;   // [hd]
   float* vcur = kcur + hd;           // [hd]
   const float* qsrc = buf_at(kp.q, c.e, l, 0) + g * G * hd;
-  for (int i = c.tid; i < G * hd; i += kThreads) qs[i] = poll_f32(c, qsrc + i, OP_ATT, l) * qscale;
+  {
+    // 16-byte polls: G * hd is a multiple of 64 and the group's q 16-byte aligned
+    const Rsrc rs = sync_rsrc(qsrc, (uint32_t)(G * hd) * 4u);
+    for (int i = c.tid * 4; i < G * hd; i += kThreads * 4) {
+      const u4 v = poll_f32x4(c, rs, (uint32_t)i * 4u, OP_ATT, l);
+      *(f4*)(qs + i) = f4{__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3])} * qscale;
+    }
+  }
   if (has_cur && c.tid < 2 * hd) {
     const int i = c.tid % hd;
     const uint16_t* src = (c.tid < hd ? kp.kc : kp.vc) + (((int64_t)l * kp.nkv + g) * kp.max_seq + c.pos) * hd + i;

@@ -35,8 +35,10 @@ def handoffs(records: np.ndarray) -> dict:
     """Per-op handoff statistics (microseconds) of a time journal.
 
     Returns {op_name: {"stages", "waiting_consumers", "median_us", "p99_us",
-    "critical_median_us", "critical_p99_us", "late_staging_median_us"}} plus an
-    "all" entry pooling every op.
+    "critical_median_us", "critical_p99_us", "late_staging_median_us",
+    "span_median_us", "span_mean_us"}} plus an "all" entry pooling every op.  The
+    span of a stage is its share of the critical path: from the last producer's
+    done time to the last consumer's.
     """
     r = np.asarray(records, dtype=np.uint32).reshape(-1, 8)
     r = r[r[:, 6] != 0]
@@ -63,13 +65,15 @@ def handoffs(records: np.ndarray) -> dict:
         waiting = cons[tw[cons] <= last_done]
         late = cons[tw[cons] > last_done]
         name = OP_NAMES.get(int(op[cons[0]]), str(int(op[cons[0]])))
-        d = per_op.setdefault(name, {"lat": [], "crit": [], "late": []})
+        d = per_op.setdefault(name, {"lat": [], "crit": [], "late": [], "span": []})
         d["lat"].extend((ready[waiting] - last_done).tolist())
         d["late"].extend(ready_rel[late].tolist())
         if len(waiting):
             d["crit"].append(int(ready[cons].max() - last_done))
+        # the stage's share of the critical path: last producer done -> last consumer done
+        d["span"].append(int(done[groups[k]].max() - last_done))
     out = {}
-    pooled = {"lat": [], "crit": [], "late": []}
+    pooled = {"lat": [], "crit": [], "late": [], "span": []}
     for name, d in per_op.items():
         for k in pooled:
             pooled[k].extend(d[k])
@@ -86,4 +90,5 @@ def _summary(d: dict) -> dict:
     return {"stages": len(d["crit"]), "waiting_consumers": len(d["lat"]),
             "median_us": q(d["lat"], 50), "p99_us": q(d["lat"], 99),
             "critical_median_us": q(d["crit"], 50), "critical_p99_us": q(d["crit"], 99),
-            "late_staging_median_us": q(d["late"], 50)}
+            "late_staging_median_us": q(d["late"], 50), "span_median_us": q(d["span"], 50),
+            "span_mean_us": float(np.mean(d["span"]) * TICK_US) if len(d["span"]) else None}

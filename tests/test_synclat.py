@@ -28,6 +28,7 @@ def test_handoff_latency_of_waiting_and_late_consumers():
     assert d["median_us"] == pytest.approx(0.40)           # median of 30 and 50 ticks
     assert d["critical_median_us"] == pytest.approx(0.50)  # last ready (+150) - last done (+100)
     assert d["late_staging_median_us"] == pytest.approx(0.08)
+    assert d["span_median_us"] == pytest.approx(2.20)  # last consumer done (+320) - last producer done (+100)
     assert "up_gate" not in res  # the first stage of the journal has no producer in it
     assert res["all"]["waiting_consumers"] == 2
 
