@@ -183,6 +183,8 @@ def main() -> int:
     ap.add_argument("--decode-steps", type=int, default=0, help="tokens per launch (default: the workload's)")
     ap.add_argument("--sync", default="sentinel", choices=["sentinel", "counter"])
     ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--top-k", type=int, default=1, help="1 = greedy (the benchmark); 2..16 = top-k sampling")
+    ap.add_argument("--temperature", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--trace-steps", type=int, default=0,
                     help="after the timed launches, run one more launch that records the per-instruction time "
@@ -232,6 +234,8 @@ def main() -> int:
     mk.mk_load_weights(ctx, wd)
     del wd
     torch.cuda.empty_cache()
+    if args.top_k > 1:
+        mk.mk_set_sampling(ctx, args.top_k, args.temperature, seed=3)
     t = time.time()
     t0 = mk.mk_prefill(ctx, ids)
     prefill_ms = mk.mk_get_stats(ctx)["gpu_ms"]
@@ -283,7 +287,9 @@ def main() -> int:
         "config": {"workload": f"{args.workload} decoder greedy decode", "layers": model.n_layers,
                    "d_model": model.d_model, "heads": f"{model.n_heads}q/{model.n_kv_heads}kv x {model.head_dim}",
                    "ffn": model.ffn, "vocab": model.vocab, "prompt_len": P, "decode_tokens_per_step": n,
-                   "batch": 1, "sync": args.sync, "xcd_replicas": args.replicas, "grid": stats["grid"],
+                   "batch": 1, "sync": args.sync, "xcd_replicas": args.replicas,
+                   "token_choice": "greedy" if args.top_k == 1 else f"top-{args.top_k} sampling, T={args.temperature}",
+                   "grid": stats["grid"],
                    "block": stats["block"], "lds_bytes": stats["lds_bytes"], "ring_depth": stats["ring_depth"]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,

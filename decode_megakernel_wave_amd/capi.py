@@ -78,6 +78,7 @@ SIGNATURES = [
                                    C.POINTER(C.c_float)]),
     ("mk_generate", C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.c_int32, C.c_int32, C.POINTER(C.c_int32)]),
     ("mk_rewind", C.c_int, [C.c_void_p, C.c_int32]),
+    ("mk_set_sampling", C.c_int, [C.c_void_p, C.c_int32, C.c_float, C.c_uint64]),
     ("mk_position", C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
     ("mk_get_stats", C.c_int, [C.c_void_p, C.POINTER(mk_stats)]),
     ("mk_count_sentinels", C.c_int, [C.c_void_p, C.POINTER(C.c_int64)]),
@@ -223,6 +224,11 @@ def mk_generate(ctx, ids, n_steps: int) -> np.ndarray:
     _check(lib().mk_generate(ctx, ids.ctypes.data_as(C.POINTER(C.c_int32)), len(ids), n_steps,
                              out.ctypes.data_as(C.POINTER(C.c_int32))), ctx)
     return out
+
+
+def mk_set_sampling(ctx, top_k: int = 1, temperature: float = 1.0, seed: int = 0) -> None:
+    """Top-k / temperature sampling for later steps (top_k = 1: greedy)."""
+    _check(lib().mk_set_sampling(ctx, int(top_k), float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF), ctx)
 
 
 def mk_rewind(ctx, pos: int) -> None:

@@ -300,6 +300,11 @@ struct mk_ctx {
   uint32_t* att_cnt = nullptr;
   uint64_t* lmp = nullptr;
   int64_t lmp_es = 0, lmp_rs = 0;
+  uint64_t* lmk = nullptr;
+  int64_t lmk_es = 0, lmk_rs = 0;
+  int top_k = 1, last_top_k = 1;
+  float temperature = 1.0f;
+  uint64_t seed = 0;
   int64_t layout[16] = {0};
   struct Region { int64_t off, words; };
   std::vector<Region> epoch_regions[3];  // per epoch: word ranges that a step fully writes
@@ -341,9 +346,13 @@ int ctx_alloc_arena(mk_ctx* c) {
   off += ((3 * c->lmp_es * 2 + 63) / 64) * 64;
   const int64_t ocnt = off;  // attention merge counters [L][n_kv_heads], zero at launch
   off += (((int64_t)L * k.n_kv_heads + 63) / 64) * 64;
+  const int64_t olmk = off;  // per-workgroup top-k keys for sampling (u64, zero = not yet written)
+  c->lmk_rs = (int64_t)p.lm_slots * kMaxTopK;
+  c->lmk_es = c->lmk_rs * R;
+  off += ((3 * c->lmk_es * 2 + 63) / 64) * 64;
   g.arena_words = off;
-  const int64_t lay[10] = {oxa, oxm, oq, oo, om, oao, oml, g.lmp_word_off, off, ocnt};
-  for (int i = 0; i < 10; ++i) c->layout[i] = lay[i];
+  const int64_t lay[11] = {oxa, oxm, oq, oo, om, oao, oml, g.lmp_word_off, off, ocnt, olmk};
+  for (int i = 0; i < 11; ++i) c->layout[i] = lay[i];
   CHK(g.alloc(&g.d_arena, off * 4));
   float* a = g.d_arena;
   c->xa.p = a + oxa;
@@ -355,6 +364,7 @@ int ctx_alloc_arena(mk_ctx* c) {
   c->att_ml = a + oml;
   c->lmp = (uint64_t*)(a + g.lmp_word_off);
   c->att_cnt = (uint32_t*)(a + ocnt);
+  c->lmk = (uint64_t*)(a + olmk);
   return MK_OK;
 }
 
@@ -410,6 +420,14 @@ int ctx_run(mk_ctx* c, int n, int first_token, const int32_t* forced, int32_t* t
   kp.lmp = c->lmp;
   kp.lmp_es = c->lmp_es;
   kp.lmp_rs = c->lmp_rs;
+  kp.lmk = c->lmk;
+  kp.lmk_es = c->lmk_es;
+  kp.lmk_rs = c->lmk_rs;
+  kp.top_k = c->top_k;
+  c->last_top_k = c->top_k;
+  kp.inv_temp = 1.0f / c->temperature;
+  kp.seed_lo = (uint32_t)c->seed;
+  kp.seed_hi = (uint32_t)(c->seed >> 32);
   kp.L = k.n_layers;
   kp.d = k.d_model;
   kp.nq = k.n_heads;
@@ -655,6 +673,18 @@ int mk_generate(mk_ctx* c, const int32_t* ids, int32_t n_prompt, int32_t n_steps
   return mk_decode(c, n_steps, tokens_out + 1, nullptr);
 }
 
+int mk_set_sampling(mk_ctx* c, int32_t top_k, float temperature, uint64_t seed) {
+  if (!c) return MK_EINVAL;
+  if (top_k < 1 || top_k > kMaxTopK || top_k > c->cfg.vocab)
+    return c->g.fail(MK_EINVAL, "top_k outside [1, min(16, vocab)]");
+  if (top_k > 1 && !(temperature > 0.0f && temperature < INFINITY))
+    return c->g.fail(MK_EINVAL, "temperature must be positive and finite");
+  c->top_k = top_k;
+  c->temperature = top_k > 1 ? temperature : 1.0f;
+  c->seed = seed;
+  return MK_OK;
+}
+
 int mk_rewind(mk_ctx* c, int32_t pos) {
   if (!c) return MK_EINVAL;
   if (c->state < ST_READY) return c->g.fail(MK_ESTATE, "rewind before prefill");
@@ -704,6 +734,13 @@ int mk_count_sentinels(mk_ctx* c, int64_t* count) {
   hipFree(d);
   if (e != hipSuccess) return g.hip_fail(e, "sentinel count");
   for (uint64_t v : keys) h += v == kSent64;
+  if (c->last_top_k > 1) {
+    // the top-k lists of the last step: [R][lm_slots][kMaxTopK], the first top_k of each written
+    std::vector<uint64_t> lists(c->lmk_es);
+    e = hipMemcpy(lists.data(), c->lmk + el * c->lmk_es, lists.size() * 8, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return g.hip_fail(e, "sentinel count");
+    for (int64_t i = 0; i < c->lmk_es; ++i) h += (i % kMaxTopK) < c->last_top_k && lists[i] == kSent64;
+  }
   *count = (int64_t)h;
   return MK_OK;
 }

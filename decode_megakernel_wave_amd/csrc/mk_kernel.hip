@@ -1102,6 +1102,83 @@ __device__ __forceinline__ uint64_t argmax_key(float v, int idx) {
   b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
   return ((uint64_t)b << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)idx);
 }
+__device__ __forceinline__ float key_value(uint64_t key) {
+  uint32_t b = (uint32_t)(key >> 32);
+  b = (b & 0x80000000u) ? (b & 0x7FFFFFFFu) : ~b;
+  return __uint_as_float(b);
+}
+__device__ __forceinline__ int key_index(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
+
+// ---------------------------------------------------------------- top-k sampling
+// Keys order logits like the greedy argmax (larger logit first, equal logits
+// by smaller id); every real key is > 1, and 1 marks an empty entry.
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src_lane) {
+  const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)v, src_lane), hi = (uint32_t)__shfl((int)(uint32_t)(v >> 32), src_lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint64_t o = shfl_u64(v, lane_id() ^ off);
+    v = v > o ? v : o;
+  }
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Insert a key (the same value in every lane) into a wavefront's list of its
+// K largest keys, held in descending order by lanes 0..K-1.
+__device__ __forceinline__ void topk_insert(uint64_t& mine, uint64_t key, int K) {
+  const int lane = lane_id();
+  const uint64_t gt = __ballot(lane < K && key > mine);  // a suffix of lanes [p, K)
+  if (gt == 0) return;
+  const int p = __builtin_ctzll(gt);
+  const uint64_t prev = shfl_u64(mine, lane > 0 ? lane - 1 : 0);
+  if (lane == p) mine = key;
+  else if (lane > p && lane < K) mine = prev;
+}
+
+// The K largest of the keys every lane holds in v[0..M) (consumed), in
+// descending order in lanes 0..K-1 (1 where fewer than K real keys exist).
+template <int M>
+__device__ __forceinline__ uint64_t wave_topk(uint64_t (&v)[M], int K) {
+  uint64_t out = 1;
+  for (int j = 0; j < K; ++j) {
+    uint64_t m = 1;
+#pragma unroll
+    for (int i = 0; i < M; ++i) m = v[i] > m ? v[i] : m;
+    const uint64_t w = wave_max_u64(m);
+    if (w <= 1) break;
+#pragma unroll
+    for (int i = 0; i < M; ++i)
+      if (v[i] == w) v[i] = 1;  // keys are distinct (each carries its row)
+    if (lane_id() == j) out = w;
+  }
+  return out;
+}
+
+// Philox4x32 with 10 rounds (Salmon, Moraes, Dror and Shaw, "Parallel random
+// numbers: as easy as 1, 2, 3", SC11): first output word for the counter
+// (ctr, 0, 0, 0) and the key (k0, k1).  A round multiplies words 0 and 2 by
+// the two round constants and recombines the 64-bit products with words 1, 3
+// and the key; the key is advanced by the two Weyl increments between rounds.
+__device__ __forceinline__ uint32_t philox_word0(uint32_t ctr, uint32_t k0, uint32_t k1) {
+  uint32_t x0 = ctr, x1 = 0u, x2 = 0u, x3 = 0u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo0 = 0xD2511F53u * x0, hi0 = __umulhi(0xD2511F53u, x0);
+    const uint32_t lo1 = 0xCD9E8D57u * x2, hi1 = __umulhi(0xCD9E8D57u, x2);
+    x0 = hi1 ^ x1 ^ k0;
+    x1 = lo1;
+    x2 = hi0 ^ x3 ^ k1;
+    x3 = lo0;
+  }
+  return x0;
+}
 
 __device__ __forceinline__ void op_lmhead(Cx& c, Ring& ring, const Ins& in) {
   const KParams& kp = *c.kp;
@@ -1109,6 +1186,8 @@ __device__ __forceinline__ void op_lmhead(Cx& c, Ring& ring, const Ins& in) {
   counter_wait(c, in.sync_in, in.n_in, OP_LMHEAD, L);
   if (!sentinel_mode(c)) cta_sync(c);
   uint64_t best = 1;  // below every real key
+  const int K = kp.top_k > 1 ? kp.top_k : 1;
+  uint64_t wl = 1;    // sampling: the workgroup's K largest keys in lanes 0..K-1 of wavefront 0
   if (in.nu > 0) {
     const uint16_t* gf = kp.norms + (int64_t)L * 2 * kp.d;
     const float ss = stage_vec(c, buf_at(kp.xm, c.e, L - 1, c.rep), c.sm.vec, kp.d, in.kpad, gf, OP_LMHEAD, L);
@@ -1117,28 +1196,53 @@ __device__ __forceinline__ void op_lmhead(Cx& c, Ring& ring, const Ins& in) {
     float bv = -INFINITY;
     int bi = -1;
     bool nan = false;
+    uint64_t mine = 1;  // sampling: this wavefront's K largest keys, lane j the j-th
     gemv_dispatch(c, ring, in, c.sm.vec, scale, [&](int u, float y, float) {
       const int row = in.u0 + u;
       if (lo && c.lane == 0) *gp(lo + row) = y;
-      if (y != y) nan = true;
-      else if (bi < 0 || y > bv || (y == bv && row < bi)) { bv = y; bi = row; }
+      if (y != y) {
+        nan = true;
+      } else {
+        if (bi < 0 || y > bv || (y == bv && row < bi)) {
+          bv = y;
+          bi = row;
+        }
+        if (K > 1) topk_insert(mine, argmax_key(y, row), K);
+      }
     });
     if (nan && c.lane == 0) raise_fault(c, -8, OP_LMHEAD, L, c.step);
     if (c.lane == 0) c.sm.keys[c.wave] = bi >= 0 ? argmax_key(bv, bi) : 1;
     cta_sync(c);
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) best = max(best, c.sm.keys[w]);
+    if (K > 1) {
+      // the workgroup's K largest: wavefront lists through the scratch, merged by wavefront 0
+      uint64_t* lists = (uint64_t*)c.sm.scratch;  // [kWaves][K]
+      if (c.lane < K) lists[c.wave * K + c.lane] = mine;
+      cta_sync(c);
+      if (c.wave == 0) {
+        static_assert(kWaves * kMaxTopK <= 128, "two list entries per lane");
+        uint64_t v[2] = {c.lane < kWaves * K ? lists[c.lane] : 1, c.lane + 64 < kWaves * K ? lists[c.lane + 64] : 1};
+        wl = wave_topk<2>(v, K);
+      }
+    }
   }
   // re-arm the slot for the step after next, then one release fence per step
   // orders this step's stores (KV cache, re-arms) before the key.
   uint64_t* slot = kp.lmp + c.e * kp.lmp_es + in.slot;
   uint64_t* slot1 = kp.lmp + c.e1 * kp.lmp_es + in.slot;
   if (sentinel_mode(c) && c.wave == 0 && c.lane < kp.R) stc64(slot1 + c.lane * kp.lmp_rs, kSent64);
+  uint64_t* list = kp.lmk + c.e * kp.lmk_es + (int64_t)in.slot * kMaxTopK;
+  uint64_t* list1 = kp.lmk + c.e1 * kp.lmk_es + (int64_t)in.slot * kMaxTopK;
+  if (K > 1 && sentinel_mode(c) && c.wave == 0 && c.lane < K)
+    for (int r = 0; r < kp.R; ++r) stc64(list1 + r * kp.lmk_rs + c.lane, kSent64);
   stores_acked();
   cta_sync(c);
   if (c.wave == 0) {
     release_stores();
     if (c.lane < kp.R) stc64(slot + c.lane * kp.lmp_rs, best);
+    if (K > 1 && c.lane < K)
+      for (int r = 0; r < kp.R; ++r) stc64(list + r * kp.lmk_rs + c.lane, wl);
     if (!sentinel_mode(c)) {
       // counter mode: the keys themselves must be out before the count says so
       release_stores();
@@ -1147,10 +1251,94 @@ __device__ __forceinline__ void op_lmhead(Cx& c, Ring& ring, const Ins& in) {
   }
 }
 
+// Sampling instead of the argmax: every workgroup merges the per-workgroup
+// top-K lists (polled like the argmax keys) into the global K largest keys,
+// then draws the token by the inverse-CDF rule with a Philox uniform.  The
+// arithmetic is the same in every workgroup, so all draw the same token.
+__device__ __forceinline__ void op_sample(Cx& c, const Ins& in) {
+  const KParams& kp = *c.kp;
+  const int K = kp.top_k, n = in.nu * K;
+  const uint64_t* src = kp.lmk + c.e * kp.lmk_es + c.rep * kp.lmk_rs;  // [slot][kMaxTopK]
+  constexpr int kPer = 8;
+  uint64_t wl = 1;  // this wavefront's running K largest
+  for (int base = 0; base < n; base += kThreads * kPer) {
+    uint64_t v[kPer + 1];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = base + c.tid + j * kThreads;
+      v[j] = i < n ? ldc64(src + (i / K) * kMaxTopK + i % K) : 1;
+    }
+    if (sentinel_mode(c)) {
+      for (;;) {
+        bool pending = false;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) pending |= v[j] == kSent64;
+        if (!pending || c.fail) break;
+        if (expired(c, OP_ARGMAX, kp.L, base)) {
+          c.fail = true;
+          break;
+        }
+        poll_pause(c);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          const int i = base + c.tid + j * kThreads;
+          if (v[j] == kSent64) v[j] = ldc64(src + (i / K) * kMaxTopK + i % K);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (v[j] == kSent64) v[j] = 1;  // only on an aborted run
+    }
+    v[kPer] = wl;
+    wl = wave_topk<kPer + 1>(v, K);
+  }
+  uint64_t* lists = (uint64_t*)c.sm.scratch;  // [kWaves][K]
+  if (c.lane < K) lists[c.wave * K + c.lane] = wl;
+  cta_sync(c);
+  mark_ready(c);
+  if (c.wave == 0) {
+    acquire_polled();
+    uint64_t v[2] = {c.lane < kWaves * K ? lists[c.lane] : 1, c.lane + 64 < kWaves * K ? lists[c.lane + 64] : 1};
+    const uint64_t key = wave_topk<2>(v, K);
+    // weights exp((z_j - z_0) / T) of the candidates in order; running sums in that order
+    const uint32_t top_hi = __builtin_amdgcn_readfirstlane((uint32_t)(key >> 32));
+    const uint32_t top_lo = __builtin_amdgcn_readfirstlane((uint32_t)key);
+    const uint64_t top = ((uint64_t)top_hi << 32) | top_lo;  // lane 0: the largest logit
+    const float z0 = key_value(top);
+    const float w = c.lane < K && key > 1 ? exp2f((key_value(key) - z0) * kp.inv_temp * kLog2e) : 0.f;
+    const uint32_t word = philox_word0((uint32_t)c.pos, kp.seed_lo, kp.seed_hi);
+    const float u = (float)(word >> 8) * 0x1p-24f;
+    float total = 0.f;
+    for (int j = 0; j < K; ++j) total += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
+    const float target = u * total;
+    float cum = 0.f;
+    int pick = K - 1;
+    for (int j = 0; j < K; ++j) {
+      cum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
+      if (cum > target) {
+        pick = j;
+        break;
+      }
+    }
+    const int id = key_index(key);
+    const int tok = __builtin_amdgcn_readlane(id, pick);
+    if (c.lane == 0) c.sm.misc[1] = (uint32_t)tok;
+  }
+  cta_sync(c);
+  int tok = __builtin_amdgcn_readfirstlane((int)c.sm.misc[1]);
+  if (tok < 0 || tok >= kp.V) tok = 0;  // only on an aborted run
+  if (c.cta == 0 && c.tid == 0) *gp(kp.tokens + c.step) = tok;
+  c.tok = tok;
+}
+
 __device__ __forceinline__ void op_argmax(Cx& c, const Ins& in) {
   const KParams& kp = *c.kp;
   counter_wait(c, in.sync_in, in.n_in, OP_ARGMAX, kp.L);
   if (!sentinel_mode(c)) cta_sync(c);
+  if (kp.top_k > 1) {
+    op_sample(c, in);
+    return;
+  }
   const uint64_t* src = kp.lmp + c.e * kp.lmp_es + c.rep * kp.lmp_rs;
   uint64_t k = 0;
   for (int i = c.tid; i < in.nu; i += kThreads) {

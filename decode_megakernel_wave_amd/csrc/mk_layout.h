@@ -26,6 +26,7 @@ constexpr int kMaxK = 16384;              // longest GEMV row
 constexpr int kRedDims = 8;               // output dims per attention-reduce unit
 constexpr int kScratchFloats = 4352;      // LDS scratch for cross-wave reductions (17 KB)
 constexpr int kResidRows = 1024;          // LDS rows for residual inputs / staged GEMV outputs
+constexpr int kMaxTopK = 16;              // largest k of top-k sampling
 
 // Small LDS fields after the residual rows (byte offsets within a 1 KB block).
 constexpr int kSmallBytes = 1024;
@@ -126,6 +127,12 @@ struct KParams {
   uint64_t watchdog_ticks;    // 100 MHz ticks
   int32_t poll_sleep;         // s_sleep units between failed poll rounds (0 = spin)
   int32_t pad2;
+  // top-k / temperature sampling (top_k == 1: greedy argmax, the lists are unused)
+  uint64_t* lmk;              // [3][R][lm_slots][kMaxTopK] per-workgroup top-k keys
+  int64_t lmk_es, lmk_rs;
+  int32_t top_k;
+  float inv_temp;             // 1 / temperature
+  uint32_t seed_lo, seed_hi;  // Philox key
 };
 
 }  // namespace mk

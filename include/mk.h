@@ -132,12 +132,30 @@ int mk_prefill(mk_ctx* ctx, const int32_t* ids, int32_t n, int32_t* t0_out);
 int mk_decode(mk_ctx* ctx, int32_t n_steps, int32_t* tokens_out, float* logits_out);
 
 /* Like mk_decode, but step s consumes tokens_in[s] (host) instead of the
- * previous greedy token (teacher forcing).  tokens_out gets each step's argmax. */
+ * previous token (teacher forcing).  tokens_out gets each step's choice (the
+ * argmax, or the draw when sampling is on: mk_set_sampling). */
 int mk_decode_forced(mk_ctx* ctx, int32_t n_steps, const int32_t* tokens_in,
                      int32_t* tokens_out, float* logits_out);
 
 /* Prefill then decode: tokens_out (host) receives n_steps + 1 tokens: t0..t_n. */
 int mk_generate(mk_ctx* ctx, const int32_t* ids, int32_t n_prompt, int32_t n_steps, int32_t* tokens_out);
+
+/* Token choice of every later step (prefill's t0 included): top_k = 1 (the
+ * default) is greedy argmax; 2 <= top_k <= 16 draws from the top_k largest
+ * logits with weights exp((z_i - z_max) / temperature), ordered by logit
+ * (equal logits by increasing id), by the inverse-CDF rule: the first
+ * candidate whose running weight sum exceeds u * total, else the last.  u is
+ * the first 32-bit word of Philox4x32-10 (Salmon et al., "Parallel random
+ * numbers: as easy as 1, 2, 3", SC11) with key (seed mod 2^32, seed div 2^32)
+ * and counter (p, 0, 0, 0), p = the position of the token the step consumes,
+ * taken as floor(word / 2^8) / 2^24.  Sampling is what "7 - AMD et le
+ * monokernel" (section 7.1) names among the single kernel's duties; the
+ * rule itself is the plain reading.  Weights and sums are fp32; the whole
+ * choice runs inside the monokernel (every workgroup merges the per-
+ * workgroup top-k lists and draws the same token).  MK_EINVAL for top_k
+ * outside [1, min(16, vocab)] or, when top_k > 1, a temperature that is not
+ * positive and finite; the state is then unchanged. */
+int mk_set_sampling(mk_ctx* ctx, int32_t top_k, float temperature, uint64_t seed);
 
 /* Move the generation state back to position pos (1 <= pos <= current): the
  * KV cache of positions < pos is kept and the token consumed at pos becomes
@@ -164,7 +182,8 @@ int mk_read_trace(mk_ctx* ctx, uint32_t* host_buf, int64_t capacity_records, int
  * at word_off into host memory.  mk_debug_layout gives the word offsets of
  * its regions: [0] xa, [1] xm, [2] q, [3] o, [4] m, [5] att_o, [6] att_ml,
  * [7] argmax keys (uint64), [8] arena size, [9] attention merge counters
- * (uint32 [n_layers][n_kv_heads]). */
+ * (uint32 [n_layers][n_kv_heads]), [10] per-workgroup top-k keys of sampling
+ * (uint64 [3][replicas][workgroups][16]). */
 int mk_debug_layout(const mk_ctx* ctx, int64_t* offsets /* [16] */);
 int mk_debug_arena(mk_ctx* ctx, int64_t word_off, int64_t n_words, uint32_t* host);
 /* (step << 16) | (pc + 1) of the last instruction each workgroup finished in
