@@ -76,3 +76,35 @@ def test_2b_bench_prompt512(w2b):
     """The benchmark's configuration: 512-token prompt, then decode."""
     err = _parity(inputs.M2B, w2b, P=512, n=4)
     print(f"2B P=512: max |dlogit| {err:.2e}")
+
+
+def test_2b_topk_sampling(w2b):
+    """Top-16 sampling at the benchmark's model size (128256 logits over 256 workgroups): every
+    draw equals the sampling oracle applied to that step's GPU logits with the oracle's Philox
+    uniform, except draws within 1e-5 of a boundary."""
+    from oracle import sampling as osamp
+    P, n, k, T, seed = 16, 6, 16, 0.8, 11
+    ids = inputs.make_prompt(inputs.M2B, P, seed=1)
+    ctx = mk.mk_create(inputs.M2B, max_seq=P + n + 1)
+    try:
+        wd = mk.to_device(w2b)
+        mk.mk_load_weights(ctx, wd)
+        del wd
+        mk.mk_set_sampling(ctx, k, T, seed)
+        mk.mk_prefill(ctx, ids)
+        toks, logits = mk.mk_decode(ctx, n, vocab=inputs.M2B.vocab)
+        sent = mk.mk_count_sentinels(ctx)
+    finally:
+        mk.mk_destroy(ctx)
+        torch.cuda.empty_cache()
+    assert sent == 0
+    compared = 0
+    for s in range(n):
+        z = logits[s].astype(np.float64)
+        u = osamp.uniform(seed, P + s)
+        want, cand, _, _ = osamp.sample(z, k, T, u)
+        assert int(toks[s]) in set(cand.tolist())
+        if osamp.draw_ambiguity(z, k, T, u) > 1e-5:
+            assert int(toks[s]) == want, f"step {s}: GPU drew {toks[s]}, oracle {want}"
+            compared += 1
+    assert compared >= n - 1
