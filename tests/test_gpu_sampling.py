@@ -119,3 +119,20 @@ def test_invalid_sampling_arguments(tiny):
         assert mk.mk_prefill(ctx, ids) >= 0
     finally:
         mk.mk_destroy(ctx)
+
+
+def test_generate_and_chunked_decode_draw_the_same_sequence(tiny):
+    """mk_generate (prefill + one decode launch) and prefill + two decode launches of half the
+    steps draw the same tokens: the Philox counter is the position, not the launch step."""
+    w, ids = tiny
+    ctx = load(mk, inputs.TINY, w, P + N + 1)
+    try:
+        mk.mk_set_sampling(ctx, 8, 1.0, 321)
+        gen = mk.mk_generate(ctx, ids, N)
+        t0 = mk.mk_prefill(ctx, ids)
+        a = mk.mk_decode(ctx, N // 2)
+        b = mk.mk_decode(ctx, N - N // 2)
+    finally:
+        mk.mk_destroy(ctx)
+    assert gen[0] == t0
+    assert np.array_equal(gen[1:], np.concatenate([a, b]))
