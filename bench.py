@@ -189,6 +189,9 @@ def main() -> int:
     ap.add_argument("--trace-steps", type=int, default=0,
                     help="after the timed launches, run one more launch that records the per-instruction time "
                          "journal of its first N steps and report the inter-stage handoff latency")
+    ap.add_argument("--probes", action="store_true",
+                    help="only run the calibration probes (empty-kernel launch cost, nontemporal read ceiling "
+                         "over 4 GiB, naive atomic grid barrier) and print one JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (torch) and exit: the reference "
                          "kernel for scaling the HBM byte counters")
@@ -214,6 +217,21 @@ def main() -> int:
 
     import decode_megakernel_wave_amd as mk
     from decode_megakernel_wave_amd import inputs
+
+    if args.probes:
+        buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+        buf.fill_(1)
+        launch = mk.mk_probe_launch(2000)
+        read = mk.mk_probe_read(buf, repeats=5)
+        del buf
+        barrier = mk.mk_probe_barrier(2000)
+        out = {"probes": "calibration", "launch": launch, "read_4GiB_GB_per_s": read,
+               "read_frac_of_8TBps": read / HBM_PEAK_GBS, "naive_grid_barrier_us": barrier,
+               "note": "pages' MI300X context: ~4.5 us launch, 7.59-7.88 us atomic grid sync"}
+        log(f"[bench] probes: launch {launch['us_per_launch_pipelined']:.2f} us pipelined / "
+            f"{launch['us_per_launch_round_trip']:.2f} us round trip; read {read:.0f} GB/s; barrier {barrier:.2f} us")
+        print(json.dumps(out), flush=True)
+        return 0
 
     if args.workload.startswith("chain"):
         return chain_bench(args)

@@ -79,6 +79,9 @@ SIGNATURES = [
     ("mk_generate", C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.c_int32, C.c_int32, C.POINTER(C.c_int32)]),
     ("mk_rewind", C.c_int, [C.c_void_p, C.c_int32]),
     ("mk_set_sampling", C.c_int, [C.c_void_p, C.c_int32, C.c_float, C.c_uint64]),
+    ("mk_probe_launch", C.c_int, [C.c_int, C.c_void_p, C.c_int32, C.POINTER(C.c_double), C.POINTER(C.c_double)]),
+    ("mk_probe_read", C.c_int, [C.c_int, C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.POINTER(C.c_double)]),
+    ("mk_probe_barrier", C.c_int, [C.c_int, C.c_void_p, C.c_int32, C.POINTER(C.c_double)]),
     ("mk_position", C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
     ("mk_get_stats", C.c_int, [C.c_void_p, C.POINTER(mk_stats)]),
     ("mk_count_sentinels", C.c_int, [C.c_void_p, C.POINTER(C.c_int64)]),
@@ -229,6 +232,28 @@ def mk_generate(ctx, ids, n_steps: int) -> np.ndarray:
 def mk_set_sampling(ctx, top_k: int = 1, temperature: float = 1.0, seed: int = 0) -> None:
     """Top-k / temperature sampling for later steps (top_k = 1: greedy)."""
     _check(lib().mk_set_sampling(ctx, int(top_k), float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF), ctx)
+
+
+def mk_probe_launch(n_launches: int = 1000, device: int = 0, stream=None) -> dict:
+    """Empty-kernel launch cost in host microseconds: back to back, and launch + synchronise."""
+    a, b = C.c_double(), C.c_double()
+    _check(lib().mk_probe_launch(device, _stream_handle(stream), n_launches, C.byref(a), C.byref(b)))
+    return {"us_per_launch_pipelined": a.value, "us_per_launch_round_trip": b.value}
+
+
+def mk_probe_read(buf, repeats: int = 5, device: int = 0, stream=None) -> float:
+    """GB/s of nontemporal 16-byte reads over the CUDA tensor ``buf``."""
+    g = C.c_double()
+    _check(lib().mk_probe_read(device, _stream_handle(stream), C.c_void_p(buf.data_ptr()),
+                               buf.numel() * buf.element_size(), repeats, C.byref(g)))
+    return g.value
+
+
+def mk_probe_barrier(rounds: int = 1000, device: int = 0, stream=None) -> float:
+    """Microseconds per naive atomic grid barrier (one workgroup per CU)."""
+    u = C.c_double()
+    _check(lib().mk_probe_barrier(device, _stream_handle(stream), rounds, C.byref(u)))
+    return u.value
 
 
 def mk_rewind(ctx, pos: int) -> None:

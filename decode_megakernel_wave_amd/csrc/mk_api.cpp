@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <chrono>
 #include <string>
 #include <vector>
 
@@ -28,6 +29,11 @@ hipError_t mk_launch_gather(uint16_t* dst, const void* desc, int64_t n_chunks, h
 hipError_t mk_launch_count32(const uint32_t* p, int64_t n, uint32_t v, unsigned long long* out, hipStream_t s);
 hipError_t mk_launch_count_kv(const uint16_t* kc, const uint16_t* vc, int64_t rows, int max_seq, int hd, int p0, int p1,
                               unsigned long long* out, hipStream_t s);
+hipError_t mk_launch_probe_empty(hipStream_t s);
+hipError_t mk_launch_probe_read(const void* p, int64_t n16, void* sink, int grid, hipStream_t s);
+hipError_t mk_launch_probe_barrier(uint32_t* counter, int rounds, uint64_t deadline_ticks, uint64_t* out, int grid,
+                                   hipStream_t s);
+hipError_t mk_probe_barrier_occupancy(int* occupancy);
 }
 
 namespace {
@@ -924,6 +930,110 @@ void mk_chain_destroy(mk_chain* ch) {
   hipSetDevice(ch->g.device);
   ch->g.release();
   delete ch;
+}
+
+}  // extern "C"
+
+// ============================================================ calibration probes
+namespace {
+
+int probe_fail(int rc, const char* what, hipError_t e = hipSuccess) {
+  g_create_error = what;
+  if (e != hipSuccess) {
+    g_create_error += ": ";
+    g_create_error += hipGetErrorString(e);
+  }
+  return rc;
+}
+
+#define PROBE_HIP(call, what)                          \
+  do {                                                 \
+    hipError_t e_ = (call);                            \
+    if (e_ != hipSuccess) return probe_fail(MK_EHIP, what, e_); \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int mk_probe_launch(int device, void* hip_stream, int32_t n_launches, double* us_pipelined, double* us_round_trip) {
+  if (n_launches < 1 || !us_pipelined || !us_round_trip) return probe_fail(MK_EINVAL, "bad probe arguments");
+  g_create_error.clear();
+  hipStream_t s = (hipStream_t)hip_stream;
+  PROBE_HIP(hipSetDevice(device), "hipSetDevice");
+  PROBE_HIP(mk_launch_probe_empty(s), "empty launch");
+  PROBE_HIP(hipStreamSynchronize(s), "sync");
+  auto now = [] { return std::chrono::steady_clock::now(); };
+  auto t0 = now();
+  for (int i = 0; i < n_launches; ++i) PROBE_HIP(mk_launch_probe_empty(s), "empty launch");
+  PROBE_HIP(hipStreamSynchronize(s), "sync");
+  auto t1 = now();
+  for (int i = 0; i < n_launches; ++i) {
+    PROBE_HIP(mk_launch_probe_empty(s), "empty launch");
+    PROBE_HIP(hipStreamSynchronize(s), "sync");
+  }
+  auto t2 = now();
+  *us_pipelined = std::chrono::duration<double, std::micro>(t1 - t0).count() / n_launches;
+  *us_round_trip = std::chrono::duration<double, std::micro>(t2 - t1).count() / n_launches;
+  return MK_OK;
+}
+
+int mk_probe_read(int device, void* hip_stream, const void* buf, int64_t bytes, int32_t repeats, double* gb_per_s) {
+  if (!buf || bytes < 16 || bytes % 16 || ((uintptr_t)buf & 15) || repeats < 1 || !gb_per_s)
+    return probe_fail(MK_EINVAL, "bad probe arguments");
+  g_create_error.clear();
+  hipStream_t s = (hipStream_t)hip_stream;
+  PROBE_HIP(hipSetDevice(device), "hipSetDevice");
+  hipDeviceProp_t prop;
+  PROBE_HIP(hipGetDeviceProperties(&prop, device), "device properties");
+  const int grid = prop.multiProcessorCount * 8;
+  void* sink = nullptr;
+  PROBE_HIP(hipMalloc(&sink, (size_t)grid * 256 * 16), "sink allocation");
+  hipEvent_t a = nullptr, b = nullptr;
+  hipError_t e = hipEventCreate(&a);
+  if (e == hipSuccess) e = hipEventCreate(&b);
+  if (e == hipSuccess) e = mk_launch_probe_read(buf, bytes / 16, sink, grid, s);  // warm-up
+  if (e == hipSuccess) e = hipEventRecord(a, s);
+  for (int i = 0; i < repeats && e == hipSuccess; ++i) e = mk_launch_probe_read(buf, bytes / 16, sink, grid, s);
+  if (e == hipSuccess) e = hipEventRecord(b, s);
+  if (e == hipSuccess) e = hipEventSynchronize(b);
+  float ms = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
+  if (a) hipEventDestroy(a);
+  if (b) hipEventDestroy(b);
+  hipFree(sink);
+  if (e != hipSuccess) return probe_fail(MK_EHIP, "read probe", e);
+  *gb_per_s = (double)bytes * repeats / (ms * 1e-3) / 1e9;
+  return MK_OK;
+}
+
+int mk_probe_barrier(int device, void* hip_stream, int32_t rounds, double* us_per_barrier) {
+  if (rounds < 1 || rounds > 1000000 || !us_per_barrier) return probe_fail(MK_EINVAL, "bad probe arguments");
+  g_create_error.clear();
+  hipStream_t s = (hipStream_t)hip_stream;
+  PROBE_HIP(hipSetDevice(device), "hipSetDevice");
+  hipDeviceProp_t prop;
+  PROBE_HIP(hipGetDeviceProperties(&prop, device), "device properties");
+  int occ = 0;
+  PROBE_HIP(mk_probe_barrier_occupancy(&occ), "occupancy");
+  const int grid = prop.multiProcessorCount;  // one workgroup per CU, all resident
+  if (occ < 1) return probe_fail(MK_EOCC, "barrier probe does not fit a CU");
+  uint32_t* counter = nullptr;
+  uint64_t* out = nullptr;
+  PROBE_HIP(hipMalloc(&counter, 4), "counter allocation");
+  hipError_t e = hipMalloc(&out, 16);
+  if (e == hipSuccess) e = mk_launch_fill32(counter, 1, 0u, s);
+  if (e == hipSuccess) e = mk_launch_fill32((uint32_t*)out, 4, 0u, s);
+  if (e == hipSuccess) e = mk_launch_probe_barrier(counter, rounds, 100000000ull /* 1 s */, out, grid, s);
+  uint64_t h[2] = {0, 0};
+  if (e == hipSuccess) e = hipMemcpyAsync(h, out, 16, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  hipFree(counter);
+  if (out) hipFree(out);
+  if (e != hipSuccess) return probe_fail(MK_EHIP, "barrier probe", e);
+  if (h[1]) return probe_fail(MK_ETIMEOUT, "a barrier round did not complete within 1 s");
+  *us_per_barrier = (double)h[0] * 0.01 / rounds;  // 100 MHz device clock
+  return MK_OK;
 }
 
 }  // extern "C"

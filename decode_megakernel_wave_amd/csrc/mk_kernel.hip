@@ -1564,6 +1564,60 @@ __global__ void mk_count_kv(const uint16_t* kc, const uint16_t* vc, int64_t rows
   atomicAdd(out, cnt);
 }
 
+// ---------------------------------------------------------------- calibration probes
+// An empty kernel: launch overhead.
+__global__ void mk_probe_empty() {}
+
+// Stream n16 16-byte words with nontemporal loads, 8 in flight per thread; the
+// XOR of everything read goes to sink[thread] so no load can be dropped.
+__global__ __launch_bounds__(256) void mk_probe_read_k(const u4* __restrict__ p, int64_t n16, u4* __restrict__ sink) {
+  u4 acc = {0u, 0u, 0u, 0u};
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    u4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = __builtin_nontemporal_load(p + i + k * stride);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc ^= v[k];
+  }
+  for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(p + i);
+  sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
+// `rounds` naive grid barriers: every workgroup's first thread releases, adds 1
+// to one counter and polls it (system scope) until it reaches round x grid --
+// the pattern the atomic-counter path pays per stage.  Workgroup 0 records the
+// elapsed device-clock ticks in out[0]; a deadline ends every wait, and out[1]
+// is set when one expired.
+__global__ __launch_bounds__(64) void mk_probe_barrier_k(uint32_t* counter, int rounds, uint64_t deadline_ticks,
+                                                          uint64_t* out) {
+  __shared__ int failed;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) failed = 0;
+  __syncthreads();
+  for (int r = 0; r < rounds; ++r) {
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __hip_atomic_fetch_add(gp(counter), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      const uint32_t target = (uint32_t)(r + 1) * gridDim.x;
+      while (__hip_atomic_load(gp(counter), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) < target) {
+        if (__builtin_amdgcn_s_memrealtime() - t0 > deadline_ticks) {
+          failed = 1;
+          break;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+    if (failed) break;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    out[0] = __builtin_amdgcn_s_memrealtime() - t0;
+    out[1] = (uint64_t)failed;
+  }
+}
+
 // ---------------------------------------------------------------- host-side launch wrappers
 // Internal to the library (not part of the C ABI in include/mk.h).
 #define MK_INTERNAL __attribute__((visibility("hidden")))
@@ -1593,6 +1647,22 @@ MK_INTERNAL hipError_t mk_launch_gather(uint16_t* dst, const void* desc, int64_t
   if (n_chunks <= 0) return hipSuccess;
   hipLaunchKernelGGL(mk_gather, dim3(4096), dim3(256), 0, s, dst, (const GatherDesc*)desc, n_chunks);
   return hipGetLastError();
+}
+MK_INTERNAL hipError_t mk_launch_probe_empty(hipStream_t s) {
+  hipLaunchKernelGGL(mk_probe_empty, dim3(1), dim3(64), 0, s);
+  return hipGetLastError();
+}
+MK_INTERNAL hipError_t mk_launch_probe_read(const void* p, int64_t n16, void* sink, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(mk_probe_read_k, dim3(grid), dim3(256), 0, s, (const u4*)p, n16, (u4*)sink);
+  return hipGetLastError();
+}
+MK_INTERNAL hipError_t mk_launch_probe_barrier(uint32_t* counter, int rounds, uint64_t deadline_ticks, uint64_t* out,
+                                               int grid, hipStream_t s) {
+  hipLaunchKernelGGL(mk_probe_barrier_k, dim3(grid), dim3(64), 0, s, counter, rounds, deadline_ticks, out);
+  return hipGetLastError();
+}
+MK_INTERNAL hipError_t mk_probe_barrier_occupancy(int* occupancy) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, mk_probe_barrier_k, 64, 0);
 }
 MK_INTERNAL hipError_t mk_launch_count32(const uint32_t* p, int64_t n, uint32_t v, unsigned long long* out, hipStream_t s) {
   if (n <= 0) return hipSuccess;

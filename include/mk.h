@@ -233,6 +233,24 @@ typedef struct mk_plan_info {
   int32_t attn_splits;
 } mk_plan_info;
 
+/* Calibration probes: the launch cost, the practical HBM read ceiling and the naive grid
+ * barrier that "7 - AMD et le monokernel" (section 7.3) compares the NaN sentinel against.  Each runs on `hip_stream` of `device` and
+ * synchronises; errors: MK_EINVAL (arguments), MK_EHIP (HIP failure), MK_EOCC, MK_ETIMEOUT;
+ * text from mk_last_error(NULL).
+ * mk_probe_launch: n_launches empty-kernel launches back to back then one synchronisation
+ *   (host microseconds per launch -> *us_pipelined), and n_launches launch + synchronise
+ *   pairs (-> *us_round_trip).
+ * mk_probe_read: reads `bytes` (a multiple of 16, 16-byte aligned device buffer, borrowed)
+ *   `repeats` times with nontemporal 16-byte loads from 8 workgroups per CU; GB/s from HIP
+ *   events (one untimed warm-up pass first).
+ * mk_probe_barrier: `rounds` (1..1e6) grid barriers of one workgroup per CU, each a release,
+ *   an atomic add to one counter and system-scope polls until every workgroup has arrived;
+ *   microseconds per barrier on the device clock.  A round that does not complete within 1 s
+ *   ends every wait and returns MK_ETIMEOUT. */
+int mk_probe_launch(int device, void* hip_stream, int32_t n_launches, double* us_pipelined, double* us_round_trip);
+int mk_probe_read(int device, void* hip_stream, const void* buf, int64_t bytes, int32_t repeats, double* gb_per_s);
+int mk_probe_barrier(int device, void* hip_stream, int32_t rounds, double* us_per_barrier);
+
 /* Build the schedule for n_cta workgroups and check it: every consumed
  * unit has exactly one producer earlier in the step, counters match the
  * producer counts, every wave's stream is consistent.  Returns MK_OK or
