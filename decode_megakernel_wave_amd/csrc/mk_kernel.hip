@@ -203,6 +203,13 @@ __device__ __forceinline__ float poll_f32(Cx& c, const float* p, int op, int lay
   return __uint_as_float(v);
 }
 
+__device__ __forceinline__ bool any_sent16(u4 v) {
+  bool any = false;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) any |= (v[j] & 0xFFFFu) == kSent16 || (v[j] >> 16) == kSent16;
+  return any;
+}
+
 __device__ __forceinline__ bool any_sent(u4 v) {
   return v[0] == kSent32 || v[1] == kSent32 || v[2] == kSent32 || v[3] == kSent32;
 }
@@ -663,6 +670,7 @@ __device__ __forceinline__ void att_pos_core(Cx& c, int l, int g, int sp, int j0
       }
     }
   }
+  ts_mark(c, 5);
   // combine the wavefronts: scratch [wave][ng][hd + 2]
   float* scr = c.sm.scratch;
   const int rec = hd + 2;
@@ -678,6 +686,7 @@ __device__ __forceinline__ void att_pos_core(Cx& c, int l, int g, int sp, int j0
     }
   }
   cta_sync(c);
+  ts_mark(c, 7);
   for (int i = c.tid; i < ng * hd; i += kThreads) {
     const int j = i / hd, dd = i % hd;
     float M = -INFINITY;
@@ -882,20 +891,29 @@ __device__ __forceinline__ void att_stage(Cx& c, int l, int g, bool has_cur, boo
       *(f4*)(qs + i) = f4{__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3])} * qscale;
     }
   }
-  if (has_cur && c.tid < 2 * hd) {
-    const int i = c.tid % hd;
-    const uint16_t* src = (c.tid < hd ? kp.kc : kp.vc) + (((int64_t)l * kp.nkv + g) * kp.max_seq + c.pos) * hd + i;
-    uint16_t v = ldc16(src);
+  if (has_cur && c.tid < hd / 4) {
+    // 16-byte polls (8 fp16 values, each checked for the fp16 sentinel): lanes
+    // [0, hd/8) read the K row, [hd/8, hd/4) the V row
+    const bool isk = c.tid < hd / 8;
+    const int i8 = (isk ? c.tid : c.tid - hd / 8) * 8;
+    const int64_t row = (((int64_t)l * kp.nkv + g) * kp.max_seq + c.pos) * hd;
+    const Rsrc rk = sync_rsrc(kp.kc + row, (uint32_t)hd * 2u), rv = sync_rsrc(kp.vc + row, (uint32_t)hd * 2u);
+    u4 v = isk ? ldc128(rk, (uint32_t)i8 * 2u) : ldc128(rv, (uint32_t)i8 * 2u);
     if (sentinel_mode(c)) {
-      while (v == kSent16 && !c.fail) {
-        if (expired(c, OP_ATT, l, i)) {
+      while (any_sent16(v) && !c.fail) {
+        if (expired(c, OP_ATT, l, i8)) {
           c.fail = true;
           break;
         }
-        v = ldc16(src);
+        v = isk ? ldc128(rk, (uint32_t)i8 * 2u) : ldc128(rv, (uint32_t)i8 * 2u);
       }
     }
-    (c.tid < hd ? kcur : vcur)[i] = (float)__builtin_bit_cast(_Float16, v);
+    float* dst = (isk ? kcur : vcur) + i8;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      dst[2 * j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[j] & 0xFFFFu));
+      dst[2 * j + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[j] >> 16));
+    }
   }
   ts_mark(c, 1);
   cta_sync(c);
