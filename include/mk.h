@@ -121,12 +121,13 @@ int mk_create(const mk_config* cfg, const mk_options* opts, int device, void* hi
 int mk_load_weights(mk_ctx* ctx, const mk_weights* w);
 
 /* Run the prompt ids[0..n) (host) at positions 0..n-1 through the monokernel,
- * token by token, filling the KV cache; *t0_out = greedy token after the
- * prompt.  Resets the generation state.  Synchronises. */
+ * token by token, filling the KV cache; *t0_out = the token chosen after the
+ * prompt (greedy, or drawn when sampling is on: mk_set_sampling).  Resets the
+ * generation state.  Synchronises. */
 int mk_prefill(mk_ctx* ctx, const int32_t* ids, int32_t n, int32_t* t0_out);
 
-/* Decode n_steps greedy tokens in ONE launch.  Step s consumes the previous
- * token at position pos+s.  tokens_out (host, n_steps) receives the tokens;
+/* Decode n_steps tokens (greedy, or drawn when sampling is on) in ONE launch.
+ * Step s consumes the previous token at position pos+s.  tokens_out (host, n_steps) receives the tokens;
  * logits_out (host, n_steps*vocab floats, or NULL) receives every step's
  * logits.  Synchronises. */
 int mk_decode(mk_ctx* ctx, int32_t n_steps, int32_t* tokens_out, float* logits_out);
