@@ -279,6 +279,7 @@ def main() -> int:
     wall = time.perf_counter() - t_start
     sent = mk.mk_count_sentinels(ctx)
     stats = mk.mk_get_stats(ctx)
+    kernel_name = mk.mk_kernel_name(ctx)
     mk.mk_destroy(ctx)
     sync_latency = None
     if args.trace_steps > 0:
@@ -288,7 +289,8 @@ def main() -> int:
     achieved = float(np.mean(algo)) / (mean_ms * 1e-3) / 1e9
     traffic = measured_traffic(args.workload, n, {"grid": stats["grid"], "block": stats["block"],
                                                   "lds_bytes": stats["lds_bytes"], "ring_depth": stats["ring_depth"],
-                                                  "sync": args.sync, "xcd_replicas": args.replicas})
+                                                  "sync": args.sync, "xcd_replicas": args.replicas,
+                                                  "kernel": kernel_name})
     out = {
         "metric": "batch-1 decode tokens/s per request on 1 MI355X; achieved HBM TB/s of 8",
         "value": n * args.steps / wall,
@@ -315,7 +317,7 @@ def main() -> int:
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "traffic_read_write": [traffic["fetch_bytes_per_launch"], traffic["write_bytes_per_launch"]]
                      if traffic else None,
-                     "kernel": "mk_monokernel", "kernel_ms": mean_ms,
+                     "kernel": kernel_name, "kernel_ms": mean_ms,
                      "algo_bytes_per_launch": float(np.mean(algo))},
         "kernel_tokens_per_s": n / mean_ms * 1e3,
         "prefill": {"prompt_len": P, "gpu_ms": prefill_ms, "note": "untimed setup: the prompt runs through the "

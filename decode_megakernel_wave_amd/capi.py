@@ -79,6 +79,7 @@ SIGNATURES = [
     ("mk_generate", C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.c_int32, C.c_int32, C.POINTER(C.c_int32)]),
     ("mk_rewind", C.c_int, [C.c_void_p, C.c_int32]),
     ("mk_set_sampling", C.c_int, [C.c_void_p, C.c_int32, C.c_float, C.c_uint64]),
+    ("mk_kernel_name", C.c_char_p, [C.c_void_p]),
     ("mk_probe_launch", C.c_int, [C.c_int, C.c_void_p, C.c_int32, C.POINTER(C.c_double), C.POINTER(C.c_double)]),
     ("mk_probe_read", C.c_int, [C.c_int, C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.POINTER(C.c_double)]),
     ("mk_probe_barrier", C.c_int, [C.c_int, C.c_void_p, C.c_int32, C.POINTER(C.c_double)]),
@@ -227,6 +228,11 @@ def mk_generate(ctx, ids, n_steps: int) -> np.ndarray:
     _check(lib().mk_generate(ctx, ids.ctypes.data_as(C.POINTER(C.c_int32)), len(ids), n_steps,
                              out.ctypes.data_as(C.POINTER(C.c_int32))), ctx)
     return out
+
+
+def mk_kernel_name(ctx) -> str:
+    """The monokernel the context launches (specialised or general)."""
+    return (lib().mk_kernel_name(ctx) or b"").decode()
 
 
 def mk_set_sampling(ctx, top_k: int = 1, temperature: float = 1.0, seed: int = 0) -> None:

@@ -23,6 +23,8 @@ using namespace mk;
 extern "C" {
 hipError_t mk_launch_monokernel(const KParams* kp_dev, int grid, int lds_bytes, hipStream_t s);
 hipError_t mk_kernel_attributes(int lds_bytes, int* occupancy);
+hipError_t mk_launch_monokernel_w4h128(const KParams* kp_dev, int grid, int lds_bytes, hipStream_t s);
+hipError_t mk_kernel_attributes_w4h128(int lds_bytes, int* occupancy);
 hipError_t mk_launch_fill32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 hipError_t mk_launch_fill_kv(uint16_t* kc, uint16_t* vc, int64_t rows, int max_seq, int hd, int p0, int p1, hipStream_t s);
 hipError_t mk_launch_gather(uint16_t* dst, const void* desc, int64_t n_chunks, hipStream_t s);
@@ -55,6 +57,7 @@ struct Engine {
   mk_options opt{};
   Plan plan;
   int n_cu = 0, occ = 0, grid = 0;
+  bool spec = false;  // every instruction fits the kernel specialised to 4-chunk slices and head_dim 128
   std::string err;
   // device buffers
   uint8_t* d_stream = nullptr;
@@ -149,6 +152,9 @@ int engine_setup(Engine& g, int device, void* stream, const mk_options* opts, in
   g.n_cu = prop.multiProcessorCount;
   if (lds_bytes > (int)prop.sharedMemPerBlock) return g.fail(MK_EOCC, "LDS footprint exceeds the per-workgroup limit");
   HIPCHK(g, mk_kernel_attributes(lds_bytes, &g.occ));
+  int occ_spec = 0;
+  HIPCHK(g, mk_kernel_attributes_w4h128(lds_bytes, &occ_spec));
+  g.occ = std::min(g.occ, occ_spec);  // either kernel may run this grid
   if (g.occ < 1) return g.fail(MK_EOCC, "the monokernel does not fit on a CU (occupancy 0)");
   const int wave = g.n_cu * g.occ;
   g.grid = g.opt.grid > 0 ? g.opt.grid : wave;
@@ -158,8 +164,21 @@ int engine_setup(Engine& g, int device, void* stream, const mk_options* opts, in
   return MK_OK;
 }
 
+// True when the kernel specialised to 4-chunk GEMV slices and head_dim 128 runs
+// every instruction of the plan exactly as the general one does.
+bool fits_specialised(const Plan& p) {
+  if (!p.dm.chain && p.dm.hd != 128) return false;
+  for (const Ins& in : p.ins) {
+    const bool gemv = in.op == OP_QKV || in.op == OP_OPROJ || in.op == OP_UPGATE || in.op == OP_DOWN ||
+                      in.op == OP_LMHEAD || in.op == OP_CHAIN;
+    if (gemv && in.cps != 4) return false;
+  }
+  return true;
+}
+
 int upload_plan(Engine& g) {
   const Plan& p = g.plan;
+  g.spec = fits_specialised(p);
   CHK(g.alloc(&g.d_ins, p.ins.size() * sizeof(Ins)));
   CHK(g.alloc(&g.d_ins_off, p.ins_off.size() * sizeof(int32_t)));
   CHK(g.alloc(&g.d_wave_off, p.wave_off.size() * sizeof(int64_t)));
@@ -241,7 +260,10 @@ int launch(Engine& g, KParams& k, int n_steps) {
   g.h_kp = k;
   HIPCHK(g, hipMemcpyAsync(g.d_kp, &g.h_kp, sizeof(KParams), hipMemcpyHostToDevice, g.stream));
   HIPCHK(g, hipEventRecord(g.ev0, g.stream));
-  HIPCHK(g, mk_launch_monokernel(g.d_kp, g.grid, g.plan.lds_bytes, g.stream));
+  // MK_GENERAL_KERNEL=1 forces the general kernel (comparison runs)
+  const bool spec = g.spec && !getenv("MK_GENERAL_KERNEL");
+  HIPCHK(g, spec ? mk_launch_monokernel_w4h128(g.d_kp, g.grid, g.plan.lds_bytes, g.stream)
+                 : mk_launch_monokernel(g.d_kp, g.grid, g.plan.lds_bytes, g.stream));
   HIPCHK(g, hipEventRecord(g.ev1, g.stream));
   HIPCHK(g, hipStreamSynchronize(g.stream));
   float ms = 0.f;
@@ -677,6 +699,11 @@ int mk_generate(mk_ctx* c, const int32_t* ids, int32_t n_prompt, int32_t n_steps
   int rc = mk_prefill(c, ids, n_prompt, tokens_out);
   if (rc != MK_OK || n_steps == 0) return rc;
   return mk_decode(c, n_steps, tokens_out + 1, nullptr);
+}
+
+const char* mk_kernel_name(const mk_ctx* c) {
+  if (!c) return "";
+  return c->g.spec && !getenv("MK_GENERAL_KERNEL") ? "mk_monokernel_w4h128" : "mk_monokernel";
 }
 
 int mk_set_sampling(mk_ctx* c, int32_t top_k, float temperature, uint64_t seed) {

@@ -38,6 +38,20 @@
 #include "mk_device.h"
 #include "mk_layout.h"
 
+// The file is compiled twice.  The general build holds mk_monokernel (every
+// slice width and head_dim) and the helper kernels.  With MK_SPECIALIZED it
+// holds only mk_monokernel_w4h128: the same interpreter restricted to GEMV
+// slices of four chunks (rows of 2048 or more columns) and head_dim 128, the
+// ~2B decoder's shapes.  Leaving the other widths and head geometries out of
+// the kernel's code made the ~2B decode about 3 % faster (the interpreter's
+// code is several times larger than the instruction cache); the host picks
+// the specialised kernel when every instruction of the schedule fits it.
+#ifdef MK_SPECIALIZED
+#define MK_MONOKERNEL mk_monokernel_w4h128
+#else
+#define MK_MONOKERNEL mk_monokernel
+#endif
+
 using namespace mk;
 
 namespace {
@@ -366,16 +380,33 @@ __device__ __forceinline__ bool staged_rows(const Ins& in) {
 }
 
 // ---------------------------------------------------------------- GEMV core
+// The next n (1..4, uniform) chunks of the ring.
+__device__ __forceinline__ void ring_read_n(Ring& ring, u4 (&w)[4], int n) {
+  switch (n) {
+    case 4: ring_read<4>(ring, w); break;
+    case 3: ring_read<3>(ring, w); break;
+    case 2: ring_read<2>(ring, w); break;
+    default: ring_read<1>(ring, w); break;
+  }
+}
+
+// GEMV body.  CPS = 4: slices of four chunks, the widest and the common case
+// (rows of 2048 or more columns); CPS = 0: any width in.cps = 1..4 with
+// uniform guards on the chunk loops.  Two bodies per op instead of one per
+// width: the monokernel's code is far larger than the instruction cache.
 template <int CPS, typename Epi>
 __device__ __forceinline__ void gemv(Cx& c, Ring& ring, const Ins& in, const float* vec, float scale, Epi epi) {
   const int ks = in.ks, rg = kWaves / ks, ki = c.wave % ks, gi = c.wave / ks;
-  const int upr = in.upr;
-  float act[CPS][8];
-  const int col0 = ki * CPS * kChunkHalfs + c.lane * 8;
+  const int upr = in.upr, cps = CPS ? CPS : in.cps;
+  float act[4][8];
+  const int col0 = ki * cps * kChunkHalfs + c.lane * 8;
 #pragma unroll
-  for (int k = 0; k < CPS; ++k) {
-    const f4 a = *(const f4*)(vec + col0 + k * kChunkHalfs);
-    const f4 b = *(const f4*)(vec + col0 + k * kChunkHalfs + 4);
+  for (int k = 0; k < 4; ++k) {
+    f4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+    if (CPS || k < cps) {
+      a = *(const f4*)(vec + col0 + k * kChunkHalfs);
+      b = *(const f4*)(vec + col0 + k * kChunkHalfs + 4);
+    }
     act[k][0] = a[0]; act[k][1] = a[1]; act[k][2] = a[2]; act[k][3] = a[3];
     act[k][4] = b[0]; act[k][5] = b[1]; act[k][6] = b[2]; act[k][7] = b[3];
 #pragma unroll
@@ -385,14 +416,18 @@ __device__ __forceinline__ void gemv(Cx& c, Ring& ring, const Ins& in, const flo
   for (int u = gi; u < in.nu; u += rg) {
     float r0 = 0.f, r1 = 0.f;
     u4 w[4];
-    ring_read<CPS>(ring, w);
+    if constexpr (CPS > 0) ring_read<CPS>(ring, w);
+    else ring_read_n(ring, w, cps);
     if (u == gi) ts_mark(c, 7);
 #pragma unroll
-    for (int k = 0; k < CPS; ++k) r0 += dot8(w[k], act[k]);
+    for (int k = 0; k < 4; ++k)
+      if (CPS ? k < CPS : k < cps) r0 += dot8(w[k], act[k]);
     if (upr == 2) {
-      ring_read<CPS>(ring, w);
+      if constexpr (CPS > 0) ring_read<CPS>(ring, w);
+      else ring_read_n(ring, w, cps);
 #pragma unroll
-      for (int k = 0; k < CPS; ++k) r1 += dot8(w[k], act[k]);
+      for (int k = 0; k < 4; ++k)
+        if (CPS ? k < CPS : k < cps) r1 += dot8(w[k], act[k]);
     }
     r0 = wave_sum(r0);
     if (upr == 2) r1 = wave_sum(r1);
@@ -433,12 +468,12 @@ __device__ __forceinline__ void gemv(Cx& c, Ring& ring, const Ins& in, const flo
 
 template <typename Epi>
 __device__ __forceinline__ void gemv_dispatch(Cx& c, Ring& ring, const Ins& in, const float* vec, float scale, Epi epi) {
-  switch (in.cps) {
-    case 1: gemv<1>(c, ring, in, vec, scale, epi); break;
-    case 2: gemv<2>(c, ring, in, vec, scale, epi); break;
-    case 3: gemv<3>(c, ring, in, vec, scale, epi); break;
-    default: gemv<4>(c, ring, in, vec, scale, epi); break;
-  }
+#ifdef MK_SPECIALIZED
+  gemv<4>(c, ring, in, vec, scale, epi);
+#else
+  if (in.cps == 4) gemv<4>(c, ring, in, vec, scale, epi);
+  else gemv<0>(c, ring, in, vec, scale, epi);
+#endif
 }
 
 // Closes the staging of an instruction's inputs: barrier, trace mark and,
@@ -991,16 +1026,25 @@ __device__ __forceinline__ void op_att(Cx& c, const Ins& in) {
     if (t1 - t0 <= kPosBatch * kWaves) {
       // short split (a few positions per wavefront): one position per wavefront per step
       const int dpl = hd / 64;
+#ifdef MK_SPECIALIZED
+      (void)dpl;
+      att_short<4, 2>(c, l, g, sp, t0, t1, G, has_cur, ui == 0);
+#else
       if (dpl == 1) att_short<8, 1>(c, l, g, sp, t0, t1, G, has_cur, ui == 0);
       else if (dpl == 2) att_short<4, 2>(c, l, g, sp, t0, t1, G, has_cur, ui == 0);
       else att_short<2, 4>(c, l, g, sp, t0, t1, G, has_cur, ui == 0);
+#endif
     } else {
       // (no prefetch of the split's K/V rows before the wait: pulling them
       // towards L2 first was measured slower at 2048 and 8192 positions)
       att_stage(c, l, g, has_cur, ui == 0);
+#ifdef MK_SPECIALIZED
+      att_heads<128>(c, l, g, sp, t0, t1, G);
+#else
       if (hd == 64) att_heads<64>(c, l, g, sp, t0, t1, G);
       else if (hd == 128) att_heads<128>(c, l, g, sp, t0, t1, G);
       else att_heads<256>(c, l, g, sp, t0, t1, G);
+#endif
     }
     ts_mark(c, 6);
     if (!sentinel_mode(c)) {
@@ -1423,7 +1467,7 @@ __device__ __forceinline__ void op_chain(Cx& c, Ring& ring, const Ins& in) {
 
 }  // namespace
 
-__global__ __launch_bounds__(kThreads, 1) void mk_monokernel(const KParams* __restrict__ kpp) {
+__global__ __launch_bounds__(kThreads, 1) void MK_MONOKERNEL(const KParams* __restrict__ kpp) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const KParams& kp = *kpp;
   Cx c;
@@ -1523,6 +1567,7 @@ done:
   asm volatile("s_waitcnt vmcnt(0)");
 }
 
+#ifndef MK_SPECIALIZED
 // ---------------------------------------------------------------- helper kernels
 // Fill n 32-bit words with a value.
 __global__ void mk_fill32(uint32_t* p, int64_t n, uint32_t v) {
@@ -1638,7 +1683,22 @@ __global__ __launch_bounds__(64) void mk_probe_barrier_k(uint32_t* counter, int 
 
 // ---------------------------------------------------------------- host-side launch wrappers
 // Internal to the library (not part of the C ABI in include/mk.h).
+#endif  // !MK_SPECIALIZED
+
 #define MK_INTERNAL __attribute__((visibility("hidden")))
+#ifdef MK_SPECIALIZED
+extern "C" {
+MK_INTERNAL hipError_t mk_launch_monokernel_w4h128(const KParams* kp_dev, int grid, int lds_bytes, hipStream_t s) {
+  hipLaunchKernelGGL(mk_monokernel_w4h128, dim3(grid), dim3(kThreads), lds_bytes, s, kp_dev);
+  return hipGetLastError();
+}
+MK_INTERNAL hipError_t mk_kernel_attributes_w4h128(int lds_bytes, int* occupancy) {
+  hipError_t e = hipFuncSetAttribute((const void*)mk_monokernel_w4h128, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+  if (e != hipSuccess) return e;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, mk_monokernel_w4h128, kThreads, lds_bytes);
+}
+}
+#else
 extern "C" {
 // kp_dev: the parameters, already copied to device memory.
 MK_INTERNAL hipError_t mk_launch_monokernel(const KParams* kp_dev, int grid, int lds_bytes, hipStream_t s) {
@@ -1694,3 +1754,4 @@ MK_INTERNAL hipError_t mk_launch_count_kv(const uint16_t* kc, const uint16_t* vc
   return hipGetLastError();
 }
 }
+#endif  // MK_SPECIALIZED

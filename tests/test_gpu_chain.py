@@ -53,3 +53,13 @@ def test_chain_full_256_stages_both_sync_modes():
     assert np.array_equal(ys.view(np.uint32), yc.view(np.uint32))
     print("chain 256x2048^2: sentinel %.3f ms (%.2f us/stage), counter %.3f ms (%.2f us/stage)"
           % (sts["gpu_ms"], sts["gpu_ms"] * 1e3 / 256, stc["gpu_ms"], stc["gpu_ms"] * 1e3 / 256))
+
+
+def test_chain_specialised_kernel_equals_general(monkeypatch):
+    """2048-wide stages run on the specialised kernel; the general one gives the same bits."""
+    W = inputs.make_chain_weights(n=2048, stages=16, seed=5)
+    x0 = inputs.make_chain_x0(2048, seed=6)
+    ys, _ = _run(W, x0)
+    monkeypatch.setenv("MK_GENERAL_KERNEL", "1")
+    yg, _ = _run(W, x0)
+    assert np.array_equal(ys.view(np.uint32), yg.view(np.uint32))

@@ -108,3 +108,27 @@ def test_2b_topk_sampling(w2b):
             assert int(toks[s]) == want, f"step {s}: GPU drew {toks[s]}, oracle {want}"
             compared += 1
     assert compared >= n - 1
+
+
+def test_2b_specialised_kernel_equals_general(w2b, monkeypatch):
+    """The ~2B schedule runs on the kernel specialised to 4-chunk slices and head_dim 128; the
+    general kernel gives bitwise the same logits and tokens."""
+    P, n = 16, 4
+    ids = inputs.make_prompt(inputs.M2B, P, seed=1)
+    ctx = mk.mk_create(inputs.M2B, max_seq=P + n + 1)
+    try:
+        wd = mk.to_device(w2b)
+        mk.mk_load_weights(ctx, wd)
+        del wd
+        assert mk.mk_kernel_name(ctx) == "mk_monokernel_w4h128"
+        mk.mk_prefill(ctx, ids)
+        a_tok, a_log = mk.mk_decode(ctx, n, vocab=inputs.M2B.vocab)
+        monkeypatch.setenv("MK_GENERAL_KERNEL", "1")
+        assert mk.mk_kernel_name(ctx) == "mk_monokernel"
+        mk.mk_prefill(ctx, ids)
+        b_tok, b_log = mk.mk_decode(ctx, n, vocab=inputs.M2B.vocab)
+    finally:
+        mk.mk_destroy(ctx)
+        torch.cuda.empty_cache()
+    assert np.array_equal(a_tok, b_tok)
+    assert np.array_equal(a_log.view(np.uint32), b_log.view(np.uint32))

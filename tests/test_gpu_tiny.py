@@ -127,3 +127,13 @@ def test_tiny_several_splits_per_workgroup(tiny):
             err = check_step_logits(logits, logs_ref, toks, toks_ref)
             print(f"grid {g} splits {s} mode {mode}: max |dlogit| {err:.2e}")
             assert sent == 0
+
+
+def test_tiny_runs_the_general_kernel():
+    """head_dim 64 and one-chunk rows do not fit the specialised kernel."""
+    w = inputs.make_weights(CFG, seed=0)
+    ctx = load(mk, CFG, w, P + 2)
+    try:
+        assert mk.mk_kernel_name(ctx) == "mk_monokernel"
+    finally:
+        mk.mk_destroy(ctx)
