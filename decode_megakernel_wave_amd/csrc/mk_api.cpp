@@ -25,6 +25,8 @@ hipError_t mk_launch_monokernel(const KParams* kp_dev, int grid, int lds_bytes, 
 hipError_t mk_kernel_attributes(int lds_bytes, int* occupancy);
 hipError_t mk_launch_monokernel_w4h128(const KParams* kp_dev, int grid, int lds_bytes, hipStream_t s);
 hipError_t mk_kernel_attributes_w4h128(int lds_bytes, int* occupancy);
+hipError_t mk_launch_monokernel_w4h128_ctr(const KParams* kp_dev, int grid, int lds_bytes, hipStream_t s);
+hipError_t mk_kernel_attributes_w4h128_ctr(int lds_bytes, int* occupancy);
 hipError_t mk_launch_fill32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 hipError_t mk_launch_fill_kv(uint16_t* kc, uint16_t* vc, int64_t rows, int max_seq, int hd, int p0, int p1, hipStream_t s);
 hipError_t mk_launch_gather(uint16_t* dst, const void* desc, int64_t n_chunks, hipStream_t s);
@@ -152,9 +154,10 @@ int engine_setup(Engine& g, int device, void* stream, const mk_options* opts, in
   g.n_cu = prop.multiProcessorCount;
   if (lds_bytes > (int)prop.sharedMemPerBlock) return g.fail(MK_EOCC, "LDS footprint exceeds the per-workgroup limit");
   HIPCHK(g, mk_kernel_attributes(lds_bytes, &g.occ));
-  int occ_spec = 0;
+  int occ_spec = 0, occ_ctr = 0;
   HIPCHK(g, mk_kernel_attributes_w4h128(lds_bytes, &occ_spec));
-  g.occ = std::min(g.occ, occ_spec);  // either kernel may run this grid
+  HIPCHK(g, mk_kernel_attributes_w4h128_ctr(lds_bytes, &occ_ctr));
+  g.occ = std::min(g.occ, std::min(occ_spec, occ_ctr));  // any of the kernels may run this grid
   if (g.occ < 1) return g.fail(MK_EOCC, "the monokernel does not fit on a CU (occupancy 0)");
   const int wave = g.n_cu * g.occ;
   g.grid = g.opt.grid > 0 ? g.opt.grid : wave;
@@ -262,8 +265,9 @@ int launch(Engine& g, KParams& k, int n_steps) {
   HIPCHK(g, hipEventRecord(g.ev0, g.stream));
   // MK_GENERAL_KERNEL=1 forces the general kernel (comparison runs)
   const bool spec = g.spec && !getenv("MK_GENERAL_KERNEL");
-  HIPCHK(g, spec ? mk_launch_monokernel_w4h128(g.d_kp, g.grid, g.plan.lds_bytes, g.stream)
-                 : mk_launch_monokernel(g.d_kp, g.grid, g.plan.lds_bytes, g.stream));
+  if (!spec) HIPCHK(g, mk_launch_monokernel(g.d_kp, g.grid, g.plan.lds_bytes, g.stream));
+  else if (g.plan.sync_mode == 0) HIPCHK(g, mk_launch_monokernel_w4h128(g.d_kp, g.grid, g.plan.lds_bytes, g.stream));
+  else HIPCHK(g, mk_launch_monokernel_w4h128_ctr(g.d_kp, g.grid, g.plan.lds_bytes, g.stream));
   HIPCHK(g, hipEventRecord(g.ev1, g.stream));
   HIPCHK(g, hipStreamSynchronize(g.stream));
   float ms = 0.f;
@@ -703,7 +707,8 @@ int mk_generate(mk_ctx* c, const int32_t* ids, int32_t n_prompt, int32_t n_steps
 
 const char* mk_kernel_name(const mk_ctx* c) {
   if (!c) return "";
-  return c->g.spec && !getenv("MK_GENERAL_KERNEL") ? "mk_monokernel_w4h128" : "mk_monokernel";
+  if (!c->g.spec || getenv("MK_GENERAL_KERNEL")) return "mk_monokernel";
+  return c->g.plan.sync_mode == 0 ? "mk_monokernel_w4h128" : "mk_monokernel_w4h128_ctr";
 }
 
 int mk_set_sampling(mk_ctx* c, int32_t top_k, float temperature, uint64_t seed) {

@@ -38,16 +38,26 @@
 #include "mk_device.h"
 #include "mk_layout.h"
 
-// The file is compiled twice.  The general build holds mk_monokernel (every
-// slice width and head_dim) and the helper kernels.  With MK_SPECIALIZED it
-// holds only mk_monokernel_w4h128: the same interpreter restricted to GEMV
-// slices of four chunks (rows of 2048 or more columns) and head_dim 128, the
-// ~2B decoder's shapes.  Leaving the other widths and head geometries out of
-// the kernel's code made the ~2B decode about 3 % faster (the interpreter's
-// code is several times larger than the instruction cache); the host picks
-// the specialised kernel when every instruction of the schedule fits it.
+// The file is compiled three times.  The general build holds mk_monokernel
+// (every slice width, head_dim and sync mode) and the helper kernels.  With
+// MK_SPECIALIZED it holds only one specialised interpreter, restricted to GEMV
+// slices of four chunks (rows of 2048 or more columns), head_dim 128 (the ~2B
+// decoder's shapes) and one sync mode fixed at compile time (MK_SPEC_SYNC 0:
+// sentinel, mk_monokernel_w4h128; 1: counter, mk_monokernel_w4h128_ctr).
+// Leaving the other widths, head geometries and the other sync mode out of
+// the kernel's code made the ~2B decode about 5 % faster (the interpreter's
+// code is several times larger than the instruction cache); the host picks a
+// specialised kernel when every instruction of the schedule fits it.
 #ifdef MK_SPECIALIZED
+#if MK_SPEC_SYNC == 0
 #define MK_MONOKERNEL mk_monokernel_w4h128
+#define MK_SPEC_LAUNCH mk_launch_monokernel_w4h128
+#define MK_SPEC_ATTR mk_kernel_attributes_w4h128
+#else
+#define MK_MONOKERNEL mk_monokernel_w4h128_ctr
+#define MK_SPEC_LAUNCH mk_launch_monokernel_w4h128_ctr
+#define MK_SPEC_ATTR mk_kernel_attributes_w4h128_ctr
+#endif
 #else
 #define MK_MONOKERNEL mk_monokernel
 #endif
@@ -168,7 +178,11 @@ __device__ __forceinline__ void mark_ready(Cx& c) {
 }
 
 // Counter mode: one thread waits until the stage counter reaches its target.
+#ifdef MK_SPECIALIZED
+__device__ __forceinline__ bool sentinel_mode(const Cx&) { return MK_SPEC_SYNC == 0; }
+#else
 __device__ __forceinline__ bool sentinel_mode(const Cx& c) { return c.kp->sync_mode == 0; }
+#endif
 
 __device__ __forceinline__ void counter_wait(Cx& c, int sid, int n_in, int op, int layer) {
   if (sentinel_mode(c)) return;
@@ -1688,14 +1702,14 @@ __global__ __launch_bounds__(64) void mk_probe_barrier_k(uint32_t* counter, int 
 #define MK_INTERNAL __attribute__((visibility("hidden")))
 #ifdef MK_SPECIALIZED
 extern "C" {
-MK_INTERNAL hipError_t mk_launch_monokernel_w4h128(const KParams* kp_dev, int grid, int lds_bytes, hipStream_t s) {
-  hipLaunchKernelGGL(mk_monokernel_w4h128, dim3(grid), dim3(kThreads), lds_bytes, s, kp_dev);
+MK_INTERNAL hipError_t MK_SPEC_LAUNCH(const KParams* kp_dev, int grid, int lds_bytes, hipStream_t s) {
+  hipLaunchKernelGGL(MK_MONOKERNEL, dim3(grid), dim3(kThreads), lds_bytes, s, kp_dev);
   return hipGetLastError();
 }
-MK_INTERNAL hipError_t mk_kernel_attributes_w4h128(int lds_bytes, int* occupancy) {
-  hipError_t e = hipFuncSetAttribute((const void*)mk_monokernel_w4h128, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+MK_INTERNAL hipError_t MK_SPEC_ATTR(int lds_bytes, int* occupancy) {
+  hipError_t e = hipFuncSetAttribute((const void*)MK_MONOKERNEL, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   if (e != hipSuccess) return e;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, mk_monokernel_w4h128, kThreads, lds_bytes);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, MK_MONOKERNEL, kThreads, lds_bytes);
 }
 }
 #else

@@ -159,8 +159,9 @@ int mk_generate(mk_ctx* ctx, const int32_t* ids, int32_t n_prompt, int32_t n_ste
 int mk_set_sampling(mk_ctx* ctx, int32_t top_k, float temperature, uint64_t seed);
 
 /* Name of the monokernel the context's launches run: "mk_monokernel_w4h128"
- * (specialised to GEMV slices of four 512-column chunks and head_dim 128, used
- * when every instruction of the schedule fits it) or "mk_monokernel" (general).
+ * or, in counter sync mode, "mk_monokernel_w4h128_ctr" (specialised to GEMV
+ * slices of four 512-column chunks, head_dim 128 and the sync mode, used when
+ * every instruction of the schedule fits it) or "mk_monokernel" (general).
  * Both compute the same results; the environment variable MK_GENERAL_KERNEL
  * forces the general one.  "" for a NULL context.  The string is static. */
 const char* mk_kernel_name(const mk_ctx* ctx);
