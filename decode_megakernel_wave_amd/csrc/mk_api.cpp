@@ -167,10 +167,11 @@ int engine_setup(Engine& g, int device, void* stream, const mk_options* opts, in
   return MK_OK;
 }
 
-// True when the kernel specialised to 4-chunk GEMV slices and head_dim 128 runs
+// True when the kernel specialised to 4-chunk GEMV slices, head_dim 128 and two
+// query heads per kv head runs
 // every instruction of the plan exactly as the general one does.
 bool fits_specialised(const Plan& p) {
-  if (!p.dm.chain && p.dm.hd != 128) return false;
+  if (!p.dm.chain && (p.dm.hd != 128 || p.dm.nq != 2 * p.dm.nkv)) return false;
   for (const Ins& in : p.ins) {
     const bool gemv = in.op == OP_QKV || in.op == OP_OPROJ || in.op == OP_UPGATE || in.op == OP_DOWN ||
                       in.op == OP_LMHEAD || in.op == OP_CHAIN;

@@ -41,13 +41,21 @@
 // The file is compiled three times.  The general build holds mk_monokernel
 // (every slice width, head_dim and sync mode) and the helper kernels.  With
 // MK_SPECIALIZED it holds only one specialised interpreter, restricted to GEMV
-// slices of four chunks (rows of 2048 or more columns), head_dim 128 (the ~2B
-// decoder's shapes) and one sync mode fixed at compile time (MK_SPEC_SYNC 0:
+// slices of four chunks (rows of 2048 or more columns), head_dim 128 with two
+// query heads per kv head (the ~2B decoder's shapes) and one sync mode fixed
+// at compile time (MK_SPEC_SYNC 0:
 // sentinel, mk_monokernel_w4h128; 1: counter, mk_monokernel_w4h128_ctr).
 // Leaving the other widths, head geometries and the other sync mode out of
 // the kernel's code made the ~2B decode about 5 % faster (the interpreter's
 // code is several times larger than the instruction cache); the host picks a
 // specialised kernel when every instruction of the schedule fits it.
+#ifdef MK_SPECIALIZED
+// query heads per kv head the specialised build is compiled for (the host
+// launches it only for that grouping); 0 = any
+constexpr int kSpecGroup = 2;
+#else
+constexpr int kSpecGroup = 0;
+#endif
 #ifdef MK_SPECIALIZED
 #if MK_SPEC_SYNC == 0
 #define MK_MONOKERNEL mk_monokernel_w4h128
@@ -705,7 +713,7 @@ __device__ __forceinline__ void att_pos_core(Cx& c, int l, int g, int sp, int j0
       if (t >= t1) break;
 #pragma unroll
       for (int j = 0; j < GP; ++j) {
-        if (j >= ng) break;
+        if (GP != kSpecGroup && j >= ng) break;
         float sc = 0.f;
 #pragma unroll
         for (int k = 0; k < DPL; ++k) sc += qs[(j0 + j) * hd + c.lane * DPL + k] * kv[b][k];
@@ -725,7 +733,7 @@ __device__ __forceinline__ void att_pos_core(Cx& c, int l, int g, int sp, int j0
   const int rec = hd + 2;
 #pragma unroll
   for (int j = 0; j < GP; ++j) {
-    if (j >= ng) break;
+    if (GP != kSpecGroup && j >= ng) break;
     float* r = scr + (c.wave * ng + j) * rec;
 #pragma unroll
     for (int k = 0; k < DPL; ++k) r[2 + c.lane * DPL + k] = o[j][k];
@@ -830,7 +838,7 @@ __device__ __forceinline__ void att_pass(Cx& c, int l, int g, int sp, int j0, in
       }
 #pragma unroll
       for (int j = 0; j < GP; ++j) {
-        if (j >= ng) break;
+        if (GP != kSpecGroup && j >= ng) break;
         float sc = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) sc = fmaf(q[j][e], kf[e], sc);
@@ -866,7 +874,7 @@ __device__ __forceinline__ void att_pass(Cx& c, int l, int g, int sp, int j0, in
   if (sub == 0) {
 #pragma unroll
     for (int j = 0; j < GP; ++j) {
-      if (j >= ng) break;
+      if (GP != kSpecGroup && j >= ng) break;
       float* r = scr + (c.wave * ng + j) * rec;
 #pragma unroll
       for (int e = 0; e < 8; ++e) r[2 + dl * 8 + e] = o[j][e];
@@ -1042,7 +1050,7 @@ __device__ __forceinline__ void op_att(Cx& c, const Ins& in) {
       const int dpl = hd / 64;
 #ifdef MK_SPECIALIZED
       (void)dpl;
-      att_short<4, 2>(c, l, g, sp, t0, t1, G, has_cur, ui == 0);
+      att_short<kSpecGroup, 2>(c, l, g, sp, t0, t1, G, has_cur, ui == 0);
 #else
       if (dpl == 1) att_short<8, 1>(c, l, g, sp, t0, t1, G, has_cur, ui == 0);
       else if (dpl == 2) att_short<4, 2>(c, l, g, sp, t0, t1, G, has_cur, ui == 0);
