@@ -50,11 +50,13 @@
 // code is several times larger than the instruction cache); the host picks a
 // specialised kernel when every instruction of the schedule fits it.
 #ifdef MK_SPECIALIZED
-// query heads per kv head the specialised build is compiled for (the host
-// launches it only for that grouping); 0 = any
+// query heads per kv head and head_dim the specialised build is compiled for
+// (the host launches it only for that geometry); 0 = any
 constexpr int kSpecGroup = 2;
+constexpr int kSpecHd = 128;
 #else
 constexpr int kSpecGroup = 0;
+constexpr int kSpecHd = 0;
 #endif
 #ifdef MK_SPECIALIZED
 #if MK_SPEC_SYNC == 0
@@ -73,6 +75,10 @@ constexpr int kSpecGroup = 0;
 using namespace mk;
 
 namespace {
+
+// head_dim and query heads per kv head: compile-time constants in the specialised build
+__device__ __forceinline__ int head_dim(const KParams& kp) { return kSpecHd ? kSpecHd : kp.hd; }
+__device__ __forceinline__ int q_group(const KParams& kp) { return kSpecGroup ? kSpecGroup : kp.nq / kp.nkv; }
 
 // ---------------------------------------------------------------- per-workgroup context
 struct Smem {
@@ -560,7 +566,7 @@ __device__ __forceinline__ void op_qkv(Cx& c, Ring& ring, const Ins& in) {
   const uint16_t* g1 = kp.norms + (int64_t)l * 2 * kp.d;
   // the (cos, sin) row of this position goes to LDS with the staging, so the
   // epilogue does not wait on a global load per unit
-  const int hh = kp.hd / 2, nqh = kp.nq * hh, nkh = kp.nkv * hh;
+  const int hh = head_dim(kp) / 2, nqh = kp.nq * hh, nkh = kp.nkv * hh;
   float* rope = c.sm.resid;
   for (int i = c.tid; i < 2 * hh; i += kThreads) rope[i] = *gp(kp.rope + (int64_t)c.pos * hh * 2 + i);
   const float ss = stage_layer_input(c, l, in.kpad, g1, OP_QKV);
@@ -570,13 +576,13 @@ __device__ __forceinline__ void op_qkv(Cx& c, Ring& ring, const Ins& in) {
   // k head (fp16 into the cache) after RoPE, or a pair of value rows.
   auto store_out = [&](int g, int half, float v) {
     if (g < nqh) {
-      const int64_t idx = (int64_t)(g / hh) * kp.hd + g % hh + half * hh;
+      const int64_t idx = (int64_t)(g / hh) * head_dim(kp) + g % hh + half * hh;
       stcf(buf_at(kp.q, c.e, l, 0) + idx, v);
       if (sentinel_mode(c)) stc32(buf_at(kp.q, c.e1, l, 0) + idx, kSent32);
     } else {
       const bool isk = g < nqh + nkh;
       g -= isk ? nqh : nqh + nkh;
-      const int64_t idx = (((int64_t)l * kp.nkv + g / hh) * kp.max_seq + c.pos) * kp.hd + g % hh + half * hh;
+      const int64_t idx = (((int64_t)l * kp.nkv + g / hh) * kp.max_seq + c.pos) * head_dim(kp) + g % hh + half * hh;
       stc16((isk ? kp.kc : kp.vc) + idx, __builtin_bit_cast(uint16_t, (_Float16)v));
     }
   };
@@ -613,7 +619,7 @@ __device__ __forceinline__ void op_qkv(Cx& c, Ring& ring, const Ins& in) {
 static_assert(kRedDims * 8 <= 64, "red_unit stores kRedDims dims to up to 8 replicas from one wavefront");
 __device__ __forceinline__ void red_unit(Cx& c, int l, int h, int b) {
   const KParams& kp = *c.kp;
-  const int hd = kp.hd, S = kp.S;
+  const int hd = head_dim(kp), S = kp.S;
   const int s = c.lane;
   const int64_t base = (((int64_t)c.e * kp.L + l) * kp.nq + h) * S + s;
   float ms = -INFINITY, ls = 0.f, os[kRedDims];
@@ -695,7 +701,7 @@ template <int GP, int DPL>
 __device__ __forceinline__ void att_pos_core(Cx& c, int l, int g, int sp, int j0, int ng, int t0, int t1, int G,
                                              const float (&kv)[kPosBatch][DPL], const float (&vv)[kPosBatch][DPL]) {
   const KParams& kp = *c.kp;
-  const int hd = kp.hd, S = kp.S;
+  const int hd = head_dim(kp), S = kp.S;
   const float* qs = c.sm.vec;  // [G][hd]
   float m[GP], lsum[GP], o[GP][DPL];
 #pragma unroll
@@ -934,7 +940,7 @@ __device__ __forceinline__ void att_heads(Cx& c, int l, int g, int sp, int t0, i
 // QKV stage writes them) into LDS; ends with a workgroup barrier.
 __device__ __forceinline__ void att_stage(Cx& c, int l, int g, bool has_cur, bool first) {
   const KParams& kp = *c.kp;
-  const int G = kp.nq / kp.nkv, hd = kp.hd;
+  const int G = q_group(kp), hd = head_dim(kp);
   const float qscale = kLog2e / __builtin_sqrtf((float)hd);
   float* qs = c.sm.vec;              // [G][hd]
   float* kcur = c.sm.vec + G * hd;   // [hd]
@@ -1003,7 +1009,7 @@ __device__ __forceinline__ float half_at(const typename RawHalves<DPL>::T& r, in
 template <int GP, int DPL>
 __device__ __forceinline__ void att_short(Cx& c, int l, int g, int sp, int t0, int t1, int G, bool has_cur, bool first) {
   const KParams& kp = *c.kp;
-  const int hd = kp.hd;
+  const int hd = head_dim(kp);
   typedef typename RawHalves<DPL>::T Raw;
   Raw kr[kPosBatch], vr[kPosBatch];
   const int64_t head_off = ((int64_t)l * kp.nkv + g) * kp.max_seq * hd + c.lane * DPL;
@@ -1036,7 +1042,7 @@ __device__ __forceinline__ void att_short(Cx& c, int l, int g, int sp, int t0, i
 __device__ __forceinline__ void op_att(Cx& c, const Ins& in) {
   const KParams& kp = *c.kp;
   const int l = in.layer;
-  const int G = kp.nq / kp.nkv, hd = kp.hd, S = kp.S;
+  const int G = q_group(kp), hd = head_dim(kp), S = kp.S;
   const int T = c.pos + 1;
   const int chunk = (T + S - 1) / S;
   counter_wait(c, in.sync_in, in.n_in, OP_ATT, l);
