@@ -64,7 +64,7 @@ class mk_plan_info(C.Structure):
     _fields_ = [("n_cta", C.c_int32), ("max_ins_per_cta", C.c_int32), ("n_sync_ids", C.c_int32),
                 ("lds_bytes", C.c_int32), ("stream_chunks", C.c_int64), ("stream_bytes", C.c_int64),
                 ("weight_bytes", C.c_int64), ("min_wave_chunks", C.c_int32), ("max_wave_chunks", C.c_int32),
-                ("attn_splits", C.c_int32)]
+                ("attn_splits", C.c_int32), ("specialised", C.c_int32)]
 
 
 # Every symbol of include/mk.h: (name, restype, argtypes)

@@ -554,6 +554,7 @@ int mk_plan_check(const mk_config* cfg, const mk_options* opts, int32_t n_cta, m
     info->min_wave_chunks = mn;
     info->max_wave_chunks = mx;
     info->attn_splits = p.S;
+    info->specialised = fits_specialised(p) ? 1 : 0;
   }
   return MK_OK;
 }

@@ -240,11 +240,12 @@ typedef struct mk_plan_info {
   int64_t stream_bytes, weight_bytes;
   int32_t min_wave_chunks, max_wave_chunks;
   int32_t attn_splits;
+  int32_t specialised;       /* 1: the schedule runs on a specialised monokernel (see mk_kernel_name) */
 } mk_plan_info;
 
 /* Calibration probes: the launch cost, the practical HBM read ceiling and the naive grid
- * barrier that "7 - AMD et le monokernel" (section 7.3) compares the NaN sentinel against.  Each runs on `hip_stream` of `device` and
- * synchronises; errors: MK_EINVAL (arguments), MK_EHIP (HIP failure), MK_EOCC, MK_ETIMEOUT;
+ * barrier that "7 - AMD et le monokernel" (section 7.3) compares the NaN sentinel against.
+ * Each runs on `hip_stream` of `device` and synchronises; errors: MK_EINVAL (arguments), MK_EHIP (HIP failure), MK_EOCC, MK_ETIMEOUT;
  * text from mk_last_error(NULL).
  * mk_probe_launch: n_launches empty-kernel launches back to back then one synchronisation
  *   (host microseconds per launch -> *us_pipelined), and n_launches launch + synchronise

@@ -173,3 +173,20 @@ def test_plan_rejects_options(field, value):
     with pytest.raises(mk.MkError) as e:
         mk.mk_plan_check(w.model, w.max_seq, 64, mk.mk_default_options(**{field: value}))
     assert e.value.code == mk.MK_EINVAL
+
+
+@pytest.mark.parametrize("name,grid,expect", [("2b", 256, 1), ("2b-long", 256, 1), ("2b", 61, 1),
+                                              ("0.5b", 256, 0), ("tiny", 256, 0)])
+def test_specialised_kernel_choice(name, grid, expect):
+    """The ~2B schedule (4-chunk slices, head_dim 128, two query heads per kv head) fits the
+    specialised monokernel at any grid; head_dim 64 or narrower rows do not."""
+    w = inputs.WORKLOADS[name]
+    info = mk.mk_plan_check(w.model, w.max_seq, grid)
+    assert info["specialised"] == expect
+
+
+def test_specialised_kernel_needs_two_query_heads_per_kv_head():
+    m = inputs.M2B
+    mha = inputs.ModelConfig("2b-mha", n_layers=2, d_model=m.d_model, n_heads=16, n_kv_heads=16, head_dim=128,
+                             ffn=m.ffn, vocab=4096, rms_eps=m.rms_eps, rope_theta=m.rope_theta)
+    assert mk.mk_plan_check(mha, 64, 256)["specialised"] == 0
