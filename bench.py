@@ -89,7 +89,8 @@ def measured_traffic(workload: str, n: int, launch: dict):
     return rec
 
 
-def traced_decode(model, w, ids, P: int, n: int, opts, trace_steps: int) -> dict:
+def traced_decode(model, w, ids, P: int, n: int, opts, trace_steps: int, top_k: int = 1,
+                  temperature: float = 1.0) -> dict:
     """One extra launch (not timed) with the time journal on for its first steps: handoff latency per op."""
     import torch
     import decode_megakernel_wave_amd as mk
@@ -102,6 +103,8 @@ def traced_decode(model, w, ids, P: int, n: int, opts, trace_steps: int) -> dict
         mk.mk_load_weights(ctx, wd)
         del wd
         torch.cuda.empty_cache()
+        if top_k > 1:
+            mk.mk_set_sampling(ctx, top_k, temperature, seed=3)
         mk.mk_prefill(ctx, ids)
         mk.mk_decode(ctx, min(n, max(trace_steps, 8)))
         rec = mk.mk_read_trace(ctx)
@@ -283,7 +286,7 @@ def main() -> int:
     mk.mk_destroy(ctx)
     sync_latency = None
     if args.trace_steps > 0:
-        sync_latency = traced_decode(model, w, ids, P, n, opts, args.trace_steps)
+        sync_latency = traced_decode(model, w, ids, P, n, opts, args.trace_steps, args.top_k, args.temperature)
 
     mean_ms = float(np.mean(kernel_ms))
     achieved = float(np.mean(algo)) / (mean_ms * 1e-3) / 1e9

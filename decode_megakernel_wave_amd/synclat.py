@@ -34,7 +34,8 @@ def _relative_ticks(t: np.ndarray) -> np.ndarray:
 def handoffs(records: np.ndarray) -> dict:
     """Per-op handoff statistics (microseconds) of a time journal.
 
-    Returns {op_name: {"stages", "waiting_consumers", "median_us", "p99_us",
+    Returns {op_name: {"stages" (stages with a waiting consumer), "waiting_consumers",
+    "median_us", "p99_us",
     "critical_median_us", "critical_p99_us", "late_staging_median_us",
     "span_median_us", "span_mean_us"}} plus an "all" entry pooling every op.  The
     span of a stage is its share of the critical path: from the last producer's
@@ -62,16 +63,23 @@ def handoffs(records: np.ndarray) -> dict:
         if len(cons) == 0:
             continue
         last_done = done[prod].max()
-        waiting = cons[tw[cons] <= last_done]
-        late = cons[tw[cons] > last_done]
         name = OP_NAMES.get(int(op[cons[0]]), str(int(op[cons[0]])))
         d = per_op.setdefault(name, {"lat": [], "crit": [], "late": [], "span": []})
+        # the span is every stage's share of the critical path
+        d["span"].append(int(done[groups[k]].max() - last_done))
+        if int(op[prod[0]]) == 8:
+            # after the argmax every workgroup starts the next step from the token it
+            # computed itself: no handoff between workgroups
+            continue
+        # consumers that were waiting when the last producer published and were staged after
+        # it (a consumer that needs only some producers may be staged earlier: not a handoff
+        # from the last one)
+        waiting = cons[(tw[cons] <= last_done) & (ready[cons] >= last_done)]
+        late = cons[tw[cons] > last_done]
         d["lat"].extend((ready[waiting] - last_done).tolist())
         d["late"].extend(ready_rel[late].tolist())
         if len(waiting):
             d["crit"].append(int(ready[cons].max() - last_done))
-        # the stage's share of the critical path: last producer done -> last consumer done
-        d["span"].append(int(done[groups[k]].max() - last_done))
     out = {}
     pooled = {"lat": [], "crit": [], "late": [], "span": []}
     for name, d in per_op.items():

@@ -37,7 +37,18 @@ def test_records_without_a_staging_mark_are_skipped():
     r = [rec(0, 0, 0, 7, 1000, 5, 50), rec(0, 0, 1, 8, 1050, 0, 20), rec(0, 1, 0, 1, 1075, 10, 40)]
     res = synclat.handoffs(np.array(r, dtype=np.uint32))
     assert "argmax" not in res
-    assert res["qkv"]["waiting_consumers"] == 0 and res["qkv"]["late_staging_median_us"] == pytest.approx(0.10)
+    # the step after the argmax starts from a token every workgroup computed itself: a span, no handoff
+    assert res["qkv"]["waiting_consumers"] == 0 and res["qkv"]["late_staging_median_us"] is None
+    assert res["qkv"]["span_median_us"] == pytest.approx(0.45)  # 1075 + 40 - (1050 + 20)
+
+
+def test_consumers_staged_before_the_last_producer_are_not_handoffs():
+    r = [rec(0, 0, 0, 1, 0, 5, 100), rec(1, 0, 0, 1, 0, 5, 300),     # QKV producers: last done at 300
+         rec(0, 0, 1, 2, 100, 50, 400),                               # needs only the early producer: ready 150
+         rec(1, 0, 1, 2, 300, 40, 400)]                               # waits for the last: ready 340
+    res = synclat.handoffs(np.array(r, dtype=np.uint32))
+    a = res["attention"]
+    assert a["waiting_consumers"] == 1 and a["median_us"] == pytest.approx(0.40)
 
 
 def test_empty_journal():
