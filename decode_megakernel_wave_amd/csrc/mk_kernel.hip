@@ -1345,7 +1345,7 @@ __device__ __forceinline__ void op_lmhead(Cx& c, Ring& ring, const Ins& in) {
 // top-K lists (polled like the argmax keys) into the global K largest keys,
 // then draws the token by the inverse-CDF rule with a Philox uniform.  The
 // arithmetic is the same in every workgroup, so all draw the same token.
-__device__ __forceinline__ void op_sample(Cx& c, const Ins& in) {
+__device__ __forceinline__ void op_sample_all(Cx& c, const Ins& in) {
   const KParams& kp = *c.kp;
   const int K = kp.top_k, n = in.nu * K;
   const uint64_t* src = kp.lmk + c.e * kp.lmk_es + c.rep * kp.lmk_rs;  // [slot][kMaxTopK]
@@ -1390,6 +1390,116 @@ __device__ __forceinline__ void op_sample(Cx& c, const Ins& in) {
     acquire_polled();
     uint64_t v[2] = {c.lane < kWaves * K ? lists[c.lane] : 1, c.lane + 64 < kWaves * K ? lists[c.lane + 64] : 1};
     const uint64_t key = wave_topk<2>(v, K);
+    // weights exp((z_j - z_0) / T) of the candidates in order; running sums in that order
+    const uint32_t top_hi = __builtin_amdgcn_readfirstlane((uint32_t)(key >> 32));
+    const uint32_t top_lo = __builtin_amdgcn_readfirstlane((uint32_t)key);
+    const uint64_t top = ((uint64_t)top_hi << 32) | top_lo;  // lane 0: the largest logit
+    const float z0 = key_value(top);
+    const float w = c.lane < K && key > 1 ? exp2f((key_value(key) - z0) * kp.inv_temp * kLog2e) : 0.f;
+    const uint32_t word = philox_word0((uint32_t)c.pos, kp.seed_lo, kp.seed_hi);
+    const float u = (float)(word >> 8) * 0x1p-24f;
+    float total = 0.f;
+    for (int j = 0; j < K; ++j) total += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
+    const float target = u * total;
+    float cum = 0.f;
+    int pick = K - 1;
+    for (int j = 0; j < K; ++j) {
+      cum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
+      if (cum > target) {
+        pick = j;
+        break;
+      }
+    }
+    const int id = key_index(key);
+    const int tok = __builtin_amdgcn_readlane(id, pick);
+    if (c.lane == 0) c.sm.misc[1] = (uint32_t)tok;
+  }
+  cta_sync(c);
+  int tok = __builtin_amdgcn_readfirstlane((int)c.sm.misc[1]);
+  if (tok < 0 || tok >= kp.V) tok = 0;  // only on an aborted run
+  if (c.cta == 0 && c.tid == 0) *gp(kp.tokens + c.step) = tok;
+  c.tok = tok;
+}
+
+// Poll M 8-byte keys per lane (null address: no key, reads as 1) until none is
+// the sentinel; every pending key is re-polled in one batch.
+template <int M>
+__device__ __forceinline__ void poll_keys(Cx& c, uint64_t (&v)[M], const uint64_t* const (&a)[M]) {
+#pragma unroll
+  for (int i = 0; i < M; ++i) v[i] = a[i] ? ldc64(a[i]) : 1;
+  if (!sentinel_mode(c)) return;
+  for (;;) {
+    bool pending = false;
+#pragma unroll
+    for (int i = 0; i < M; ++i) pending |= v[i] == kSent64;
+    if (!pending || c.fail) break;
+    if (expired(c, OP_ARGMAX, c.kp->L, -1)) {
+      c.fail = true;
+      break;
+    }
+    poll_pause(c);
+#pragma unroll
+    for (int i = 0; i < M; ++i)
+      if (v[i] == kSent64) v[i] = ldc64(a[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < M; ++i)
+    if (v[i] == kSent64) v[i] = 1;  // only on an aborted run
+}
+
+// Sampling with at most 256 workgroup lists: the global K largest keys all come
+// from the workgroups whose own maximum is among the K largest maxima (any other
+// workgroup has K larger keys elsewhere), so wavefront 0 first polls the
+// per-workgroup maxima (the argmax keys), picks the K workgroups with the
+// largest ones, then polls only their K lists (K*K <= 256 keys) and merges them.
+__device__ __forceinline__ void op_sample(Cx& c, const Ins& in) {
+  const KParams& kp = *c.kp;
+  const int K = kp.top_k, nslot = in.nu;
+  if (nslot > 256) {
+    op_sample_all(c, in);
+    return;
+  }
+  if (c.wave == 0) {
+    const uint64_t* maxk = kp.lmp + c.e * kp.lmp_es + c.rep * kp.lmp_rs;  // [slot]
+    const uint64_t* lists = kp.lmk + c.e * kp.lmk_es + c.rep * kp.lmk_rs;  // [slot][kMaxTopK]
+    uint64_t v[4];
+    const uint64_t* a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sl = c.lane + 64 * i;
+      a[i] = sl < nslot ? maxk + sl : nullptr;
+    }
+    poll_keys<4>(c, v, a);
+    // lane j: slot of the j-th largest maximum (slot 0 where fewer than K exist)
+    int sel = 0;
+    for (int j = 0; j < K; ++j) {
+      uint64_t m = 1;
+      int mi = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (v[i] > m) {
+          m = v[i];
+          mi = i;
+        }
+      const uint64_t w = wave_max_u64(m);
+      if (w <= 1) break;
+      const int owner = (int)__builtin_ctzll(__ballot(m == w));
+      const int slot = __builtin_amdgcn_readlane(c.lane + 64 * mi, owner);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (c.lane == owner && i == mi) v[i] = 1;
+      if (c.lane == j) sel = slot;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = c.lane + 64 * i;  // key q: element q % K of the (q / K)-th selected list
+      const int sl = __shfl(sel, q < K * K ? q / K : 0);
+      a[i] = q < K * K ? lists + (int64_t)sl * kMaxTopK + q % K : nullptr;
+    }
+    poll_keys<4>(c, v, a);
+    mark_ready(c);
+    acquire_polled();
+    const uint64_t key = wave_topk<4>(v, K);  // lane j: the j-th largest key
     // weights exp((z_j - z_0) / T) of the candidates in order; running sums in that order
     const uint32_t top_hi = __builtin_amdgcn_readfirstlane((uint32_t)(key >> 32));
     const uint32_t top_lo = __builtin_amdgcn_readfirstlane((uint32_t)key);
