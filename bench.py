@@ -180,7 +180,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", default="2b", choices=["2b", "2b-long", "0.5b", "tiny", "chain", "chain-s"],
+    ap.add_argument("--workload", default="2b", choices=["2b", "2b-long", "2b-tp8-shard", "0.5b", "tiny", "chain", "chain-s"],
                     help="decoder workloads, or the GEMV-tanh chain microbenchmark (chain: 256 stages of "
                          "2048x2048; chain-s: 256 stages of 256x256, cache-resident, to isolate sync latency)")
     ap.add_argument("--decode-steps", type=int, default=0, help="tokens per launch (default: the workload's)")

@@ -72,12 +72,21 @@ M05 = ModelConfig("0.5b", n_layers=24, d_model=1024, n_heads=16, n_kv_heads=8,
                   head_dim=64, ffn=2816, vocab=32000)
 M2B = ModelConfig("2b", n_layers=24, d_model=2048, n_heads=16, n_kv_heads=8,
                   head_dim=128, ffn=8192, vocab=128256)
+# One GPU's share of the ~2B decoder under 8-way tensor parallelism: 2 query
+# heads and 1 kv head (512 QKV rows), a 1024-row slice of gate/up with the
+# matching 1024 input columns of down, the 256 input columns of O for those
+# heads, and 16032 of the 128256 LM-head rows.  Each partial residual would be
+# summed over the 8 GPUs; with the other GPUs' slots empty that sum is the
+# local value, so the shard runs as a decoder of its own with these dims.
+M2B_TP8 = ModelConfig("2b-tp8-shard", n_layers=24, d_model=2048, n_heads=2, n_kv_heads=1,
+                      head_dim=128, ffn=1024, vocab=16032)
 
 WORKLOADS = {
     "tiny": Workload(TINY, 32, 16),
     "0.5b": Workload(M05, 128, 256),
     "2b": Workload(M2B, 512, 512),
     "2b-long": Workload(M2B, 8192, 256),
+    "2b-tp8-shard": Workload(M2B_TP8, 512, 512),
 }
 
 # GEMV-tanh chain: 256 dependent stages y_i = tanh(W_i y_{i-1}), W_i 2048x2048.

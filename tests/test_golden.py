@@ -13,7 +13,7 @@ from oracle import chain as ochain
 from oracle import decoder as od
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "derived_values.json")))
-MODELS = {"tiny": inputs.TINY, "0.5b": inputs.M05, "2b": inputs.M2B}
+MODELS = {"tiny": inputs.TINY, "0.5b": inputs.M05, "2b": inputs.M2B, "2b-tp8-shard": inputs.M2B_TP8}
 
 
 @pytest.mark.parametrize("name", list(MODELS))

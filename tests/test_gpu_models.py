@@ -4,7 +4,8 @@
 chunks of 512: zero-padded K slices), vocab 32000.
 ~2B: 24 layers, d 2048, 16 / 8 heads of 128, SwiGLU 8192, vocab 128256 -- the
 benchmark's model, in the benchmark's launch configuration (same grid, ring,
-replicas and schedule; the 512-token prompt case is the benchmark's own).
+replicas and schedule; the 512-token prompt case is the benchmark's own); and
+one GPU's 1/8 tensor-parallel share of it.
 The oracle is teacher-forced with its own greedy tokens; the GPU is fed the
 same tokens, so every step is compared (|dlogit| <= 1e-2, equal argmax where
 the oracle's top-2 margin exceeds 2e-2).
@@ -70,6 +71,15 @@ def test_05b_counter_mode(w05):
 def test_2b_short_prompt(w2b):
     err = _parity(inputs.M2B, w2b, P=16, n=6)
     print(f"2B P=16: max |dlogit| {err:.2e}")
+
+
+def test_2b_tp8_shard():
+    """One GPU's share of the ~2B decoder under 8-way tensor parallelism (2 q heads, 1 kv head:
+    64 attention splits of one head; O rows of 256 columns, one zero-padded chunk; ffn 1024;
+    16032 LM-head rows), as a decoder of its own, with the benchmark's 512-token prompt."""
+    w = inputs.make_weights(inputs.M2B_TP8, seed=0)
+    err = _parity(inputs.M2B_TP8, w, P=512, n=4)
+    print(f"2B tp8 shard P=512: max |dlogit| {err:.2e}")
 
 
 def test_2b_bench_prompt512(w2b):
