@@ -120,6 +120,43 @@ def traced_decode(model, w, ids, P: int, n: int, opts, trace_steps: int, top_k: 
             "consumer ready - last producer done, per stage", "per_op": res}
 
 
+def fine_mark_decode(model, w, ids, P: int, opts) -> dict:
+    """One extra launch (not timed) of 4 decode steps with the fine marks of step 0 recorded
+    (MK_DEBUG_TS): median phase durations of each instruction, per op, over layers 1..L-1."""
+    import torch
+    import decode_megakernel_wave_amd as mk
+    from decode_megakernel_wave_amd import synclat
+
+    L = model.n_layers
+    os.environ["MK_DEBUG_TS"] = "1"
+    ctx = mk.mk_create(model, max_seq=P + 5, opts=opts)
+    try:
+        wd = mk.to_device(w)
+        mk.mk_load_weights(ctx, wd)
+        del wd
+        torch.cuda.empty_cache()
+        mk.mk_prefill(ctx, ids)
+        mk.mk_decode(ctx, 4)
+        grid = mk.mk_get_stats(ctx)["grid"]
+        max_ins = mk.mk_plan_check(model, P + 5, grid)["max_ins_per_cta"]
+        if max_ins != 5 * L + 2:
+            raise RuntimeError(f"fine marks expect 5 instructions per layer and workgroup, got {max_ins} in all")
+        ts = mk.mk_debug_ts(ctx, grid, max_ins)
+        if not (ts[:, -1, 0] > 0).all():
+            raise RuntimeError("fine marks expect every workgroup to run all 5 ops of every layer")
+        kernel = mk.mk_kernel_name(ctx)
+    finally:
+        mk.mk_destroy(ctx)
+        del os.environ["MK_DEBUG_TS"]
+    names = ["qkv", "attention", "o_proj", "up_gate", "down"]
+    ops = [None] * 5 + names * (L - 1) + ["lm_head", "argmax"]  # layer 0 stages the embedding row
+    res = synclat.fine_marks(ts, ops)
+    for k, v in res.items():
+        log(f"[bench] fine marks {k}: " + ", ".join(f"{p} {x:.2f}" for p, x in v.items()))
+    return {"kernel": kernel, "unit": "us", "definition": "median over workgroups and layers 1..L-1 of the phases "
+            "between the marks wavefront 0 takes per instruction in step 0 (mk_debug_ts)", "per_op": res}
+
+
 def chain_bench(args) -> int:
     """GEMV-tanh chain y_i = tanh(W_i y_{i-1}), 256 dependent stages in one persistent launch, run with
     NaN-sentinel and with atomic-counter inter-stage sync: microseconds per stage, GB/s, handoff latency."""
@@ -192,6 +229,9 @@ def main() -> int:
     ap.add_argument("--trace-steps", type=int, default=0,
                     help="after the timed launches, run one more launch that records the per-instruction time "
                          "journal of its first N steps and report the inter-stage handoff latency")
+    ap.add_argument("--fine-marks", action="store_true",
+                    help="after the timed launches, run one more launch with the fine per-instruction marks of "
+                         "its first step recorded and report the median phase durations per op")
     ap.add_argument("--probes", action="store_true",
                     help="only run the calibration probes (empty-kernel launch cost, nontemporal read ceiling "
                          "over 4 GiB, naive atomic grid barrier) and print one JSON line")
@@ -287,6 +327,7 @@ def main() -> int:
     sync_latency = None
     if args.trace_steps > 0:
         sync_latency = traced_decode(model, w, ids, P, n, opts, args.trace_steps, args.top_k, args.temperature)
+    fine = fine_mark_decode(model, w, ids, P, opts) if args.fine_marks else None
 
     mean_ms = float(np.mean(kernel_ms))
     achieved = float(np.mean(algo)) / (mean_ms * 1e-3) / 1e9
@@ -329,6 +370,8 @@ def main() -> int:
     }
     if sync_latency is not None:
         out["sync_latency"] = sync_latency
+    if fine is not None:
+        out["fine_marks"] = fine
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle (bounded sample)")
         try:

@@ -91,6 +91,7 @@ SIGNATURES = [
     ("mk_debug_layout", C.c_int, [C.c_void_p, C.POINTER(C.c_int64)]),
     ("mk_debug_arena", C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.POINTER(C.c_uint32)]),
     ("mk_debug_progress", C.c_int, [C.c_void_p, C.POINTER(C.c_uint32), C.c_int32]),
+    ("mk_debug_ts", C.c_int, [C.c_void_p, C.POINTER(C.c_uint64), C.c_int64]),
     ("mk_last_error", C.c_char_p, [C.c_void_p]),
     ("mk_destroy", None, [C.c_void_p]),
     ("mk_chain_create", C.c_int, [C.c_int32, C.c_int32, C.c_void_p, C.POINTER(mk_options), C.c_int, C.c_void_p,
@@ -296,6 +297,14 @@ def mk_read_trace(ctx) -> np.ndarray:
     buf = np.zeros((n.value, 8), dtype=np.uint32)
     if n.value:
         _check(lib().mk_read_trace(ctx, buf.ctypes.data_as(C.POINTER(C.c_uint32)), n.value, C.byref(n)), ctx)
+    return buf
+
+
+def mk_debug_ts(ctx, grid: int, max_ins: int) -> np.ndarray:
+    """Fine marks of step 0 of the last launch (recorded when MK_DEBUG_TS was set at launch):
+    uint64 [grid][max_ins][8], 100 MHz device-clock ticks, 0 where not recorded."""
+    buf = np.zeros((grid, max_ins, 8), dtype=np.uint64)
+    _check(lib().mk_debug_ts(ctx, buf.ctypes.data_as(C.POINTER(C.c_uint64)), buf.size), ctx)
     return buf
 
 

@@ -100,3 +100,31 @@ def _summary(d: dict) -> dict:
             "critical_median_us": q(d["crit"], 50), "critical_p99_us": q(d["crit"], 99),
             "late_staging_median_us": q(d["late"], 50), "span_median_us": q(d["span"], 50),
             "span_mean_us": float(np.mean(d["span"]) * TICK_US) if len(d["span"]) else None}
+
+
+# Phases between the fine marks that wavefront 0 of every workgroup takes per
+# instruction (marks: 0 start, 1 inputs polled, 2 staged after the barrier,
+# 5 activations in registers -- attention: the wavefront's positions done,
+# 7 first weight chunk read -- attention: wavefront partials combined,
+# 6 own rows done -- attention: split partials published, 3 op end (the
+# workgroup's rows published; attention: split merge done), 4 failure vote done).
+FINE_PHASES = (("wait_and_poll", 0, 1), ("barrier", 1, 2), ("activations", 2, 5),
+               ("first_chunk", 5, 7), ("own_rows", 7, 6), ("workgroup_and_publish", 6, 3),
+               ("vote", 3, 4), ("total", 0, 4))
+
+
+def fine_marks(ts: np.ndarray, ops: list) -> dict:
+    """Median duration in µs of each phase per op over every workgroup and every
+    instruction of that op.  ts: [grid][n_ins][8] 100 MHz ticks (0 = not
+    recorded); ops: the op name of each instruction index (None to skip one)."""
+    t = ts.astype(np.int64)
+    out = {}
+    for name in dict.fromkeys(o for o in ops if o is not None):
+        a = t[:, [i for i, o in enumerate(ops) if o == name], :]
+        d = {}
+        for ph, i, j in FINE_PHASES:
+            ok = (a[..., i] > 0) & (a[..., j] > 0)
+            if ok.any():
+                d[ph] = round(float(np.median((a[..., j] - a[..., i])[ok])) * 0.01, 3)
+        out[name] = d
+    return out

@@ -53,3 +53,30 @@ def test_consumers_staged_before_the_last_producer_are_not_handoffs():
 
 def test_empty_journal():
     assert synclat.handoffs(np.zeros((4, 8), dtype=np.uint32)) == {}
+
+
+def test_fine_marks_phase_medians():
+    """Phases are differences of the marks of each instruction (10 ns ticks -> µs), medians per
+    op over workgroups and instructions, unrecorded marks (0) left out, skipped indices ignored."""
+    ts = np.zeros((3, 3, 8), dtype=np.uint64)
+    for g in range(3):
+        for i in range(3):
+            t0 = 1000 * (i + 1) + 10 * g
+            # marks in time order 0, 1, 2, 5, 7, 6, 3, 4 (array index = mark number)
+            m = {0: t0, 1: t0 + 100 + g, 2: t0 + 110 + g, 5: t0 + 150 + g, 7: t0 + 200 + g,
+                 6: t0 + 250 + g, 3: t0 + 300 + g, 4: t0 + 400 + g}
+            for k, v in m.items():
+                ts[g, i, k] = v
+    ts[0, 0] = 1  # instruction 0 is skipped: its values must not count
+    ts[2, 1, 4] = 0  # the vote mark of one instruction was not recorded
+    res = synclat.fine_marks(ts, [None, "a", "a"])
+    assert list(res) == ["a"]
+    a = res["a"]
+    assert a["wait_and_poll"] == pytest.approx(1.01)  # 100 + g over g = 0, 1, 2
+    assert a["barrier"] == pytest.approx(0.10)
+    assert a["activations"] == pytest.approx(0.40)
+    assert a["first_chunk"] == pytest.approx(0.50)
+    assert a["own_rows"] == pytest.approx(0.50)
+    assert a["workgroup_and_publish"] == pytest.approx(0.50)
+    assert a["vote"] == pytest.approx(1.00)
+    assert a["total"] == pytest.approx(4.01)  # 400 + g without the unrecorded one: median of 5 values
