@@ -712,25 +712,51 @@ __device__ __forceinline__ void att_pos_core(Cx& c, int l, int g, int sp, int j0
     for (int k = 0; k < DPL; ++k) o[j][k] = 0.f;
   }
   {
+    // The wavefront's nb positions tb, tb + kWaves, ... (nb <= kPosBatch,
+    // uniform) are one batch: every score first -- the wavefront sums do not
+    // depend on each other, so they overlap -- then per head the batch maximum,
+    // the weights 2^(s - m), their sum and the weighted V sum.  Positions past
+    // nb hold zero K/V rows; their sums are computed and ignored.
     const int tb = t0 + c.wave;
+    const int nb = tb < t1 ? min(kPosBatch, (t1 - tb + kWaves - 1) / kWaves) : 0;
+    float sc[GP][kPosBatch];
 #pragma unroll
-    for (int b = 0; b < kPosBatch; ++b) {
-      const int t = tb + b * kWaves;
-      if (t >= t1) break;
+    for (int j = 0; j < GP; ++j) {
+      if (GP != kSpecGroup && j >= ng) break;
+      float qv[DPL];
 #pragma unroll
-      for (int j = 0; j < GP; ++j) {
-        if (GP != kSpecGroup && j >= ng) break;
-        float sc = 0.f;
+      for (int k = 0; k < DPL; ++k) qv[k] = qs[(j0 + j) * hd + c.lane * DPL + k];
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) sc += qs[(j0 + j) * hd + c.lane * DPL + k] * kv[b][k];
-        sc = wave_sum(sc);
-        const float mn = fmaxf(m[j], sc);
-        const float al = exp2f(m[j] - mn), p = exp2f(sc - mn);
-        lsum[j] = lsum[j] * al + p;
+      for (int b = 0; b < kPosBatch; ++b) {
+        float s = 0.f;
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) o[j][k] = o[j][k] * al + p * vv[b][k];
-        m[j] = mn;
+        for (int k = 0; k < DPL; ++k) s += qv[k] * kv[b][k];
+        sc[j][b] = s;
       }
+    }
+#pragma unroll
+    for (int j = 0; j < GP; ++j) {
+      if (GP != kSpecGroup && j >= ng) break;
+#pragma unroll
+      for (int b = 0; b < kPosBatch; ++b) sc[j][b] = wave_sum(sc[j][b]);
+    }
+#pragma unroll
+    for (int j = 0; j < GP; ++j) {
+      if (GP != kSpecGroup && j >= ng) break;
+      float mn = -INFINITY;
+#pragma unroll
+      for (int b = 0; b < kPosBatch; ++b)
+        if (b < nb) mn = fmaxf(mn, sc[j][b]);
+#pragma unroll
+      for (int b = 0; b < kPosBatch; ++b) {
+        if (b < nb) {
+          const float p = exp2f(sc[j][b] - mn);
+          lsum[j] += p;
+#pragma unroll
+          for (int k = 0; k < DPL; ++k) o[j][k] += p * vv[b][k];
+        }
+      }
+      m[j] = mn;
     }
   }
   ts_mark(c, 5);
