@@ -33,8 +33,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(model, w, prompt_len: int = 64, steps: int = 8) -> dict:
-    """Time the CPU oracle: decode `steps` tokens after a `prompt_len` prompt."""
+def cpu_baseline(model, w, P: int, n: int, prompt_len: int = 64, steps: int = 8, steps_1t: int = 2) -> dict:
+    """Time the CPU oracle: decode `steps` tokens after a `prompt_len` prompt on every host core
+    of this process, then `steps_1t` more tokens on one thread."""
     import numpy as np
     import threadpoolctl
     from decode_megakernel_wave_amd import inputs
@@ -42,20 +43,29 @@ def cpu_baseline(model, w, prompt_len: int = 64, steps: int = 8) -> dict:
 
     ids = inputs.make_prompt(model, prompt_len, seed=1)
     cores = len(os.sched_getaffinity(0))
+    dec = od.Decoder(w, model.n_heads, model.n_kv_heads, model.rms_eps, model.rope_theta,
+                     max_seq=prompt_len + steps + steps_1t + 1)
     with threadpoolctl.threadpool_limits(cores):
         info = threadpoolctl.threadpool_info()
         threads = max([i.get("num_threads", 1) for i in info] or [1])
-        dec = od.Decoder(w, model.n_heads, model.n_kv_heads, model.rms_eps, model.rope_theta,
-                         max_seq=prompt_len + steps + 1)
         t = int(np.argmax(dec.prefill(ids)))
         t0 = time.perf_counter()
         for s in range(steps):
             t = int(np.argmax(dec.step(t, prompt_len + s)))
         dt = time.perf_counter() - t0
+    with threadpoolctl.threadpool_limits(1):
+        t1 = time.perf_counter()
+        for s in range(steps, steps + steps_1t):
+            t = int(np.argmax(dec.step(t, prompt_len + s)))
+        dt1 = time.perf_counter() - t1
+    kv = 2 * model.n_layers * model.n_kv_heads * model.head_dim * 2 * (P + (n + 1) / 2)
+    kv_share = kv / (kv + 2 * model.n_params() - 2 * model.vocab * model.d_model + 2 * model.d_model)
     return {"value": steps / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"float64 oracle decode of {steps} greedy tokens of the same 2B decoder after a "
+            "one_thread": {"value": steps_1t / dt1, "unit": "tokens/s", "cores": 1, "steps": steps_1t},
+            "sample": f"float64 oracle decode of {steps} greedy tokens of the same {model.name} decoder after a "
                       f"{prompt_len}-token prompt (KV context {prompt_len}..{prompt_len + steps} instead of "
-                      f"512..1024; attention is ~2% of the bytes per token)"}
+                      f"{P}..{P + n}; K/V are {100 * kv_share:.1f}% of the bytes per token at the full context), "
+                      f"then {steps_1t} tokens on one thread"}
 
 
 # sources that decide what the monokernel reads and writes: the device code and the schedule
@@ -375,7 +385,7 @@ def main() -> int:
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle (bounded sample)")
         try:
-            out["cpu_baseline"] = cpu_baseline(model, w)
+            out["cpu_baseline"] = cpu_baseline(model, w, P, n)
         except MemoryError:
             out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
