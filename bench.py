@@ -371,7 +371,7 @@ def main() -> int:
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "traffic_read_write": [traffic["fetch_bytes_per_launch"], traffic["write_bytes_per_launch"]]
                      if traffic else None,
-                     "kernel": kernel_name, "kernel_ms": mean_ms,
+                     "kernel": kernel_name, "kernel_ms": mean_ms, "kernel_ms_median": float(np.median(kernel_ms)),
                      "algo_bytes_per_launch": float(np.mean(algo))},
         "kernel_tokens_per_s": n / mean_ms * 1e3,
         "prefill": {"prompt_len": P, "gpu_ms": prefill_ms, "note": "untimed setup: the prompt runs through the "
