@@ -1078,7 +1078,7 @@ __device__ __forceinline__ void op_att(Cx& c, const Ins& in) {
     const int t0 = sp * chunk, t1 = min(T, t0 + chunk);
     const bool has_cur = t0 <= c.pos && c.pos < t1;
     if (t1 - t0 <= kPosBatch * kWaves) {
-      // short split (a few positions per wavefront): one position per wavefront per step
+      // short split (at most kPosBatch positions per wavefront): scores of the batch first, then one softmax per head
       const int dpl = hd / 64;
 #ifdef MK_SPECIALIZED
       (void)dpl;
