@@ -147,7 +147,7 @@ def fine_mark_decode(model, w, ids, P: int, opts) -> dict:
         torch.cuda.empty_cache()
         mk.mk_prefill(ctx, ids)
         mk.mk_decode(ctx, 4)
-        grid = mk.mk_get_stats(ctx)["grid"]
+        grid = mk.mk_stats(ctx)["grid"]
         max_ins = mk.mk_plan_check(model, P + 5, grid)["max_ins_per_cta"]
         if max_ins != 5 * L + 2:
             raise RuntimeError(f"fine marks expect 5 instructions per layer and workgroup, got {max_ins} in all")
@@ -309,13 +309,13 @@ def main() -> int:
         mk.mk_set_sampling(ctx, args.top_k, args.temperature, seed=3)
     t = time.time()
     t0 = mk.mk_prefill(ctx, ids)
-    prefill_ms = mk.mk_get_stats(ctx)["gpu_ms"]
+    prefill_ms = mk.mk_stats(ctx)["gpu_ms"]
     log(f"[bench] prefill of {P} tokens in one launch: {time.time() - t:.2f}s wall, {prefill_ms:.1f} ms GPU; t0={t0}")
 
     def step():
         mk.mk_rewind(ctx, P)
         toks = mk.mk_decode(ctx, n)
-        return toks, mk.mk_get_stats(ctx)
+        return toks, mk.mk_stats(ctx)
 
     for i in range(args.warmup):
         toks, st = step()
@@ -331,7 +331,7 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     sent = mk.mk_count_sentinels(ctx)
-    stats = mk.mk_get_stats(ctx)
+    stats = mk.mk_stats(ctx)
     kernel_name = mk.mk_kernel_name(ctx)
     mk.mk_destroy(ctx)
     sync_latency = None

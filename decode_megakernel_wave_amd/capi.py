@@ -15,8 +15,7 @@ import numpy as np
 
 from . import inputs
 
-# MK_LIBRARY selects another build of the same sources (tuning variants)
-_LIB_PATH = os.environ.get("MK_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmk.so")
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmk.so")
 _lib = None
 
 MK_OK, MK_EINVAL, MK_ENOMEM, MK_EHIP, MK_ESTATE, MK_ERANGE, MK_EOCC, MK_ETIMEOUT, MK_ENAN = 0, -1, -2, -3, -4, -5, -6, -7, -8
@@ -38,7 +37,7 @@ class mk_config(C.Structure):
 
 class mk_options(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("sync_mode", "xcd_replicas", "attn_splits", "trace_steps",
-                                          "watchdog_ms", "grid")]
+                                          "watchdog_us", "grid")]
 
 
 _PP = C.POINTER(C.c_void_p)
@@ -53,7 +52,7 @@ class mk_fault(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("code", "cta", "pc", "op", "step", "layer", "index", "pad")]
 
 
-class mk_stats(C.Structure):
+class mk_stats_t(C.Structure):
     _fields_ = [("gpu_ms", C.c_double), ("steps", C.c_int32), ("pos0", C.c_int32), ("grid", C.c_int32),
                 ("block", C.c_int32), ("lds_bytes", C.c_int32), ("ring_depth", C.c_int32),
                 ("stream_bytes", C.c_int64), ("weight_bytes", C.c_int64), ("kv_bytes_per_pos", C.c_int64),
@@ -84,7 +83,7 @@ SIGNATURES = [
     ("mk_probe_read", C.c_int, [C.c_int, C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.POINTER(C.c_double)]),
     ("mk_probe_barrier", C.c_int, [C.c_int, C.c_void_p, C.c_int32, C.POINTER(C.c_double)]),
     ("mk_position", C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
-    ("mk_get_stats", C.c_int, [C.c_void_p, C.POINTER(mk_stats)]),
+    ("mk_stats", C.c_int, [C.c_void_p, C.POINTER(mk_stats_t)]),
     ("mk_count_sentinels", C.c_int, [C.c_void_p, C.POINTER(C.c_int64)]),
     ("mk_read_trace", C.c_int, [C.c_void_p, C.POINTER(C.c_uint32), C.c_int64, C.POINTER(C.c_int64)]),
     ("mk_debug_streams", C.c_int, [C.c_void_p, C.POINTER(C.c_void_p), C.POINTER(C.c_void_p), C.POINTER(C.c_void_p)]),
@@ -97,7 +96,7 @@ SIGNATURES = [
     ("mk_chain_create", C.c_int, [C.c_int32, C.c_int32, C.c_void_p, C.POINTER(mk_options), C.c_int, C.c_void_p,
                                   C.POINTER(C.c_void_p)]),
     ("mk_chain_run", C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p]),
-    ("mk_chain_stats", C.c_int, [C.c_void_p, C.POINTER(mk_stats)]),
+    ("mk_chain_stats", C.c_int, [C.c_void_p, C.POINTER(mk_stats_t)]),
     ("mk_chain_read_trace", C.c_int, [C.c_void_p, C.POINTER(C.c_uint32), C.c_int64, C.POINTER(C.c_int64)]),
     ("mk_chain_last_error", C.c_char_p, [C.c_void_p]),
     ("mk_chain_destroy", None, [C.c_void_p]),
@@ -273,15 +272,15 @@ def mk_position(ctx):
     return int(p.value), int(t.value)
 
 
-def _stats_dict(s: mk_stats) -> dict:
-    d = {f: getattr(s, f) for f, _ in mk_stats._fields_ if f != "fault"}
+def _stats_dict(s: mk_stats_t) -> dict:
+    d = {f: getattr(s, f) for f, _ in mk_stats_t._fields_ if f != "fault"}
     d["fault"] = {f: getattr(s.fault, f) for f, _ in mk_fault._fields_}
     return d
 
 
-def mk_get_stats(ctx) -> dict:
-    s = mk_stats()
-    _check(lib().mk_get_stats(ctx, C.byref(s)), ctx)
+def mk_stats(ctx) -> dict:
+    s = mk_stats_t()
+    _check(lib().mk_stats(ctx, C.byref(s)), ctx)
     return _stats_dict(s)
 
 
@@ -356,7 +355,7 @@ def mk_chain_run(ch, x0, y) -> None:
 
 
 def mk_chain_stats(ch) -> dict:
-    s = mk_stats()
+    s = mk_stats_t()
     _check(lib().mk_chain_stats(ch, C.byref(s)), ch, chain=True)
     return _stats_dict(s)
 

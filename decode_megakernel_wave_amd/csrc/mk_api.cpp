@@ -15,6 +15,7 @@
 #include <vector>
 
 #include "mk.h"
+#include "mk_diag.h"
 #include "mk_layout.h"
 #include "mk_plan.h"
 
@@ -83,7 +84,7 @@ struct Engine {
   KParams* d_kp = nullptr;
   KParams h_kp{};
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
-  mk_stats last{};
+  mk_stats_t last{};
   std::vector<void*> allocs;
 
   int fail(int code, const std::string& msg) {
@@ -134,7 +135,7 @@ int sanitize_options(const mk_options* in, mk_options* out) {
   if (out->sync_mode != MK_SYNC_SENTINEL && out->sync_mode != MK_SYNC_COUNTER) return MK_EINVAL;
   if (!(out->xcd_replicas == 1 || out->xcd_replicas == 2 || out->xcd_replicas == 4 || out->xcd_replicas == 8)) return MK_EINVAL;
   if (out->attn_splits < 0 || out->attn_splits > 64) return MK_EINVAL;
-  if (out->trace_steps < 0 || out->watchdog_ms <= 0 || out->grid < 0) return MK_EINVAL;
+  if (out->trace_steps < 0 || out->watchdog_us <= 0 || out->grid < 0) return MK_EINVAL;
   return MK_OK;
 }
 
@@ -250,7 +251,7 @@ void fill_common_params(Engine& g, KParams& k) {
   k.R = p.R;
   k.sync_mode = p.sync_mode;
   k.lm_slots = p.lm_slots;
-  k.watchdog_ticks = (uint64_t)g.opt.watchdog_ms * 100000ull;  // 100 MHz wall clock
+  k.watchdog_ticks = (uint64_t)g.opt.watchdog_us * 100ull;  // 100 MHz wall clock
   k.poll_sleep = getenv("MK_POLL_SLEEP") ? atoi(getenv("MK_POLL_SLEEP")) : 0;
 }
 
@@ -505,7 +506,7 @@ int mk_default_options(mk_options* o) {
   o->xcd_replicas = 8;
   o->attn_splits = 0;
   o->trace_steps = 0;
-  o->watchdog_ms = 2000;
+  o->watchdog_us = 2000000;
   o->grid = 0;
   return MK_OK;
 }
@@ -743,7 +744,7 @@ int mk_position(const mk_ctx* c, int32_t* pos, int32_t* next_token) {
   return MK_OK;
 }
 
-int mk_get_stats(const mk_ctx* c, mk_stats* out) {
+int mk_stats(const mk_ctx* c, mk_stats_t* out) {
   if (!c || !out) return MK_EINVAL;
   *out = c->g.last;
   return MK_OK;
@@ -948,7 +949,7 @@ int mk_chain_debug_ts(mk_chain* ch, uint64_t* host, int64_t capacity) {
   return MK_OK;
 }
 
-int mk_chain_stats(const mk_chain* ch, mk_stats* out) {
+int mk_chain_stats(const mk_chain* ch, mk_stats_t* out) {
   if (!ch || !out) return MK_EINVAL;
   *out = ch->g.last;
   return MK_OK;

@@ -81,6 +81,16 @@ M2B = ModelConfig("2b", n_layers=24, d_model=2048, n_heads=16, n_kv_heads=8,
 M2B_TP8 = ModelConfig("2b-tp8-shard", n_layers=24, d_model=2048, n_heads=2, n_kv_heads=1,
                       head_dim=128, ffn=1024, vocab=16032)
 
+# Two layers of the ~2B decoder's geometry (d 2048, 16 query / 8 kv heads of
+# 128, vocab cut to 4096): small enough for the float64 oracle at long
+# prompts, shaped like the ~2B model in every GEMV and attention path.  The
+# first keeps the ~2B SwiGLU width (8192); the second narrows it to 2048 so the
+# oracle can prefill an 8192-token prompt in test time.
+M2B_GEOM_L2 = ModelConfig("2b-geometry-2-layers", n_layers=2, d_model=2048, n_heads=16, n_kv_heads=8,
+                          head_dim=128, ffn=8192, vocab=4096)
+M2B_GEOM_L2_NARROW = ModelConfig("2b-geometry-2-layers-ffn2048", n_layers=2, d_model=2048, n_heads=16,
+                                 n_kv_heads=8, head_dim=128, ffn=2048, vocab=4096)
+
 WORKLOADS = {
     "tiny": Workload(TINY, 32, 16),
     "0.5b": Workload(M05, 128, 256),

@@ -67,7 +67,7 @@ typedef struct mk_options {
   int32_t xcd_replicas;  /* copies of re-read activation vectors: 1, 2, 4 or 8 (default 8) */
   int32_t attn_splits;   /* sequence splits per kv head, 1..64 (0 = choose) */
   int32_t trace_steps;   /* record a per-instruction time journal for the first N steps (0 = off) */
-  int32_t watchdog_ms;   /* per-wait timeout inside the kernel (default 2000) */
+  int32_t watchdog_us;   /* per-wait timeout inside the kernel, microseconds (default 2000000) */
   int32_t grid;          /* workgroups to launch (0 = CUs x occupancy; larger values are refused) */
 } mk_options;
 
@@ -95,7 +95,7 @@ typedef struct mk_fault {
   int32_t cta, pc, op, step, layer, index, pad;
 } mk_fault;
 
-typedef struct mk_stats {
+typedef struct mk_stats_t {
   double gpu_ms;             /* duration of the last monokernel launch (HIP events on the bound stream) */
   int32_t steps;             /* decode steps in that launch */
   int32_t pos0;              /* first position of that launch */
@@ -106,30 +106,53 @@ typedef struct mk_stats {
   int64_t algo_bytes;        /* algorithmic bytes of the last launch: sum over its steps */
   int32_t n_cu, occupancy;
   mk_fault fault;
-} mk_stats;
+} mk_stats_t;
 
 typedef struct mk_ctx mk_ctx;
 
+/* Fill *opts with the defaults (sentinel sync, 8 replicas, chosen splits, no
+ * trace, 2 s watchdog, full grid).  MK_EINVAL for NULL. */
 int mk_default_options(mk_options* opts);
 
 /* Create a context on `device`, enqueueing on `hip_stream` (NULL = default
- * stream).  Builds the per-workgroup instruction lists and allocates all
- * device memory the library needs (repacked weights, KV cache, sync buffers). */
+ * stream).  Sizes the one-wave launch as "8 - Ecrire son megakernel" (section
+ * 8.3) prescribes -- dynamic LDS set, occupancy queried, grid = CUs x
+ * occupancy -- and builds the per-workgroup instruction lists of section 8.2
+ * for one decode step; allocates all device memory the library needs
+ * (repacked weights, KV cache of max_seq positions, sync buffers).  *out is a
+ * context owned by the library until mk_destroy.  Errors: MK_EINVAL (shape or
+ * option outside the documented limits, or a device that is not gfx950),
+ * MK_EOCC (the kernel does not fit a CU, or opts->grid exceeds CUs x
+ * occupancy), MK_ENOMEM, MK_EHIP; text from mk_last_error(NULL). */
 int mk_create(const mk_config* cfg, const mk_options* opts, int device, void* hip_stream, mk_ctx** out);
 
-/* Copy and repack the weights (device pointers).  Synchronises. */
+/* Copy and repack the weights (device pointers, borrowed for the call only)
+ * into the per-wavefront streams the monokernel reads in order, so weights
+ * flow from HBM without interruption ("7 - AMD et le monokernel", section
+ * 7.5).  Resets the generation state (position 0).  Errors: MK_EINVAL (a NULL
+ * pointer), MK_ENOMEM, MK_EHIP.  Synchronises. */
 int mk_load_weights(mk_ctx* ctx, const mk_weights* w);
 
-/* Run the prompt ids[0..n) (host) at positions 0..n-1 through the monokernel,
- * token by token, filling the KV cache; *t0_out = the token chosen after the
- * prompt (greedy, or drawn when sampling is on: mk_set_sampling).  Resets the
- * generation state.  Synchronises. */
+/* Prefill ("7 - AMD et le monokernel", section 7.1 names prefill among the
+ * single kernel's duties): run the prompt ids[0..n) (host, each in [0,
+ * vocab)) at positions 0..n-1, filling the KV cache; *t0_out = the token
+ * chosen after the prompt (greedy, or drawn when sampling is on:
+ * mk_set_sampling).  The prompt runs through the monokernel one
+ * teacher-forced step per token.  Resets the generation state; afterwards
+ * the position is n.  Errors: MK_ESTATE (no weights loaded), MK_EINVAL
+ * (n < 1 or NULL), MK_ERANGE (n > max_seq or an id outside the vocabulary),
+ * MK_ETIMEOUT, MK_ENAN, MK_EHIP.  Synchronises. */
 int mk_prefill(mk_ctx* ctx, const int32_t* ids, int32_t n, int32_t* t0_out);
 
-/* Decode n_steps tokens (greedy, or drawn when sampling is on) in ONE launch.
- * Step s consumes the previous token at position pos+s.  tokens_out (host, n_steps) receives the tokens;
+/* Decode ("7 - AMD et le monokernel", section 7.1: one persistent kernel,
+ * no return to the host between tokens): n_steps tokens (greedy, or drawn
+ * when sampling is on) in ONE launch.  Step s consumes the previous token at
+ * position pos+s.  tokens_out (host, n_steps) receives the tokens;
  * logits_out (host, n_steps*vocab floats, or NULL) receives every step's
- * logits.  Synchronises. */
+ * logits.  Errors: MK_ESTATE (before mk_prefill), MK_EINVAL (n_steps < 1),
+ * MK_ERANGE (pos + n_steps > max_seq), MK_ETIMEOUT (the device watchdog
+ * fired; the context then needs mk_prefill again), MK_ENAN (a NaN logit;
+ * tokens are still returned), MK_EHIP.  Synchronises. */
 int mk_decode(mk_ctx* ctx, int32_t n_steps, int32_t* tokens_out, float* logits_out);
 
 /* Like mk_decode, but step s consumes tokens_in[s] (host) instead of the
@@ -138,7 +161,10 @@ int mk_decode(mk_ctx* ctx, int32_t n_steps, int32_t* tokens_out, float* logits_o
 int mk_decode_forced(mk_ctx* ctx, int32_t n_steps, const int32_t* tokens_in,
                      int32_t* tokens_out, float* logits_out);
 
-/* Prefill then decode: tokens_out (host) receives n_steps + 1 tokens: t0..t_n. */
+/* Generation as "7 - AMD et le monokernel" (section 7.1) describes it --
+ * prefill, then decode with the kernel's own token choice: mk_prefill(ids)
+ * then mk_decode(n_steps); tokens_out (host) receives n_steps + 1 tokens
+ * t0..t_n.  Errors: those of the two calls. */
 int mk_generate(mk_ctx* ctx, const int32_t* ids, int32_t n_prompt, int32_t n_steps, int32_t* tokens_out);
 
 /* Token choice of every later step (prefill's t0 included): top_k = 1 (the
@@ -174,65 +200,35 @@ int mk_rewind(mk_ctx* ctx, int32_t pos);
 /* Current position and the token the next decode step consumes. */
 int mk_position(const mk_ctx* ctx, int32_t* pos, int32_t* next_token);
 
-int mk_get_stats(const mk_ctx* ctx, mk_stats* out);
+/* Figures of the last launch: GPU time from HIP events on the bound stream,
+ * algorithmic bytes (the roofline numerator of "7 - AMD et le monokernel",
+ * section 7.5: weights plus the K/V read per token), launch shape and the
+ * watchdog's fault record ("8 - Ecrire son megakernel", section 8.7).  No
+ * device work.  MK_EINVAL for NULL. */
+int mk_stats(const mk_ctx* ctx, mk_stats_t* out);
 
-/* Count words still holding a sentinel in the sync buffers of the last step
- * of the last launch and in the KV cache positions it wrote.  0 after a good run. */
-int mk_count_sentinels(mk_ctx* ctx, int64_t* count);
-
-/* Copy the time journal of the last launch into host memory.  Each record is
- * 8 uint32: {cta, step, pc, op | layer << 8, t_wait_lo, t_ready - t_wait,
- * t_done - t_wait, xcc}, in ticks of the 100 MHz device wall clock; unused
- * records are zero.  *n_records receives the record count (capacity query if
- * host_buf is NULL). */
-int mk_read_trace(mk_ctx* ctx, uint32_t* host_buf, int64_t capacity_records, int64_t* n_records);
-
-/* Diagnostics.  Copy n_words 32-bit words of the sync-buffer arena starting
- * at word_off into host memory.  mk_debug_layout gives the word offsets of
- * its regions: [0] xa, [1] xm, [2] q, [3] o, [4] m, [5] att_o, [6] att_ml,
- * [7] argmax keys (uint64), [8] arena size, [9] attention merge counters
- * (uint32 [n_layers][n_kv_heads]), [10] per-workgroup top-k keys of sampling
- * (uint64 [3][replicas][workgroups][16]). */
-int mk_debug_layout(const mk_ctx* ctx, int64_t* offsets /* [16] */);
-int mk_debug_arena(mk_ctx* ctx, int64_t word_off, int64_t n_words, uint32_t* host);
-/* (step << 16) | (pc + 1) of the last instruction each workgroup finished in
- * the last launch; host receives `grid` words. */
-int mk_debug_progress(mk_ctx* ctx, uint32_t* host, int32_t capacity);
-
-/* Device addresses of the repacked weight streams: base, per-wavefront chunk
- * offsets [grid * 8] (int64) and chunk counts [grid * 8] (int32). */
-int mk_debug_streams(const mk_ctx* ctx, const void** base, const void** wave_off, const void** wave_n);
-
-/* Fine timestamps of step 0 of the last launch (recorded only when the
- * environment variable MK_DEBUG_TS is set at run time): per workgroup and
- * instruction, 8 uint64 device-clock (100 MHz) marks taken by thread 0
- * (wavefront 0) {0 instruction start, 1 inputs polled, 2 inputs staged (after
- * the barrier), 3 op end, 4 failure check done, 5 GEMV: activations in
- * registers / attention: the wavefront's positions done, 6 GEMV: the
- * wavefront's own rows done / attention: split partials published, 7 GEMV:
- * first weight chunk read / attention: wavefront partials combined}; zero
- * where not recorded.  capacity is in uint64 and must be at least
- * grid * max_ins_per_cta * 8. */
-int mk_debug_ts(mk_ctx* ctx, uint64_t* host, int64_t capacity);
-
+/* Text of the context's last error (of the last failed mk_create or probe
+ * for NULL).  The string belongs to the library. */
 const char* mk_last_error(const mk_ctx* ctx);
+/* Free every device buffer of the context (synchronises its stream first). */
 void mk_destroy(mk_ctx* ctx);
 
 /* ---- GEMV-tanh chain microbenchmark ------------------------------------
  * stages dependent stages y_i = tanh(W_i y_{i-1}) (W_i fp16 [n, n] row-major,
  * y fp32) spread over all workgroups of one persistent launch, with the same
- * streaming and synchronisation as the decoder.  W is a device pointer to
- * [stages][n][n] fp16 (borrowed during mk_chain_create only). */
+ * streaming and synchronisation as the decoder: the per-stage cost of a
+ * dependent handoff that "7 - AMD et le monokernel" (section 7.3) compares
+ * between an atomic grid barrier and the NaN sentinel.  W is a device pointer
+ * to [stages][n][n] fp16 (borrowed during mk_chain_create only); n a multiple
+ * of 4 in [4, 16384].  Errors as for mk_create / mk_decode. */
 typedef struct mk_chain mk_chain;
 int mk_chain_create(int32_t n, int32_t stages, const void* W, const mk_options* opts,
                     int device, void* hip_stream, mk_chain** out);
-/* x0: device [n] fp32; y: device [stages][n] fp32 (written).  Synchronises. */
+/* x0: device [n] fp32; y: device [stages][n] fp32 (written, caller-owned).
+ * One launch.  Synchronises. */
 int mk_chain_run(mk_chain* ch, const float* x0, float* y);
-int mk_chain_stats(const mk_chain* ch, mk_stats* out);
-/* Time journal of the last chain run (same record format as mk_read_trace). */
-int mk_chain_read_trace(mk_chain* ch, uint32_t* host_buf, int64_t capacity_records, int64_t* n_records);
-/* Fine timestamps of step 0 of the last chain run (layout of mk_debug_ts). */
-int mk_chain_debug_ts(mk_chain* ch, uint64_t* host, int64_t capacity);
+/* Figures of the last chain run (layout of mk_stats_t). */
+int mk_chain_stats(const mk_chain* ch, mk_stats_t* out);
 const char* mk_chain_last_error(const mk_chain* ch);
 void mk_chain_destroy(mk_chain* ch);
 
@@ -246,23 +242,6 @@ typedef struct mk_plan_info {
   int32_t specialised;       /* 1: the schedule runs on a specialised monokernel (see mk_kernel_name) */
 } mk_plan_info;
 
-/* Calibration probes: the launch cost, the practical HBM read ceiling and the naive grid
- * barrier that "7 - AMD et le monokernel" (section 7.3) compares the NaN sentinel against.
- * Each runs on `hip_stream` of `device` and synchronises; errors: MK_EINVAL (arguments), MK_EHIP (HIP failure), MK_EOCC, MK_ETIMEOUT;
- * text from mk_last_error(NULL).
- * mk_probe_launch: n_launches empty-kernel launches back to back then one synchronisation
- *   (host microseconds per launch -> *us_pipelined), and n_launches launch + synchronise
- *   pairs (-> *us_round_trip).
- * mk_probe_read: reads `bytes` (a multiple of 16, 16-byte aligned device buffer, borrowed)
- *   `repeats` times with nontemporal 16-byte loads from 8 workgroups per CU; GB/s from HIP
- *   events (one untimed warm-up pass first).
- * mk_probe_barrier: `rounds` (1..1e6) grid barriers of one workgroup per CU, each a release,
- *   an atomic add to one counter and system-scope polls until every workgroup has arrived;
- *   microseconds per barrier on the device clock.  A round that does not complete within 1 s
- *   ends every wait and returns MK_ETIMEOUT. */
-int mk_probe_launch(int device, void* hip_stream, int32_t n_launches, double* us_pipelined, double* us_round_trip);
-int mk_probe_read(int device, void* hip_stream, const void* buf, int64_t bytes, int32_t repeats, double* gb_per_s);
-int mk_probe_barrier(int device, void* hip_stream, int32_t rounds, double* us_per_barrier);
 
 /* Build the schedule for n_cta workgroups and check it: every consumed
  * unit has exactly one producer earlier in the step, counters match the

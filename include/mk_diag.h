@@ -1,0 +1,88 @@
+/*
+ * mk_diag.h -- diagnostics and calibration probes of the decode monokernel
+ * library (include/mk.h holds the decoding calls).
+ *
+ * These calls read back what the product calls leave behind (sentinel counts,
+ * the per-instruction time journal, the sync-buffer arena, fine per-op marks)
+ * or run stand-alone calibration kernels.  "8 - Ecrire son megakernel"
+ * (section 8.7) asks for exactly these aids when a megakernel is debugged: a
+ * trace of every instruction's start and end and a record of where each
+ * workgroup stood.  Conventions are those of mk.h: MK_OK or a negative code,
+ * host buffers owned by the caller, the context's stream synchronised before
+ * returning.
+ */
+#ifndef MK_DIAG_H
+#define MK_DIAG_H
+
+#include "mk.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Count words still holding a sentinel in the sync buffers of the last step
+ * of the last launch and in the KV cache positions it wrote.  0 after a good run. */
+int mk_count_sentinels(mk_ctx* ctx, int64_t* count);
+
+/* Copy the time journal of the last launch into host memory.  Each record is
+ * 8 uint32: {cta, step, pc, op | layer << 8, t_wait_lo, t_ready - t_wait,
+ * t_done - t_wait, xcc}, in ticks of the 100 MHz device wall clock; unused
+ * records are zero.  *n_records receives the record count (capacity query if
+ * host_buf is NULL). */
+int mk_read_trace(mk_ctx* ctx, uint32_t* host_buf, int64_t capacity_records, int64_t* n_records);
+
+/* Diagnostics.  Copy n_words 32-bit words of the sync-buffer arena starting
+ * at word_off into host memory.  mk_debug_layout gives the word offsets of
+ * its regions: [0] xa, [1] xm, [2] q, [3] o, [4] m, [5] att_o, [6] att_ml,
+ * [7] argmax keys (uint64), [8] arena size, [9] attention merge counters
+ * (uint32 [n_layers][n_kv_heads]), [10] per-workgroup top-k keys of sampling
+ * (uint64 [3][replicas][workgroups][16]). */
+int mk_debug_layout(const mk_ctx* ctx, int64_t* offsets /* [16] */);
+int mk_debug_arena(mk_ctx* ctx, int64_t word_off, int64_t n_words, uint32_t* host);
+/* (step << 16) | (pc + 1) of the last instruction each workgroup finished in
+ * the last launch; host receives `grid` words. */
+int mk_debug_progress(mk_ctx* ctx, uint32_t* host, int32_t capacity);
+
+/* Device addresses of the repacked weight streams: base, per-wavefront chunk
+ * offsets [grid * 8] (int64) and chunk counts [grid * 8] (int32). */
+int mk_debug_streams(const mk_ctx* ctx, const void** base, const void** wave_off, const void** wave_n);
+
+/* Fine timestamps of step 0 of the last launch (recorded only when the
+ * environment variable MK_DEBUG_TS is set at run time): per workgroup and
+ * instruction, 8 uint64 device-clock (100 MHz) marks taken by thread 0
+ * (wavefront 0) {0 instruction start, 1 inputs polled, 2 inputs staged (after
+ * the barrier), 3 op end, 4 failure check done, 5 GEMV: activations in
+ * registers / attention: the wavefront's positions done, 6 GEMV: the
+ * wavefront's own rows done / attention: split partials published, 7 GEMV:
+ * first weight chunk read / attention: wavefront partials combined}; zero
+ * where not recorded.  capacity is in uint64 and must be at least
+ * grid * max_ins_per_cta * 8. */
+int mk_debug_ts(mk_ctx* ctx, uint64_t* host, int64_t capacity);
+
+/* Time journal of the last chain run (same record format as mk_read_trace). */
+int mk_chain_read_trace(mk_chain* ch, uint32_t* host_buf, int64_t capacity_records, int64_t* n_records);
+/* Fine timestamps of step 0 of the last chain run (layout of mk_debug_ts). */
+int mk_chain_debug_ts(mk_chain* ch, uint64_t* host, int64_t capacity);
+
+/* Calibration probes: the launch cost, the practical HBM read ceiling and the naive grid
+ * barrier that "7 - AMD et le monokernel" (section 7.3) compares the NaN sentinel against.
+ * Each runs on `hip_stream` of `device` and synchronises; errors: MK_EINVAL (arguments), MK_EHIP (HIP failure), MK_EOCC, MK_ETIMEOUT;
+ * text from mk_last_error(NULL).
+ * mk_probe_launch: n_launches empty-kernel launches back to back then one synchronisation
+ *   (host microseconds per launch -> *us_pipelined), and n_launches launch + synchronise
+ *   pairs (-> *us_round_trip).
+ * mk_probe_read: reads `bytes` (a multiple of 16, 16-byte aligned device buffer, borrowed)
+ *   `repeats` times with nontemporal 16-byte loads from 8 workgroups per CU; GB/s from HIP
+ *   events (one untimed warm-up pass first).
+ * mk_probe_barrier: `rounds` (1..1e6) grid barriers of one workgroup per CU, each a release,
+ *   an atomic add to one counter and system-scope polls until every workgroup has arrived;
+ *   microseconds per barrier on the device clock.  A round that does not complete within 1 s
+ *   ends every wait and returns MK_ETIMEOUT. */
+int mk_probe_launch(int device, void* hip_stream, int32_t n_launches, double* us_pipelined, double* us_round_trip);
+int mk_probe_read(int device, void* hip_stream, const void* buf, int64_t bytes, int32_t repeats, double* gb_per_s);
+int mk_probe_barrier(int device, void* hip_stream, int32_t rounds, double* us_per_barrier);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_DIAG_H */

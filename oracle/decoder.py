@@ -186,16 +186,6 @@ class Decoder:
             logs.append(lg)
         return t0, np.array(toks, dtype=np.int32), np.array(logs)
 
-    def forced(self, ids, feed):
-        """Prefill ``ids``, then run the tokens ``feed`` at positions P, P+1, ...
-
-        Returns ``(logits_after_prompt, logits[len(feed), V])``.
-        """
-        P = len(ids)
-        l0 = self.prefill(ids)
-        logs = [self.step(int(t), P + s) for s, t in enumerate(feed)]
-        return l0, np.array(logs)
-
 
 def top2_margin(logits: np.ndarray) -> np.ndarray:
     """Difference between the largest and second-largest logit along the last axis."""

@@ -110,6 +110,6 @@ def test_calls_out_of_order_or_range_fail_cleanly():
             mk.mk_decode(ctx, 13)  # 4 + 13 > 16
         assert e.value.code == mk.MK_ERANGE
         assert len(mk.mk_decode(ctx, 12)) == 12  # exactly fills the cache
-        assert mk.mk_get_stats(ctx)["fault"]["code"] == 0
+        assert mk.mk_stats(ctx)["fault"]["code"] == 0
     finally:
         mk.mk_destroy(ctx)

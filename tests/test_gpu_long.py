@@ -66,7 +66,7 @@ def test_2b_long_context_consistency():
         mk.mk_rewind(ctx, P_LONG)
         a, la = mk.mk_decode(ctx, 4, vocab=model.vocab)
         b, lb = mk.mk_decode(ctx, 4, vocab=model.vocab)
-        st = mk.mk_get_stats(ctx)
+        st = mk.mk_stats(ctx)
     finally:
         mk.mk_destroy(ctx)
         torch.cuda.empty_cache()

@@ -34,7 +34,7 @@ def _forced_run(tiny, **opts):
         feed = np.concatenate([[t0_ref], toks_ref[:-1]])
         toks, logits = mk.mk_decode_forced(ctx, feed, vocab=CFG.vocab)
         sent = mk.mk_count_sentinels(ctx)
-        stats = mk.mk_get_stats(ctx)
+        stats = mk.mk_stats(ctx)
     finally:
         mk.mk_destroy(ctx)
     return t0, toks, logits, sent, stats

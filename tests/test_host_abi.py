@@ -1,6 +1,6 @@
 """Host-side checks of the C ABI (no GPU needed).
 
-- libmk.so loads and exports exactly the functions include/mk.h declares;
+- libmk.so loads and exports exactly the functions include/*.h declare;
 - the ctypes mirrors of the ABI structs have the C compiler's layout;
 - the schedule builder accepts every model at the grids the kernel runs at,
   conserves the weight bytes (every matrix byte streamed once per step), fits
@@ -8,6 +8,7 @@
   shapes and options with a reason.
 """
 import ctypes as C
+import glob
 import os
 import re
 import shutil
@@ -20,12 +21,16 @@ from decode_megakernel_wave_amd import capi, inputs
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mk.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(mk_\w+)\s*\(", text, flags=re.M))
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(mk_\w+)\s*\(", text, flags=re.M))
+    return names
 
 
 def test_library_exports_every_declared_function():
@@ -42,10 +47,10 @@ def test_library_exports_nothing_undeclared():
                          check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if re.search(r" T mk_\w+$", ln)}
     extra = sorted(exported - _declared())
-    assert not extra, f"exported but not declared in include/mk.h: {extra}"
+    assert not extra, f"exported but not declared in include/*.h: {extra}"
 
 
-_STRUCTS = ["mk_config", "mk_options", "mk_weights", "mk_fault", "mk_stats", "mk_plan_info"]
+_STRUCTS = ["mk_config", "mk_options", "mk_weights", "mk_fault", "mk_stats_t", "mk_plan_info"]
 
 
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
@@ -75,7 +80,7 @@ def test_ctypes_struct_layout_matches_header(tmp_path):
 def test_default_options():
     o = mk.mk_default_options()
     assert (o.sync_mode, o.xcd_replicas, o.attn_splits, o.grid) == (mk.MK_SYNC_SENTINEL, 8, 0, 0)
-    assert o.watchdog_ms > 0 and o.trace_steps == 0
+    assert o.watchdog_us > 0 and o.trace_steps == 0
 
 
 def _matrix_params(m: inputs.ModelConfig) -> int:
@@ -167,7 +172,7 @@ def test_plan_rejects(model, max_seq, grid, opts, reason):
 
 
 @pytest.mark.parametrize("field,value", [("xcd_replicas", 3), ("attn_splits", 65), ("sync_mode", 2),
-                                         ("watchdog_ms", 0), ("grid", -1), ("attn_splits", -1)])
+                                         ("watchdog_us", 0), ("grid", -1), ("attn_splits", -1)])
 def test_plan_rejects_options(field, value):
     w = inputs.WORKLOADS["tiny"]
     with pytest.raises(mk.MkError) as e:

@@ -316,10 +316,20 @@ def test_pins_reject_planted_mistakes_in_helpers():
 
 
 @pytest.mark.parametrize("mistake", ["kv_group_interleaved", "no_kv_rounding", "no_rope_on_k",
-                                     "pos_off_by_one", "silu_scaled"])
+                                     "pos_off_by_one", "silu_scaled", "transposed_wq", "transposed_wo"])
 def test_brute_force_rejects_planted_mistakes_in_decoder(monkeypatch, mistake):
     cfg = SMALL_GQA
-    if mistake == "kv_group_interleaved":
+    if mistake.startswith("transposed_"):
+        # a square weight (64 x 64 here) used as its transpose when the oracle loads it
+        key = mistake[len("transposed_"):]
+        orig_init = od.Decoder.__init__
+
+        def init_transposed(self, *a, **k):
+            orig_init(self, *a, **k)
+            for L in self.layers:
+                L[key] = np.ascontiguousarray(L[key].T)
+        monkeypatch.setattr(od.Decoder, "__init__", init_transposed)
+    elif mistake == "kv_group_interleaved":
         monkeypatch.setattr(od.Decoder, "kv_head_of", lambda self, j: j % self.n_kv)
     elif mistake == "no_kv_rounding":
         monkeypatch.setattr(od, "fp16_round", lambda x: np.asarray(x, dtype=np.float64))

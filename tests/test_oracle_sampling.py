@@ -29,6 +29,16 @@ def test_philox_known_answers():
     assert check_philox(osm.philox4x32_10)
 
 
+def test_uniform_pinned_to_first_known_answer_vector():
+    # seed 0 is key (0, 0) and position 0 is counter (0, 0, 0, 0): the first published
+    # known-answer vector, whose first output word is the uniform's numerator
+    with open(GOLDEN) as f:
+        kat = json.load(f)["vectors"][0]
+    assert kat["counter"] == ["00000000"] * 4 and kat["key"] == ["00000000"] * 2
+    assert osm.uniform(0, 0) == int(kat["out"][0], 16) / 2.0 ** 32
+    assert osm.uniform(0, 0) == 0x6627E8D5 / 2.0 ** 32
+
+
 def test_uniform_range_and_inputs():
     us = [osm.uniform(1234, p) for p in range(200)]
     assert all(0.0 <= u < 1.0 for u in us)
