@@ -90,6 +90,7 @@ SIGNATURES = [
     ("mk_debug_layout", C.c_int, [C.c_void_p, C.POINTER(C.c_int64)]),
     ("mk_debug_arena", C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.POINTER(C.c_uint32)]),
     ("mk_debug_progress", C.c_int, [C.c_void_p, C.POINTER(C.c_uint32), C.c_int32]),
+    ("mk_debug_force_stall", C.c_int, [C.c_void_p, C.c_int32]),
     ("mk_debug_ts", C.c_int, [C.c_void_p, C.POINTER(C.c_uint64), C.c_int64]),
     ("mk_last_error", C.c_char_p, [C.c_void_p]),
     ("mk_destroy", None, [C.c_void_p]),
@@ -329,6 +330,11 @@ def mk_debug_progress(ctx, grid: int) -> np.ndarray:
     buf = np.zeros(grid, dtype=np.uint32)
     _check(lib().mk_debug_progress(ctx, buf.ctypes.data_as(C.POINTER(C.c_uint32)), grid), ctx)
     return buf
+
+
+def mk_debug_force_stall(ctx, cta: int) -> None:
+    """Arm the failure-path test for the next launch (see include/mk_diag.h)."""
+    _check(lib().mk_debug_force_stall(ctx, int(cta)), ctx)
 
 
 def mk_last_error(ctx=None) -> str:

@@ -76,6 +76,8 @@ struct Engine {
   uint32_t* d_trace = nullptr;
   uint32_t* d_progress = nullptr;
   uint64_t* d_ts = nullptr;
+  uint32_t* d_stall = nullptr;  // a word left at the sentinel for the failure-path test
+  int stall_cta = -1;           // armed for the next launch only
   int64_t trace_words = 0;
   int32_t* d_tokens = nullptr;
   int32_t* d_forced = nullptr;
@@ -196,6 +198,7 @@ int upload_plan(Engine& g) {
   CHK(g.alloc(&g.d_counters, std::max(1, p.n_sync) * sizeof(uint32_t)));
   CHK(g.alloc(&g.d_fault, sizeof(Fault)));
   CHK(g.alloc(&g.d_abort, sizeof(uint32_t)));
+  CHK(g.alloc(&g.d_stall, sizeof(uint32_t)));
   CHK(g.alloc(&g.d_kp, sizeof(KParams)));
   CHK(g.alloc(&g.d_progress, (size_t)g.grid * 4));
   CHK(g.alloc(&g.d_ts, (size_t)g.grid * p.max_ins * 8 * 8));
@@ -253,6 +256,8 @@ void fill_common_params(Engine& g, KParams& k) {
   k.lm_slots = p.lm_slots;
   k.watchdog_ticks = (uint64_t)g.opt.watchdog_us * 100ull;  // 100 MHz wall clock
   k.poll_sleep = getenv("MK_POLL_SLEEP") ? atoi(getenv("MK_POLL_SLEEP")) : 0;
+  k.stall_cta = g.stall_cta;
+  k.stall_word = g.d_stall;
 }
 
 // Reset sync state, launch once, wait, collect the fault record.
@@ -261,6 +266,8 @@ int launch(Engine& g, KParams& k, int n_steps) {
   HIPCHK(g, mk_launch_fill32((uint32_t*)g.d_fault, sizeof(Fault) / 4, 0u, g.stream));
   HIPCHK(g, mk_launch_fill32(g.d_abort, 1, 0u, g.stream));
   HIPCHK(g, mk_launch_fill32(g.d_progress, g.grid, 0u, g.stream));
+  HIPCHK(g, mk_launch_fill32(g.d_stall, 1, kSent32, g.stream));
+  g.stall_cta = -1;  // one launch only
   if (g.d_trace) HIPCHK(g, mk_launch_fill32(g.d_trace, g.trace_words, 0u, g.stream));
   g.h_kp = k;
   HIPCHK(g, hipMemcpyAsync(g.d_kp, &g.h_kp, sizeof(KParams), hipMemcpyHostToDevice, g.stream));
@@ -813,6 +820,14 @@ int mk_debug_layout(const mk_ctx* c, int64_t* offsets) {
 int mk_debug_arena(mk_ctx* c, int64_t word_off, int64_t n_words, uint32_t* host) {
   if (!c || !host || word_off < 0 || n_words < 0 || word_off + n_words > c->g.arena_words) return MK_EINVAL;
   HIPCHK(c->g, hipMemcpy(host, (uint32_t*)c->g.d_arena + word_off, n_words * 4, hipMemcpyDeviceToHost));
+  return MK_OK;
+}
+
+int mk_debug_force_stall(mk_ctx* c, int32_t cta) {
+  if (!c) return MK_EINVAL;
+  if (cta < 0 || cta >= c->g.grid) return c->g.fail(MK_EINVAL, "no such workgroup");
+  if (c->g.plan.sync_mode != MK_SYNC_SENTINEL) return c->g.fail(MK_EINVAL, "the stall test needs sentinel sync");
+  c->g.stall_cta = cta;
   return MK_OK;
 }
 

@@ -1561,6 +1561,10 @@ __device__ __forceinline__ void op_argmax(Cx& c, const Ins& in) {
   const KParams& kp = *c.kp;
   counter_wait(c, in.sync_in, in.n_in, OP_ARGMAX, kp.L);
   if (!sentinel_mode(c)) cta_sync(c);
+  // Failure-path test (armed by the host for one launch): wait for a word that
+  // is never written, so this wait's watchdog fires and every other workgroup
+  // leaves its own waits through the abort flag.
+  if (c.step == 0 && c.cta == kp.stall_cta && c.tid == 0) (void)poll_f32(c, (const float*)kp.stall_word, OP_ARGMAX, kp.L);
   if (kp.top_k > 1) {
     op_sample(c, in);
     return;

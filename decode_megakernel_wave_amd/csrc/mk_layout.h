@@ -126,13 +126,14 @@ struct KParams {
   float eps;
   uint64_t watchdog_ticks;    // 100 MHz ticks
   int32_t poll_sleep;         // s_sleep units between failed poll rounds (0 = spin)
-  int32_t pad2;
+  int32_t stall_cta;          // diagnostics: this workgroup waits on stall_word in step 0 (-1: none)
   // top-k / temperature sampling (top_k == 1: greedy argmax, the lists are unused)
   uint64_t* lmk;              // [3][R][lm_slots][kMaxTopK] per-workgroup top-k keys
   int64_t lmk_es, lmk_rs;
   int32_t top_k;
   float inv_temp;             // 1 / temperature
   uint32_t seed_lo, seed_hi;  // Philox key
+  const uint32_t* stall_word; // a sync word the host leaves at the sentinel (see stall_cta)
 };
 
 }  // namespace mk

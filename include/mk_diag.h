@@ -43,6 +43,16 @@ int mk_debug_arena(mk_ctx* ctx, int64_t word_off, int64_t n_words, uint32_t* hos
  * the last launch; host receives `grid` words. */
 int mk_debug_progress(mk_ctx* ctx, uint32_t* host, int32_t capacity);
 
+/* Failure-path test: in the next launch only, workgroup `cta` waits in step 0,
+ * before its argmax, for a sync word the host never writes, so that wait's
+ * watchdog fires ("8 - Ecrire son megakernel", section 8.7: a watchdog that
+ * turns a lost dependency into a report) after the context's watchdog_us, the
+ * fault record names that workgroup, and every other workgroup leaves its
+ * own waits through the abort flag: the launch ends normally and returns
+ * MK_ETIMEOUT.  Sentinel sync only (MK_EINVAL otherwise, or for a workgroup
+ * outside the grid). */
+int mk_debug_force_stall(mk_ctx* ctx, int32_t cta);
+
 /* Device addresses of the repacked weight streams: base, per-wavefront chunk
  * offsets [grid * 8] (int64) and chunk counts [grid * 8] (int32). */
 int mk_debug_streams(const mk_ctx* ctx, const void** base, const void** wave_off, const void** wave_n);

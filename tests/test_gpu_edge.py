@@ -7,6 +7,8 @@
 - A one-token prompt decoded until the KV cache is exactly full, against
   the oracle; one more step is refused and leaves the context usable.
 - Calls out of order or out of range fail with the documented codes.
+- The watchdog: a wait the host arms never to be satisfied ends the launch
+  with MK_ETIMEOUT, every workgroup exits, and the context recovers.
 """
 import numpy as np
 import pytest
@@ -113,3 +115,43 @@ def test_calls_out_of_order_or_range_fail_cleanly():
         assert mk.mk_stats(ctx)["fault"]["code"] == 0
     finally:
         mk.mk_destroy(ctx)
+
+
+def test_watchdog_reports_a_lost_dependency_and_every_workgroup_exits():
+    """The failure path, forced from the host: in one launch workgroup 1 waits (step 0, before its
+    argmax) for a sync word the host never writes.  That wait's watchdog fires after watchdog_us,
+    the fault record and the error text name the wait, every other workgroup leaves its own waits
+    through the abort flag, the launch ends normally with MK_ETIMEOUT, the context asks for a new
+    prefill, and the next launch (not armed) decodes normally."""
+    model = inputs.TINY
+    w = inputs.make_weights(model, seed=0)
+    ids = inputs.make_prompt(model, 4, seed=3)
+    ctx = load(mk, model, w, 16, watchdog_us=2000)
+    try:
+        mk.mk_debug_force_stall(ctx, 1)
+        with pytest.raises(mk.MkError) as e:
+            mk.mk_prefill(ctx, ids)
+        assert e.value.code == mk.MK_ETIMEOUT
+        assert "device watchdog" in str(e.value)
+        st = mk.mk_stats(ctx)
+        assert st["fault"]["code"] == mk.MK_ETIMEOUT
+        assert st["fault"]["step"] in (0, 1)
+        # every workgroup stopped by step 1: none ran on past the lost dependency
+        prog = mk.mk_debug_progress(ctx, st["grid"])
+        assert int((prog >> 16).max()) <= 1
+        with pytest.raises(mk.MkError) as e:
+            mk.mk_decode(ctx, 1)
+        assert e.value.code == mk.MK_ESTATE
+        t0 = mk.mk_prefill(ctx, ids)
+        toks = mk.mk_decode(ctx, 4)
+        assert mk.mk_count_sentinels(ctx) == 0
+        assert mk.mk_stats(ctx)["fault"]["code"] == 0
+    finally:
+        mk.mk_destroy(ctx)
+    ref = mk.mk_create(model, max_seq=16)
+    try:
+        mk.mk_load_weights(ref, mk.to_device(w))
+        assert mk.mk_prefill(ref, ids) == t0
+        assert np.array_equal(mk.mk_decode(ref, 4), toks)
+    finally:
+        mk.mk_destroy(ref)
