@@ -56,7 +56,8 @@ class mk_stats_t(C.Structure):
     _fields_ = [("gpu_ms", C.c_double), ("steps", C.c_int32), ("pos0", C.c_int32), ("grid", C.c_int32),
                 ("block", C.c_int32), ("lds_bytes", C.c_int32), ("ring_depth", C.c_int32),
                 ("stream_bytes", C.c_int64), ("weight_bytes", C.c_int64), ("kv_bytes_per_pos", C.c_int64),
-                ("algo_bytes", C.c_int64), ("n_cu", C.c_int32), ("occupancy", C.c_int32), ("fault", mk_fault)]
+                ("algo_bytes", C.c_int64), ("n_cu", C.c_int32), ("occupancy", C.c_int32), ("fault", mk_fault),
+                ("prefill_ms", C.c_double), ("prefill_positions", C.c_int32), ("prefill_grid", C.c_int32)]
 
 
 class mk_plan_info(C.Structure):
@@ -91,6 +92,8 @@ SIGNATURES = [
     ("mk_debug_arena", C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.POINTER(C.c_uint32)]),
     ("mk_debug_progress", C.c_int, [C.c_void_p, C.POINTER(C.c_uint32), C.c_int32]),
     ("mk_debug_force_stall", C.c_int, [C.c_void_p, C.c_int32]),
+    ("mk_debug_kv", C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_uint16),
+                              C.POINTER(C.c_uint16)]),
     ("mk_debug_ts", C.c_int, [C.c_void_p, C.POINTER(C.c_uint64), C.c_int64]),
     ("mk_last_error", C.c_char_p, [C.c_void_p]),
     ("mk_destroy", None, [C.c_void_p]),
@@ -330,6 +333,15 @@ def mk_debug_progress(ctx, grid: int) -> np.ndarray:
     buf = np.zeros(grid, dtype=np.uint32)
     _check(lib().mk_debug_progress(ctx, buf.ctypes.data_as(C.POINTER(C.c_uint32)), grid), ctx)
     return buf
+
+
+def mk_debug_kv(ctx, layer: int, kv_head: int, pos0: int, n: int, head_dim: int):
+    """Cached K and V of positions [pos0, pos0 + n) of one layer and kv head: two float16 [n, head_dim] arrays."""
+    k = np.zeros((n, head_dim), dtype=np.uint16)
+    v = np.zeros((n, head_dim), dtype=np.uint16)
+    _check(lib().mk_debug_kv(ctx, layer, kv_head, pos0, n, k.ctypes.data_as(C.POINTER(C.c_uint16)),
+                             v.ctypes.data_as(C.POINTER(C.c_uint16))), ctx)
+    return k.view(np.float16), v.view(np.float16)
 
 
 def mk_debug_force_stall(ctx, cta: int) -> None:

@@ -39,6 +39,9 @@ hipError_t mk_launch_probe_read(const void* p, int64_t n16, void* sink, int grid
 hipError_t mk_launch_probe_barrier(uint32_t* counter, int rounds, uint64_t deadline_ticks, uint64_t* out, int grid,
                                    hipStream_t s);
 hipError_t mk_probe_barrier_occupancy(int* occupancy);
+int mk_prefill_lds_bytes(int hd);
+hipError_t mk_prefill_attributes(int lds_bytes, int* occupancy);
+hipError_t mk_launch_prefill(const PParams* pp_dev, int grid, int lds_bytes, hipStream_t s);
 }
 
 namespace {
@@ -349,6 +352,15 @@ struct mk_ctx {
   int64_t layout[16] = {0};
   struct Region { int64_t off, words; };
   std::vector<Region> epoch_regions[3];  // per epoch: word ranges that a step fully writes
+  // prompt prefill on MFMA (mk_prefill.hip)
+  bool pf_ok = false;               // the shapes fit the prefill kernel
+  int pf_grid = 0, pf_lds = 0;
+  uint16_t* d_canon = nullptr;      // canonical weights, per layer [wq; wk; wv], wo, wg, wu, wd
+  float *d_pX = nullptr, *d_pQ = nullptr, *d_pO = nullptr, *d_pM = nullptr;
+  int32_t* d_pids = nullptr;
+  uint32_t* d_pbar = nullptr;
+  PParams* d_pp = nullptr;
+  PParams h_pp{};
 };
 
 namespace {
@@ -406,6 +418,98 @@ int ctx_alloc_arena(mk_ctx* c) {
   c->lmp = (uint64_t*)(a + g.lmp_word_off);
   c->att_cnt = (uint32_t*)(a + ocnt);
   c->lmk = (uint64_t*)(a + olmk);
+  return MK_OK;
+}
+
+// Buffers of the MFMA prefill, sized for a prompt of max_seq - 1 positions
+// (the prompt's last token runs through the decode monokernel).  The prefill
+// kernel needs every K dimension (d_model, n_heads * head_dim, ffn) to be a
+// multiple of 8; other shapes prefill through the decode monokernel.
+int ctx_alloc_prefill(mk_ctx* c) {
+  Engine& g = c->g;
+  const mk_config& k = c->cfg;
+  const int qd = k.n_heads * k.head_dim, kvd = k.n_kv_heads * k.head_dim;
+  c->pf_ok = k.d_model % 8 == 0 && k.ffn % 8 == 0 && qd % 8 == 0;
+  if (!c->pf_ok) return MK_OK;
+  c->pf_lds = mk_prefill_lds_bytes(k.head_dim);
+  int occ = 0;
+  hipError_t e = mk_prefill_attributes(c->pf_lds, &occ);
+  if (e != hipSuccess) return g.hip_fail(e, "prefill kernel attributes");
+  if (occ < 1) {
+    c->pf_ok = false;
+    return MK_OK;
+  }
+  c->pf_grid = g.n_cu;  // one workgroup per CU: all resident, so the grid barriers cannot deadlock
+  const int64_t P = std::max(1, k.max_seq - 1);
+  const int64_t per_layer = (int64_t)(qd + 2 * kvd) * k.d_model + (int64_t)k.d_model * qd + 3LL * k.ffn * k.d_model;
+  CHK(g.alloc(&c->d_canon, (size_t)per_layer * k.n_layers * 2));
+  CHK(g.alloc(&c->d_pX, (size_t)P * k.d_model * 4));
+  CHK(g.alloc(&c->d_pQ, (size_t)P * qd * 4));
+  CHK(g.alloc(&c->d_pO, (size_t)P * qd * 4));
+  CHK(g.alloc(&c->d_pM, (size_t)P * k.ffn * 4));
+  CHK(g.alloc(&c->d_pids, (size_t)P * 4));
+  CHK(g.alloc(&c->d_pbar, 256));
+  CHK(g.alloc(&c->d_pp, sizeof(PParams)));
+  return MK_OK;
+}
+
+// Positions [0, n) of a prompt through every layer in one launch of the
+// prefill kernel (MFMA GEMMs, causal attention); fills the KV cache.
+int ctx_prefill_mfma(mk_ctx* c, const int32_t* ids, int n) {
+  Engine& g = c->g;
+  const mk_config& k = c->cfg;
+  HIPCHK(g, hipSetDevice(g.device));
+  HIPCHK(g, hipMemcpyAsync(c->d_pids, ids, (size_t)n * 4, hipMemcpyHostToDevice, g.stream));
+  HIPCHK(g, mk_launch_fill32(c->d_pbar, 1, 0u, g.stream));
+  HIPCHK(g, mk_launch_fill32((uint32_t*)g.d_fault, sizeof(Fault) / 4, 0u, g.stream));
+  HIPCHK(g, mk_launch_fill32(g.d_abort, 1, 0u, g.stream));
+  HIPCHK(g, mk_launch_fill32(g.d_progress, g.grid, 0u, g.stream));
+  PParams& pp = c->h_pp;
+  pp = PParams{};
+  pp.L = k.n_layers;
+  pp.d = k.d_model;
+  pp.nq = k.n_heads;
+  pp.nkv = k.n_kv_heads;
+  pp.hd = k.head_dim;
+  pp.f = k.ffn;
+  pp.max_seq = k.max_seq;
+  pp.P = n;
+  pp.eps = k.rms_eps;
+  pp.canon = c->d_canon;
+  pp.norms = c->d_norms;
+  pp.embed = c->d_embed;
+  pp.ids = c->d_pids;
+  pp.rope = c->d_rope;
+  pp.kc = c->d_kc;
+  pp.vc = c->d_vc;
+  pp.X = c->d_pX;
+  pp.Q = c->d_pQ;
+  pp.O = c->d_pO;
+  pp.M = c->d_pM;
+  pp.barrier = c->d_pbar;
+  pp.abort_flag = g.d_abort;
+  pp.fault = g.d_fault;
+  pp.progress = g.d_progress;
+  pp.watchdog_ticks = (uint64_t)g.opt.watchdog_us * 100ull;
+  HIPCHK(g, hipMemcpyAsync(c->d_pp, &pp, sizeof(PParams), hipMemcpyHostToDevice, g.stream));
+  HIPCHK(g, hipEventRecord(g.ev0, g.stream));
+  HIPCHK(g, mk_launch_prefill(c->d_pp, c->pf_grid, c->pf_lds, g.stream));
+  HIPCHK(g, hipEventRecord(g.ev1, g.stream));
+  HIPCHK(g, hipStreamSynchronize(g.stream));
+  float ms = 0.f;
+  HIPCHK(g, hipEventElapsedTime(&ms, g.ev0, g.ev1));
+  g.last.prefill_ms = ms;
+  g.last.prefill_positions = n;
+  g.last.prefill_grid = c->pf_grid;
+  Fault f{};
+  HIPCHK(g, hipMemcpy(&f, g.d_fault, sizeof(Fault), hipMemcpyDeviceToHost));
+  memcpy(&g.last.fault, &f, sizeof(Fault));
+  if (f.code == MK_ETIMEOUT) {
+    char buf[160];
+    snprintf(buf, sizeof buf, "device watchdog: prefill workgroup %d waited too long at grid barrier %d (op %d, layer %d)",
+             f.cta, f.pc, f.op, f.layer);
+    return g.fail(MK_ETIMEOUT, buf);
+  }
   return MK_OK;
 }
 
@@ -607,6 +711,7 @@ int mk_create(const mk_config* cfg, const mk_options* opts, int device, void* hi
   if ((rc = g.alloc(&g.d_tokens, (size_t)k.max_seq * 4)) != MK_OK) return bail(rc);
   if ((rc = g.alloc(&g.d_forced, (size_t)k.max_seq * 4)) != MK_OK) return bail(rc);
   if ((rc = ctx_alloc_arena(c)) != MK_OK) return bail(rc);
+  if ((rc = ctx_alloc_prefill(c)) != MK_OK) return bail(rc);
   // RoPE table: cos/sin of pos * theta^(-2i/hd), computed in double
   {
     const int hh = k.head_dim / 2;
@@ -649,6 +754,18 @@ int mk_load_weights(mk_ctx* c, const mk_weights* w) {
   }
   mats[7 * L] = (const uint16_t*)w->lm_head;
   CHK(repack(g, mats));
+  if (c->pf_ok) {
+    // canonical copy for the prefill GEMMs: per layer [wq; wk; wv], wo, wg, wu, wd
+    const int qd = k.n_heads * k.head_dim, kvd = k.n_kv_heads * k.head_dim;
+    const size_t d = k.d_model, f = k.ffn;
+    const size_t sz[7] = {qd * d, kvd * d, kvd * d, d * qd, f * d, f * d, d * f};
+    uint16_t* dst = c->d_canon;
+    for (int l = 0; l < L; ++l)
+      for (int m = 0; m < 7; ++m) {
+        HIPCHK(g, hipMemcpyAsync(dst, mats[7 * l + m], sz[m] * 2, hipMemcpyDeviceToDevice, g.stream));
+        dst += sz[m];
+      }
+  }
   const size_t drow = (size_t)k.d_model * 2;
   HIPCHK(g, hipMemcpyAsync(c->d_embed, w->embed, (size_t)k.vocab * drow, hipMemcpyDeviceToDevice, g.stream));
   for (int l = 0; l < L; ++l) {
@@ -669,16 +786,40 @@ int mk_prefill(mk_ctx* c, const int32_t* ids, int32_t n, int32_t* t0_out) {
   if (c->state < ST_LOADED) return c->g.fail(MK_ESTATE, "prefill before mk_load_weights");
   if (n < 1) return c->g.fail(MK_EINVAL, "empty prompt");
   if (n > c->cfg.max_seq) return c->g.fail(MK_ERANGE, "prompt longer than max_seq");
+  for (int i = 0; i < n; ++i)
+    if (ids[i] < 0 || ids[i] >= c->cfg.vocab) return c->g.fail(MK_ERANGE, "token id outside [0, vocab)");
   c->pos = 0;
   c->hist.clear();
-  std::vector<int32_t> toks(n);
-  int rc = ctx_run(c, n, 0, ids, toks.data(), nullptr);
+  c->g.last.prefill_ms = 0;
+  c->g.last.prefill_positions = 0;
+  c->g.last.prefill_grid = 0;
+  // positions 0..n-2 on the MFMA prefill kernel (unless MK_PREFILL_STEPS asks for the
+  // token-by-token path), then the last prompt token through the decode monokernel,
+  // which chooses t0 exactly as every later step is chosen
+  const bool mfma = c->pf_ok && n >= 2 && !getenv("MK_PREFILL_STEPS");
+  const int head = mfma ? n - 1 : 0;
+  int rc = MK_OK;
+  if (mfma) {
+    rc = ctx_prefill_mfma(c, ids, head);
+    if (rc != MK_OK) {
+      c->state = ST_LOADED;
+      return rc;
+    }
+    c->pos = head;
+    c->hist.assign(ids, ids + head);
+  }
+  const double pf_ms = c->g.last.prefill_ms;
+  std::vector<int32_t> toks(n - head);
+  rc = ctx_run(c, n - head, 0, ids + head, toks.data(), nullptr);
+  c->g.last.prefill_ms = pf_ms;
+  c->g.last.prefill_positions = head;
+  c->g.last.prefill_grid = mfma ? c->pf_grid : 0;
   if (rc != MK_OK) {
     c->state = ST_LOADED;
     return rc;
   }
-  advance(c, n, nullptr, ids, toks.data());
-  *t0_out = toks[n - 1];
+  advance(c, n - head, nullptr, ids + head, toks.data());
+  *t0_out = toks[n - head - 1];
   c->state = ST_READY;
   return MK_OK;
 }
@@ -820,6 +961,20 @@ int mk_debug_layout(const mk_ctx* c, int64_t* offsets) {
 int mk_debug_arena(mk_ctx* c, int64_t word_off, int64_t n_words, uint32_t* host) {
   if (!c || !host || word_off < 0 || n_words < 0 || word_off + n_words > c->g.arena_words) return MK_EINVAL;
   HIPCHK(c->g, hipMemcpy(host, (uint32_t*)c->g.d_arena + word_off, n_words * 4, hipMemcpyDeviceToHost));
+  return MK_OK;
+}
+
+int mk_debug_kv(mk_ctx* c, int32_t layer, int32_t kv_head, int32_t pos0, int32_t n, uint16_t* k_out, uint16_t* v_out) {
+  if (!c || !k_out || !v_out) return MK_EINVAL;
+  const mk_config& k = c->cfg;
+  if (layer < 0 || layer >= k.n_layers || kv_head < 0 || kv_head >= k.n_kv_heads || pos0 < 0 || n < 0 ||
+      (int64_t)pos0 + n > k.max_seq)
+    return c->g.fail(MK_EINVAL, "KV range outside the cache");
+  HIPCHK(c->g, hipSetDevice(c->g.device));
+  const int64_t off = (((int64_t)layer * k.n_kv_heads + kv_head) * k.max_seq + pos0) * k.head_dim;
+  const size_t bytes = (size_t)n * k.head_dim * 2;
+  HIPCHK(c->g, hipMemcpy(k_out, c->d_kc + off, bytes, hipMemcpyDeviceToHost));
+  HIPCHK(c->g, hipMemcpy(v_out, c->d_vc + off, bytes, hipMemcpyDeviceToHost));
   return MK_OK;
 }
 

@@ -204,7 +204,7 @@ __device__ __forceinline__ void counter_wait(Cx& c, int sid, int n_in, int op, i
     const uint32_t target = (uint32_t)n_in * (uint32_t)(c.step + 1);
     uint32_t* ctr = c.kp->counters + sid;
     int tries = 0;
-    while (__hip_atomic_load(gp(ctr), __ATOMIC_RELAXED, MK_SCOPE) < target) {
+    while (!c.fail && __hip_atomic_load(gp(ctr), __ATOMIC_RELAXED, MK_SCOPE) < target) {
       // exponential back-off ("8 - Ecrire son megakernel", section 8.5)
       const int k = tries < 4 ? (1 << tries) : 16;
       for (int i = 0; i < k; ++i) __builtin_amdgcn_s_sleep(1);
@@ -1125,7 +1125,7 @@ __device__ __forceinline__ void op_att(Cx& c, const Ins& in) {
       if (c.tid == 0) {
         const uint32_t* cnt = kp.att_cnt + l * kp.nkv + g;
         const uint32_t target = (uint32_t)S * (uint32_t)(c.step + 1);
-        while (__hip_atomic_load(gp(cnt), __ATOMIC_RELAXED, MK_SCOPE) < target) {
+        while (!c.fail && __hip_atomic_load(gp(cnt), __ATOMIC_RELAXED, MK_SCOPE) < target) {
           if (expired(c, OP_ATT, l, g)) {
             c.fail = true;
             break;

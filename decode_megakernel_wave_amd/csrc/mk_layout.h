@@ -136,4 +136,29 @@ struct KParams {
   const uint32_t* stall_word; // a sync word the host leaves at the sentinel (see stall_cta)
 };
 
+// ---------------------------------------------------------------- prompt prefill
+// Parameters of the prefill kernel (mk_prefill.hip): positions [0, P) of a
+// prompt through every layer with MFMA GEMMs, filling the KV cache.
+struct PParams {
+  int32_t L, d, nq, nkv, hd, f, max_seq, P;
+  float eps;
+  int32_t pad0;
+  const uint16_t* canon;    // per layer [wq; wk; wv] [(nq + 2 nkv) hd][d], wo [d][nq hd], wg, wu [f][d], wd [d][f]
+  const uint16_t* norms;    // [L][2][d]
+  const uint16_t* embed;    // [V][d]
+  const int32_t* ids;       // [P]
+  const float* rope;        // [max_seq][hd/2][2] (cos, sin)
+  uint16_t* kc;             // [L][nkv][max_seq][hd]
+  uint16_t* vc;
+  float* X;                 // [P][d] residual stream
+  float* Q;                 // [P][nq hd] rotated queries
+  float* O;                 // [P][nq hd] attention output
+  float* M;                 // [P][f] silu(gate) * up
+  uint32_t* barrier;        // grid barrier counter (zero at launch)
+  uint32_t* abort_flag;
+  Fault* fault;
+  uint32_t* progress;       // [grid]: stages finished by each workgroup
+  uint64_t watchdog_ticks;  // 100 MHz ticks per wait
+};
+
 }  // namespace mk

@@ -106,6 +106,9 @@ typedef struct mk_stats_t {
   int64_t algo_bytes;        /* algorithmic bytes of the last launch: sum over its steps */
   int32_t n_cu, occupancy;
   mk_fault fault;
+  double prefill_ms;          /* last mk_prefill: GPU time of the MFMA prefill launch (0 if none ran) */
+  int32_t prefill_positions;  /* positions that launch filled (the prompt's last token runs a decode step) */
+  int32_t prefill_grid;       /* its workgroups (0 if none ran) */
 } mk_stats_t;
 
 typedef struct mk_ctx mk_ctx;
@@ -137,11 +140,17 @@ int mk_load_weights(mk_ctx* ctx, const mk_weights* w);
  * single kernel's duties): run the prompt ids[0..n) (host, each in [0,
  * vocab)) at positions 0..n-1, filling the KV cache; *t0_out = the token
  * chosen after the prompt (greedy, or drawn when sampling is on:
- * mk_set_sampling).  The prompt runs through the monokernel one
- * teacher-forced step per token.  Resets the generation state; afterwards
- * the position is n.  Errors: MK_ESTATE (no weights loaded), MK_EINVAL
- * (n < 1 or NULL), MK_ERANGE (n > max_seq or an id outside the vocabulary),
- * MK_ETIMEOUT, MK_ENAN, MK_EHIP.  Synchronises. */
+ * mk_set_sampling).  Positions 0..n-2 run in one persistent launch of the
+ * prefill kernel: every projection as an MFMA GEMM over all positions (fp32
+ * activations split into fp16 hi + lo, fp32 accumulation) and causal
+ * attention tiles; the last token then runs one decode step of the
+ * monokernel, which chooses t0 as every later token is chosen.  Shapes the
+ * prefill kernel does not take (d_model, ffn or n_heads*head_dim not a
+ * multiple of 8), and the environment variable MK_PREFILL_STEPS, run every
+ * prompt token as a teacher-forced decode step instead.  Resets the
+ * generation state; afterwards the position is n.  Errors: MK_ESTATE (no
+ * weights loaded), MK_EINVAL (n < 1 or NULL), MK_ERANGE (n > max_seq or an id
+ * outside the vocabulary), MK_ETIMEOUT, MK_ENAN, MK_EHIP.  Synchronises. */
 int mk_prefill(mk_ctx* ctx, const int32_t* ids, int32_t n, int32_t* t0_out);
 
 /* Decode ("7 - AMD et le monokernel", section 7.1: one persistent kernel,

@@ -43,6 +43,11 @@ int mk_debug_arena(mk_ctx* ctx, int64_t word_off, int64_t n_words, uint32_t* hos
  * the last launch; host receives `grid` words. */
 int mk_debug_progress(mk_ctx* ctx, uint32_t* host, int32_t capacity);
 
+/* Copy the cached K and V rows of positions [pos0, pos0 + n) of one layer and
+ * kv head into host memory (fp16 bit patterns, [n][head_dim] each).
+ * MK_EINVAL for a range outside the cache. */
+int mk_debug_kv(mk_ctx* ctx, int32_t layer, int32_t kv_head, int32_t pos0, int32_t n, uint16_t* k_out, uint16_t* v_out);
+
 /* Failure-path test: in the next launch only, workgroup `cta` waits in step 0,
  * before its argmax, for a sync word the host never writes, so that wait's
  * watchdog fires ("8 - Ecrire son megakernel", section 8.7: a watchdog that
