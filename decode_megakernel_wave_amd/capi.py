@@ -92,6 +92,7 @@ SIGNATURES = [
     ("mk_debug_arena", C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.POINTER(C.c_uint32)]),
     ("mk_debug_progress", C.c_int, [C.c_void_p, C.POINTER(C.c_uint32), C.c_int32]),
     ("mk_debug_force_stall", C.c_int, [C.c_void_p, C.c_int32]),
+    ("mk_debug_prefill_marks", C.c_int, [C.c_void_p, C.POINTER(C.c_uint64), C.c_int32]),
     ("mk_debug_kv", C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_uint16),
                               C.POINTER(C.c_uint16)]),
     ("mk_debug_ts", C.c_int, [C.c_void_p, C.POINTER(C.c_uint64), C.c_int64]),
@@ -342,6 +343,13 @@ def mk_debug_kv(ctx, layer: int, kv_head: int, pos0: int, n: int, head_dim: int)
     _check(lib().mk_debug_kv(ctx, layer, kv_head, pos0, n, k.ctypes.data_as(C.POINTER(C.c_uint16)),
                              v.ctypes.data_as(C.POINTER(C.c_uint16))), ctx)
     return k.view(np.float16), v.view(np.float16)
+
+
+def mk_debug_prefill_marks(ctx, n_layers: int) -> np.ndarray:
+    """Device-clock ticks (100 MHz) when the last prefill launch left each grid barrier: 1 + 5 n_layers."""
+    buf = np.zeros(1 + 5 * n_layers, dtype=np.uint64)
+    _check(lib().mk_debug_prefill_marks(ctx, buf.ctypes.data_as(C.POINTER(C.c_uint64)), buf.size), ctx)
+    return buf
 
 
 def mk_debug_force_stall(ctx, cta: int) -> None:

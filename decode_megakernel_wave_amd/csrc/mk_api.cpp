@@ -359,6 +359,7 @@ struct mk_ctx {
   float *d_pX = nullptr, *d_pQ = nullptr, *d_pO = nullptr, *d_pM = nullptr;
   int32_t* d_pids = nullptr;
   uint32_t* d_pbar = nullptr;
+  uint64_t* d_pmarks = nullptr;     // [1 + 5 L + 1]: start, then each grid barrier (device clock)
   PParams* d_pp = nullptr;
   PParams h_pp{};
 };
@@ -449,6 +450,7 @@ int ctx_alloc_prefill(mk_ctx* c) {
   CHK(g.alloc(&c->d_pM, (size_t)P * k.ffn * 4));
   CHK(g.alloc(&c->d_pids, (size_t)P * 4));
   CHK(g.alloc(&c->d_pbar, 256));
+  CHK(g.alloc(&c->d_pmarks, (size_t)(5 * k.n_layers + 2) * 8));
   CHK(g.alloc(&c->d_pp, sizeof(PParams)));
   return MK_OK;
 }
@@ -491,6 +493,8 @@ int ctx_prefill_mfma(mk_ctx* c, const int32_t* ids, int n) {
   pp.fault = g.d_fault;
   pp.progress = g.d_progress;
   pp.watchdog_ticks = (uint64_t)g.opt.watchdog_us * 100ull;
+  pp.marks = c->d_pmarks;
+  HIPCHK(g, mk_launch_fill32((uint32_t*)c->d_pmarks, 2 * (5 * k.n_layers + 2), 0u, g.stream));
   HIPCHK(g, hipMemcpyAsync(c->d_pp, &pp, sizeof(PParams), hipMemcpyHostToDevice, g.stream));
   HIPCHK(g, hipEventRecord(g.ev0, g.stream));
   HIPCHK(g, mk_launch_prefill(c->d_pp, c->pf_grid, c->pf_lds, g.stream));
@@ -975,6 +979,15 @@ int mk_debug_kv(mk_ctx* c, int32_t layer, int32_t kv_head, int32_t pos0, int32_t
   const size_t bytes = (size_t)n * k.head_dim * 2;
   HIPCHK(c->g, hipMemcpy(k_out, c->d_kc + off, bytes, hipMemcpyDeviceToHost));
   HIPCHK(c->g, hipMemcpy(v_out, c->d_vc + off, bytes, hipMemcpyDeviceToHost));
+  return MK_OK;
+}
+
+int mk_debug_prefill_marks(mk_ctx* c, uint64_t* host, int32_t capacity) {
+  if (!c || !host) return MK_EINVAL;
+  const int n = 5 * c->cfg.n_layers + 1;
+  if (capacity < n) return c->g.fail(MK_EINVAL, "capacity below 1 + 5 n_layers");
+  if (!c->d_pmarks) return c->g.fail(MK_ESTATE, "this context has no prefill kernel");
+  HIPCHK(c->g, hipMemcpy(host, c->d_pmarks, (size_t)n * 8, hipMemcpyDeviceToHost));
   return MK_OK;
 }
 

@@ -159,6 +159,7 @@ struct PParams {
   Fault* fault;
   uint32_t* progress;       // [grid]: stages finished by each workgroup
   uint64_t watchdog_ticks;  // 100 MHz ticks per wait
+  uint64_t* marks;          // [1 + 5 L]: device clock when workgroup 0 left each grid barrier, or null
 };
 
 }  // namespace mk

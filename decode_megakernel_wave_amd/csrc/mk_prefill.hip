@@ -108,6 +108,7 @@ __device__ __forceinline__ bool grid_barrier(PCx& c, int op, int layer) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     *flag = failed;
     stc32(p.progress + c.cta, c.epoch + 1);
+    if (p.marks && c.cta == 0) *gp(p.marks + c.epoch) = __builtin_amdgcn_s_memrealtime();
   }
   __syncthreads();
   const uint32_t failed = __builtin_amdgcn_readfirstlane(*flag);

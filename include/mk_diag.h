@@ -48,6 +48,13 @@ int mk_debug_progress(mk_ctx* ctx, uint32_t* host, int32_t capacity);
  * MK_EINVAL for a range outside the cache. */
 int mk_debug_kv(mk_ctx* ctx, int32_t layer, int32_t kv_head, int32_t pos0, int32_t n, uint16_t* k_out, uint16_t* v_out);
 
+/* Device-clock (100 MHz) times at which workgroup 0 left each grid barrier of
+ * the last MFMA prefill launch: [0] the embedding stage, then per layer the
+ * QKV, attention, O-projection, up/gate and down stages (1 + 5 n_layers
+ * values; differences are stage durations).  MK_ESTATE when the context has
+ * no prefill kernel. */
+int mk_debug_prefill_marks(mk_ctx* ctx, uint64_t* host, int32_t capacity);
+
 /* Failure-path test: in the next launch only, workgroup `cta` waits in step 0,
  * before its argmax, for a sync word the host never writes, so that wait's
  * watchdog fires ("8 - Ecrire son megakernel", section 8.7: a watchdog that
