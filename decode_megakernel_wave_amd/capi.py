@@ -86,6 +86,7 @@ SIGNATURES = [
     ("mk_position", C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
     ("mk_stats", C.c_int, [C.c_void_p, C.POINTER(mk_stats_t)]),
     ("mk_count_sentinels", C.c_int, [C.c_void_p, C.POINTER(C.c_int64)]),
+    ("mk_count_sentinels_noalloc", C.c_int, [C.c_void_p, C.POINTER(C.c_int64)]),
     ("mk_read_trace", C.c_int, [C.c_void_p, C.POINTER(C.c_uint32), C.c_int64, C.POINTER(C.c_int64)]),
     ("mk_debug_streams", C.c_int, [C.c_void_p, C.POINTER(C.c_void_p), C.POINTER(C.c_void_p), C.POINTER(C.c_void_p)]),
     ("mk_debug_layout", C.c_int, [C.c_void_p, C.POINTER(C.c_int64)]),
@@ -292,6 +293,13 @@ def mk_stats(ctx) -> dict:
 def mk_count_sentinels(ctx) -> int:
     n = C.c_int64()
     _check(lib().mk_count_sentinels(ctx, C.byref(n)), ctx)
+    return int(n.value)
+
+
+def mk_count_sentinels_noalloc(ctx) -> int:
+    """mk_count_sentinels without any allocation (a static per-GPU counter); see include/mk_diag.h."""
+    n = C.c_int64()
+    _check(lib().mk_count_sentinels_noalloc(ctx, C.byref(n)), ctx)
     return int(n.value)
 
 

@@ -39,6 +39,9 @@ hipError_t mk_launch_probe_read(const void* p, int64_t n16, void* sink, int grid
 hipError_t mk_launch_probe_barrier(uint32_t* counter, int rounds, uint64_t deadline_ticks, uint64_t* out, int grid,
                                    hipStream_t s);
 hipError_t mk_probe_barrier_occupancy(int* occupancy);
+hipError_t mk_launch_count64(const uint64_t* p, int64_t n, int stride, int width, uint64_t v, unsigned long long* out,
+                             hipStream_t s);
+hipError_t mk_scratch_address(int device, void** out, size_t* bytes);
 int mk_prefill_lds_bytes(int hd);
 hipError_t mk_prefill_attributes(int lds_bytes, int* occupancy);
 hipError_t mk_launch_prefill(const PParams* pp_dev, int grid, int lds_bytes, hipStream_t s);
@@ -934,6 +937,37 @@ int mk_count_sentinels(mk_ctx* c, int64_t* count) {
     if (e != hipSuccess) return g.hip_fail(e, "sentinel count");
     for (int64_t i = 0; i < c->lmk_es; ++i) h += (i % kMaxTopK) < c->last_top_k && lists[i] == kSent64;
   }
+  *count = (int64_t)h;
+  return MK_OK;
+}
+
+int mk_count_sentinels_noalloc(mk_ctx* c, int64_t* count) {
+  if (!c || !count) return MK_EINVAL;
+  Engine& g = c->g;
+  if (c->last_n < 1) return g.fail(MK_ESTATE, "no launch yet");
+  HIPCHK(g, hipSetDevice(g.device));
+  void* sp = nullptr;
+  size_t sbytes = 0;
+  HIPCHK(g, mk_scratch_address(g.device, &sp, &sbytes));
+  if (sbytes < sizeof(unsigned long long)) return g.fail(MK_EINVAL, "the static scratch is smaller than one counter");
+  unsigned long long* d = (unsigned long long*)sp;
+  // cleared by a fill kernel (no memset node), then the same counts as mk_count_sentinels,
+  // the argmax keys and top-k lists counted on the device as well
+  hipError_t e = mk_launch_fill32((uint32_t*)d, 2, 0u, g.stream);
+  const int el = (c->last_n - 1) % 3;
+  for (const auto& r : c->epoch_regions[el])
+    if (e == hipSuccess) e = mk_launch_count32((const uint32_t*)g.d_arena + r.off, r.words, kSent32, d, g.stream);
+  const mk_config& k = c->cfg;
+  if (e == hipSuccess)
+    e = mk_launch_count_kv(c->d_kc, c->d_vc, (int64_t)k.n_layers * k.n_kv_heads, k.max_seq, k.head_dim, c->last_pos0,
+                           c->last_pos0 + c->last_n, d, g.stream);
+  if (e == hipSuccess) e = mk_launch_count64(c->lmp + el * c->lmp_es, c->lmp_es, 1, 1, kSent64, d, g.stream);
+  if (e == hipSuccess && c->last_top_k > 1)
+    e = mk_launch_count64(c->lmk + el * c->lmk_es, c->lmk_es, kMaxTopK, c->last_top_k, kSent64, d, g.stream);
+  unsigned long long h = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&h, d, sizeof h, hipMemcpyDeviceToHost, g.stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(g.stream);
+  if (e != hipSuccess) return g.hip_fail(e, "sentinel count");
   *count = (int64_t)h;
   return MK_OK;
 }

@@ -35,6 +35,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "mk_device.h"
 #include "mk_layout.h"
 
@@ -1795,6 +1797,24 @@ __global__ void mk_count_kv(const uint16_t* kc, const uint16_t* vc, int64_t rows
   atomicAdd(out, cnt);
 }
 
+// Count 64-bit words equal to v among the first `width` words of every group
+// of `stride` (width == stride: every word).
+__global__ void mk_count64(const uint64_t* p, int64_t n, int stride, int width, uint64_t v, unsigned long long* out) {
+  unsigned long long cnt = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    cnt += (i % stride) < width && p[i] == v;
+  atomicAdd(out, cnt);
+}
+
+// ---------------------------------------------------------------- allocation-free scratch
+// Device memory of the allocation-free entry point mk_count_sentinels_noalloc:
+// its sentinel counter lives here instead of in a per-call allocation.  Each
+// GPU holds its own copy until the process ends.  In host code this name is
+// not a device address: host code reaches the array only through the address
+// hipGetSymbolAddress gives on that device (mk_scratch_address below).
+constexpr int kScratchWords = 32;  // 256 bytes; the counter takes the first 8
+static __device__ __align__(256) unsigned long long scratch[kScratchWords];
+
 // ---------------------------------------------------------------- calibration probes
 // An empty kernel: launch overhead.
 __global__ void mk_probe_empty() {}
@@ -1914,6 +1934,34 @@ MK_INTERNAL hipError_t mk_launch_count32(const uint32_t* p, int64_t n, uint32_t 
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(mk_count32, dim3(1024), dim3(256), 0, s, p, n, v, out);
   return hipGetLastError();
+}
+MK_INTERNAL hipError_t mk_launch_count64(const uint64_t* p, int64_t n, int stride, int width, uint64_t v,
+                                         unsigned long long* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mk_count64, dim3(256), dim3(256), 0, s, p, n, stride, width, v, out);
+  return hipGetLastError();
+}
+// Device address and size of `scratch` on `device`: looked up once per device
+// (with that device current) and kept for later calls.
+MK_INTERNAL hipError_t mk_scratch_address(int device, void** out, size_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != device) e = hipSetDevice(device);
+    void* p = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != device) hipSetDevice(cur);
+    if (e != hipSuccess) return e;
+    addr[device] = p;
+  }
+  *out = addr[device];
+  *bytes = sizeof(scratch);
+  return hipSuccess;
 }
 MK_INTERNAL hipError_t mk_launch_count_kv(const uint16_t* kc, const uint16_t* vc, int64_t rows, int max_seq, int hd, int p0, int p1,
                               unsigned long long* out, hipStream_t s) {

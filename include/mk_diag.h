@@ -24,6 +24,18 @@ extern "C" {
  * of the last launch and in the KV cache positions it wrote.  0 after a good run. */
 int mk_count_sentinels(mk_ctx* ctx, int64_t* count);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the count of
+ * mk_count_sentinels with no allocation.  Its counter lives in a static
+ * device array of 256 bytes per GPU (held until the process ends) instead of
+ * the 8 bytes mk_count_sentinels allocates per call; the array is found once
+ * per device and reused, and cleared by a fill kernel at every call.  The
+ * scratch does not grow with the model (one counter whatever the arena size),
+ * so no size is refused.  Every call on a GPU shares that GPU's array: calls
+ * that overlap on one GPU (other threads, other streams) race on the
+ * counter.  Synchronises the context's stream; errors as mk_count_sentinels. */
+int mk_count_sentinels_noalloc(mk_ctx* ctx, int64_t* count);
+
 /* Copy the time journal of the last launch into host memory.  Each record is
  * 8 uint32: {cta, step, pc, op | layer << 8, t_wait_lo, t_ready - t_wait,
  * t_done - t_wait, xcc}, in ticks of the 100 MHz device wall clock; unused
