@@ -418,6 +418,139 @@ __device__ void att_stage(PCx& c, int l) {
   }
 }
 
+// ---------------------------------------------------------------- causal attention on MFMA
+// Work item of one wavefront: query head h and 32 consecutive positions.  It
+// walks the keys 0 .. (last query) in blocks of 32 with an online softmax in
+// the exp2 domain (q pre-scaled by log2(e)/sqrt(hd)):
+//   S^T = K Q^T    A = the K block (rows = keys, K-dim = head dims), loaded
+//                  straight from the cache; B = Q^T as fp16 hi + lo halves
+//   O^T += V^T P^T A = the V block transposed through this wavefront's LDS
+//                  slice; B = the probabilities P^T as fp16 hi + lo halves
+// With the products transposed this way, lane l owns query l % 32 in every
+// accumulator (S^T columns, O^T columns), so the softmax statistics and the
+// rescaling of O stay in the lane; the other 16 keys of a block sit in lane
+// l ^ 32.  The probabilities enter the second product in the order the S^T
+// accumulator holds them, and the V^T operand reads its keys in that order.
+constexpr int kVtStride = 40;  // halves per V^T row in LDS (32 keys + padding)
+
+template <int HD>
+__device__ __attribute__((noinline)) void att_stage_mfma(PCx& c, int l) {
+  constexpr int KS = HD / 16;  // MFMA K-steps over the head dims
+  constexpr int DB = HD / 32;  // 32-dim blocks of O^T
+  const PParams& p = *c.pp;
+  const int P = p.P, nqb = (P + 31) / 32, items = p.nq * nqb;
+  const int i32 = c.lane & 31, hh = c.lane >> 5;
+  const float qscale = kLog2e / __builtin_sqrtf((float)HD);
+  _Float16* vt = (_Float16*)pf_smem + c.wave * HD * kVtStride;  // this wavefront's V^T block [HD][kVtStride]
+  const int nw = c.grid * kPW, gw = c.cta * kPW + c.wave;
+  for (int it = gw; it < items; it += nw) {
+    // the longest items (latest query blocks) first
+    const int qb = nqb - 1 - it / p.nq, h = it - (it / p.nq) * p.nq;
+    const int g = h * p.nkv / p.nq;
+    const int q0 = qb * 32, pq = q0 + i32;           // this lane's query
+    const int lim = min(pq, P - 1);                  // last key it attends
+    const int kmax = min(q0 + 31, P - 1);            // last key of any query of the block
+    // Q^T operands: dims 16 s + 8 hh + e of query pq, as hi and lo halves
+    h8 qh[KS], ql[KS];
+    {
+      const float* qrow = p.Q + (int64_t)min(pq, P - 1) * p.nq * HD + h * HD + 8 * hh;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const f4 a = *gp((const f4*)(qrow + 16 * s)), b = *gp((const f4*)(qrow + 16 * s + 4));
+        const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = v[e] * qscale;
+          qh[s][e] = (_Float16)x;
+          ql[s][e] = (_Float16)(x - (float)qh[s][e]);
+        }
+      }
+    }
+    f32x16 o[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) o[b] = f32x16{};
+    float m = -INFINITY, ls = 0.f;
+    const int64_t hbase = ((int64_t)l * p.nkv + g) * p.max_seq * HD;
+    const uint16_t* kbase = p.kc + hbase;
+    const uint16_t* vbase = p.vc + hbase;
+    for (int kb0 = 0; kb0 <= kmax; kb0 += 32) {
+      // S^T block: lane l holds query pq and keys kb0 + 8 (v / 4) + 4 hh + v % 4
+      const int key = kb0 + i32;                      // this lane's K / V row for the operands
+      const bool kin = key <= kmax;
+      f32x16 st = {};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const u4 kr = kin ? *gp((const u4*)(kbase + (int64_t)key * HD + 16 * s + 8 * hh)) : u4{0u, 0u, 0u, 0u};
+        const h8 ka = __builtin_bit_cast(h8, kr);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qh[s], st, 0, 0, 0);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, ql[s], st, 0, 0, 0);
+      }
+      // V block -> V^T in LDS: lane (key i32, half hh) writes dims [HD/2 hh, HD/2 (hh + 1)) of its key
+#pragma unroll
+      for (int v8 = 0; v8 < HD / 16; ++v8) {
+        const int d0 = hh * (HD / 2) + v8 * 8;
+        const u4 vr = kin ? *gp((const u4*)(vbase + (int64_t)key * HD + d0)) : u4{0u, 0u, 0u, 0u};
+        const h8 vh = __builtin_bit_cast(h8, vr);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vt[(d0 + e) * kVtStride + i32] = vh[e];
+      }
+      // mask, block maximum (this lane's 16 keys, then the other 16 in lane l ^ 32)
+      float mb = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int kk = kb0 + (v >> 2) * 8 + hh * 4 + (v & 3);
+        st[v] = kk <= lim ? st[v] : -INFINITY;
+        mb = fmaxf(mb, st[v]);
+      }
+      mb = fmaxf(mb, __shfl_xor(mb, 32));
+      const float mn = fmaxf(m, mb);
+      const float al = mn == -INFINITY ? 1.f : exp2f(m - mn);
+      ls *= al;
+#pragma unroll
+      for (int b = 0; b < DB; ++b) o[b] *= al;
+      m = mn;
+      // probabilities, as the B operand of O^T += V^T P^T in two K-steps of 16 keys
+      h8 ph[2], pl[2];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float w = st[v] == -INFINITY ? 0.f : exp2f(st[v] - mn);
+        ls += w;
+        const _Float16 hi = (_Float16)w;
+        ph[v >> 3][v & 7] = hi;
+        pl[v >> 3][v & 7] = (_Float16)(w - (float)hi);
+      }
+      // V^T operand of step t: dim 32 b + i32, keys 16 t + 4 hh + {0..3} and 16 t + 8 + 4 hh + {0..3}
+#pragma unroll
+      for (int b = 0; b < DB; ++b) {
+        const _Float16* row = vt + (b * 32 + i32) * kVtStride;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+          const h4 x0 = *(const h4*)(row + 16 * t + 4 * hh);
+          const h4 x1 = *(const h4*)(row + 16 * t + 8 + 4 * hh);
+          const h8 va = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, ph[t], o[b], 0, 0, 0);
+          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pl[t], o[b], 0, 0, 0);
+        }
+      }
+    }
+    // the query's sum over all keys: this lane's keys plus those of lane l ^ 32
+    const float lt = ls + __shfl_xor(ls, 32);
+    if (pq < P) {
+      float* orow = p.O + (int64_t)pq * p.nq * HD + h * HD;
+      const float inv = 1.0f / lt;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          // dims 32 b + 8 a + 4 hh + {0..3}: registers 4 a .. 4 a + 3
+          const f4 v = {o[b][4 * a] * inv, o[b][4 * a + 1] * inv, o[b][4 * a + 2] * inv, o[b][4 * a + 3] * inv};
+          *gp((f4*)(orow + 32 * b + 8 * a + 4 * hh)) = v;
+        }
+    }
+  }
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(kPT, 1) void mk_prefill_kernel(const PParams* __restrict__ ppp) {
@@ -451,8 +584,8 @@ __global__ __launch_bounds__(kPT, 1) void mk_prefill_kernel(const PParams* __res
     const uint16_t* g2 = g1 + p.d;
     gemm_stage(c, Gemm{EPI_QKV, l, p.X, p.d, p.d, g1, wl, (p.nq + 2 * p.nkv) * (p.hd / 2), nullptr, 0, nullptr});
     if (grid_barrier(c, OP_QKV, l)) return;
-    if (p.hd == 64) att_stage<64>(c, l);
-    else if (p.hd == 128) att_stage<128>(c, l);
+    if (p.hd == 64) att_stage_mfma<64>(c, l);
+    else if (p.hd == 128) att_stage_mfma<128>(c, l);
     else att_stage<256>(c, l);
     if (grid_barrier(c, OP_ATT, l)) return;
     gemm_stage(c, Gemm{EPI_RESID, l, p.O, qd, qd, nullptr, wo, p.d, p.X, p.d, nullptr});
@@ -470,7 +603,8 @@ extern "C" {
 // LDS bytes of the prefill kernel for head_dim hd: the GEMM staging or the
 // attention merge, whichever is larger.
 MK_INTERNAL int mk_prefill_lds_bytes(int hd) {
-  const int att = 2 * 16 * (hd + 2) * 4;
+  // head_dim 256: the merge of the vector-unit attention; 64 and 128: one V^T block per wavefront
+  const int att = hd >= 256 ? 2 * 16 * (hd + 2) * 4 : kPW * hd * kVtStride * 2;
   return kGemmLdsBytes > att ? kGemmLdsBytes : att;
 }
 MK_INTERNAL hipError_t mk_prefill_attributes(int lds_bytes, int* occupancy) {
