@@ -37,7 +37,7 @@ class mk_config(C.Structure):
 
 class mk_options(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("sync_mode", "xcd_replicas", "attn_splits", "trace_steps",
-                                          "watchdog_us", "grid")]
+                                          "watchdog_us", "grid", "work_queue")]
 
 
 _PP = C.POINTER(C.c_void_p)

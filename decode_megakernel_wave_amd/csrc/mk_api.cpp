@@ -144,6 +144,7 @@ int sanitize_options(const mk_options* in, mk_options* out) {
   if (!(out->xcd_replicas == 1 || out->xcd_replicas == 2 || out->xcd_replicas == 4 || out->xcd_replicas == 8)) return MK_EINVAL;
   if (out->attn_splits < 0 || out->attn_splits > 64) return MK_EINVAL;
   if (out->trace_steps < 0 || out->watchdog_us <= 0 || out->grid < 0) return MK_EINVAL;
+  if (out->work_queue != 0 && out->work_queue != 1) return MK_EINVAL;
   return MK_OK;
 }
 
@@ -363,6 +364,7 @@ struct mk_ctx {
   int32_t* d_pids = nullptr;
   uint32_t* d_pbar = nullptr;
   uint64_t* d_pmarks = nullptr;     // [1 + 5 L + 1]: start, then each grid barrier (device clock)
+  uint32_t* d_pqueue = nullptr;     // [1 + 5 L] work-queue counters
   PParams* d_pp = nullptr;
   PParams h_pp{};
 };
@@ -454,6 +456,7 @@ int ctx_alloc_prefill(mk_ctx* c) {
   CHK(g.alloc(&c->d_pids, (size_t)P * 4));
   CHK(g.alloc(&c->d_pbar, 256));
   CHK(g.alloc(&c->d_pmarks, (size_t)(5 * k.n_layers + 2) * 8));
+  CHK(g.alloc(&c->d_pqueue, (size_t)(5 * k.n_layers + 2) * 4));
   CHK(g.alloc(&c->d_pp, sizeof(PParams)));
   return MK_OK;
 }
@@ -497,6 +500,9 @@ int ctx_prefill_mfma(mk_ctx* c, const int32_t* ids, int n) {
   pp.progress = g.d_progress;
   pp.watchdog_ticks = (uint64_t)g.opt.watchdog_us * 100ull;
   pp.marks = c->d_pmarks;
+  pp.queue = c->d_pqueue;
+  pp.dynamic = g.opt.work_queue;
+  HIPCHK(g, mk_launch_fill32(c->d_pqueue, 5 * k.n_layers + 2, 0u, g.stream));
   HIPCHK(g, mk_launch_fill32((uint32_t*)c->d_pmarks, 2 * (5 * k.n_layers + 2), 0u, g.stream));
   HIPCHK(g, hipMemcpyAsync(c->d_pp, &pp, sizeof(PParams), hipMemcpyHostToDevice, g.stream));
   HIPCHK(g, hipEventRecord(g.ev0, g.stream));
@@ -626,6 +632,7 @@ int mk_default_options(mk_options* o) {
   o->trace_steps = 0;
   o->watchdog_us = 2000000;
   o->grid = 0;
+  o->work_queue = 0;
   return MK_OK;
 }
 

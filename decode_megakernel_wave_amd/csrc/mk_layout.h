@@ -160,6 +160,9 @@ struct PParams {
   uint32_t* progress;       // [grid]: stages finished by each workgroup
   uint64_t watchdog_ticks;  // 100 MHz ticks per wait
   uint64_t* marks;          // [1 + 5 L]: device clock when workgroup 0 left each grid barrier, or null
+  uint32_t* queue;          // [1 + 5 L] work-queue counters, one per stage (zero at launch)
+  int32_t dynamic;          // 1: workgroups / wavefronts claim their tiles from the queue; 0: static deal
+  int32_t pad1;
 };
 
 }  // namespace mk

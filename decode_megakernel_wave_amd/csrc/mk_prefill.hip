@@ -44,6 +44,10 @@ constexpr int kLS = kTK + 8;           // LDS row stride in halves (padding spre
 constexpr int kOpHalves = kTM * kLS;   // one staged operand tile
 // LDS: A hi, A lo, B, each double-buffered, then the row scales
 constexpr int kGemmLdsBytes = 6 * kOpHalves * 2 + kTM * 4;
+// The work-queue slot a workgroup reads its claimed tile from, past every
+// stage's own LDS use (the largest: 8 wavefronts' V^T blocks at head_dim 128).
+constexpr int kClaimOff = 8 * 128 * 40 * 2;
+static_assert(kClaimOff >= kGemmLdsBytes, "claim slot overlaps the GEMM staging");
 
 enum Epi { EPI_QKV = 0, EPI_UG = 1, EPI_RESID = 2 };
 
@@ -287,12 +291,40 @@ __device__ __forceinline__ void gemm_tile(PCx& c, const Gemm& g, int tm, int tn)
   __syncthreads();  // the staging buffers and scales are reused by the next tile
 }
 
+// Work distribution of a stage whose items a whole workgroup processes.
+// Static: workgroup c takes items c, c + grid, ...  Dynamic (a work queue,
+// "8 - Ecrire son megakernel", section 8.8): the workgroup claims its next
+// item from the stage's counter while it works on the current one, so a
+// workgroup that finishes early takes more items.
+template <typename F>
+__device__ __forceinline__ void wg_items(PCx& c, int items, F&& work) {
+  const PParams& p = *c.pp;
+  if (!p.dynamic) {
+    for (int t = c.cta; t < items; t += c.grid) work(t);
+    return;
+  }
+  int* slot = (int*)(pf_smem + kClaimOff);
+  uint32_t* ctr = p.queue + c.epoch;
+  if (c.tid == 0) *slot = (int)__hip_atomic_fetch_add(gp(ctr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __syncthreads();
+  int t = *slot;
+  __syncthreads();
+  while (t < items) {
+    uint32_t nxt = 0;
+    if (c.tid == 0) nxt = __hip_atomic_fetch_add(gp(ctr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    work(t);
+    if (c.tid == 0) *slot = (int)nxt;
+    __syncthreads();
+    t = *slot;
+    __syncthreads();
+  }
+}
+
 __device__ __forceinline__ void gemm_stage(PCx& c, const Gemm& g) {
   const int n_tm = (c.pp->P + kTM - 1) / kTM;
   const int n_tn = g.ep == EPI_RESID ? (g.n_out + kTN - 1) / kTN : (g.n_out + 63) / 64;
-  const int tiles = n_tm * n_tn;
-  // consecutive workgroups take the row tiles of one weight tile: they share its weight rows in L2
-  for (int t = c.cta; t < tiles; t += c.grid) gemm_tile(c, g, t % n_tm, t / n_tm);
+  // consecutive items are the row tiles of one weight tile: workgroups working at the same time share its weight rows in L2
+  wg_items(c, n_tm * n_tn, [&](int t) { gemm_tile(c, g, t % n_tm, t / n_tm); });
 }
 
 // ---------------------------------------------------------------- causal attention
@@ -313,7 +345,7 @@ __device__ void att_stage(PCx& c, int l) {
   const int sb = c.wave & 3, kh = c.wave >> 2;
   const float qscale = kLog2e / __builtin_sqrtf((float)HD);
   float* part = (float*)pf_smem;  // [2][16][HD + 2]
-  for (int it = c.cta; it < items; it += c.grid) {
+  wg_items(c, items, [&](int it) {
     const int qb = nqb - 1 - it / p.nq, h = it - (it / p.nq) * p.nq;
     const int g = h * p.nkv / p.nq;
     const int p0 = qb * 16, qi = sb * 4 + row, pq = p0 + qi;
@@ -415,7 +447,7 @@ __device__ void att_stage(PCx& c, int l) {
       *gp(p.O + (int64_t)pos * p.nq * HD + h * HD + dd) = (a0 * r0[2 + dd] + a1 * r1[2 + dd]) / (a0 * r0[1] + a1 * r1[1]);
     }
     __syncthreads();
-  }
+  });
 }
 
 // ---------------------------------------------------------------- causal attention on MFMA
@@ -432,6 +464,7 @@ __device__ void att_stage(PCx& c, int l) {
 // l ^ 32.  The probabilities enter the second product in the order the S^T
 // accumulator holds them, and the V^T operand reads its keys in that order.
 constexpr int kVtStride = 40;  // halves per V^T row in LDS (32 keys + padding)
+static_assert(kPW * 128 * kVtStride * 2 <= kClaimOff && 2 * 16 * (256 + 2) * 4 <= kClaimOff, "claim slot overlaps attention LDS");
 
 template <int HD>
 __device__ __attribute__((noinline)) void att_stage_mfma(PCx& c, int l) {
@@ -443,7 +476,17 @@ __device__ __attribute__((noinline)) void att_stage_mfma(PCx& c, int l) {
   const float qscale = kLog2e / __builtin_sqrtf((float)HD);
   _Float16* vt = (_Float16*)pf_smem + c.wave * HD * kVtStride;  // this wavefront's V^T block [HD][kVtStride]
   const int nw = c.grid * kPW, gw = c.cta * kPW + c.wave;
-  for (int it = gw; it < items; it += nw) {
+  // static: wavefront gw takes items gw, gw + nw, ...; dynamic: each wavefront claims its next
+  // item from the stage's counter while it works on the current one
+  uint32_t* ctr = p.queue + c.epoch;
+  auto claim = [&]() -> int {
+    uint32_t v = 0;
+    if (c.lane == 0) v = __hip_atomic_fetch_add(gp(ctr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    return v;
+  };
+  int it = p.dynamic ? __builtin_amdgcn_readfirstlane(claim()) : gw;
+  while (it < items) {
+    const int nxt_raw = p.dynamic ? claim() : it + nw;
     // the longest items (latest query blocks) first
     const int qb = nqb - 1 - it / p.nq, h = it - (it / p.nq) * p.nq;
     const int g = h * p.nkv / p.nq;
@@ -548,6 +591,7 @@ __device__ __attribute__((noinline)) void att_stage_mfma(PCx& c, int l) {
           *gp((f4*)(orow + 32 * b + 8 * a + 4 * hh)) = v;
         }
     }
+    it = p.dynamic ? __builtin_amdgcn_readfirstlane(nxt_raw) : nxt_raw;
   }
 }
 
@@ -603,9 +647,10 @@ extern "C" {
 // LDS bytes of the prefill kernel for head_dim hd: the GEMM staging or the
 // attention merge, whichever is larger.
 MK_INTERNAL int mk_prefill_lds_bytes(int hd) {
-  // head_dim 256: the merge of the vector-unit attention; 64 and 128: one V^T block per wavefront
-  const int att = hd >= 256 ? 2 * 16 * (hd + 2) * 4 : kPW * hd * kVtStride * 2;
-  return kGemmLdsBytes > att ? kGemmLdsBytes : att;
+  // every stage's use (GEMM staging; head_dim 256: the merge of the vector-unit attention;
+  // 64 and 128: one V^T block per wavefront) lies below the work-queue slot
+  (void)hd;
+  return kClaimOff + 16;
 }
 MK_INTERNAL hipError_t mk_prefill_attributes(int lds_bytes, int* occupancy) {
   hipError_t e = hipFuncSetAttribute((const void*)mk_prefill_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);

@@ -69,6 +69,9 @@ typedef struct mk_options {
   int32_t trace_steps;   /* record a per-instruction time journal for the first N steps (0 = off) */
   int32_t watchdog_us;   /* per-wait timeout inside the kernel, microseconds (default 2000000) */
   int32_t grid;          /* workgroups to launch (0 = CUs x occupancy; larger values are refused) */
+  int32_t work_queue;    /* prefill work distribution: 0 = static deal of tiles to workgroups (default),
+                            1 = dynamic work queue (each workgroup / wavefront claims its next tile from a
+                            per-stage counter; "8 - Ecrire son megakernel", section 8.8) */
 } mk_options;
 
 /* Device pointers to canonical fp16 weights; per-layer entries are host

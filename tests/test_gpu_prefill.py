@@ -14,7 +14,9 @@ attention tiles) and the last prompt token as one decode step.  Checked here:
   prefill kernel's position count reported by mk_stats;
 - prompts that leave ragged GEMM and attention tiles (1, 2, 33, 129, 200
   positions), and the token-by-token prefill (MK_PREFILL_STEPS) giving the
-  same first token and the same decode within the acceptance rule.
+  same first token and the same decode within the acceptance rule;
+- the dynamic work queue (option work_queue) giving bitwise the results of
+  the static deal.
 """
 import numpy as np
 import pytest
@@ -54,13 +56,13 @@ def _kv_check(ctx, dec, model, P):
     return mism, total
 
 
-def _run(model, P, n, seed=1, w=None, env_steps=False, monkeypatch=None):
+def _run(model, P, n, seed=1, w=None, env_steps=False, monkeypatch=None, **opts):
     w = w if w is not None else inputs.make_weights(model, seed=0)
     ids = inputs.make_prompt(model, P, seed=seed)
     t0_ref, toks_ref, logs_ref, dec, m0 = oracle_run(model, w, ids, n)
     if env_steps:
         monkeypatch.setenv("MK_PREFILL_STEPS", "1")
-    ctx = mk.mk_create(model, max_seq=P + n + 1)
+    ctx = mk.mk_create(model, max_seq=P + n + 1, opts=mk.mk_default_options(**opts) if opts else None)
     try:
         wd = mk.to_device(w)
         mk.mk_load_weights(ctx, wd)
@@ -101,6 +103,20 @@ def test_2b_geometry_prefill_prompt512():
     assert st["prefill_positions"] == 511
     print(f"2B geometry P=512: prefill {st['prefill_ms']:.2f} ms, max |dlogit| {err:.2e}, "
           f"ulp-off values {mism}/{total}")
+
+
+@pytest.mark.parametrize("model,P", [(inputs.TINY, 200), (inputs.M2B_GEOM_L2, 512)])
+def test_prefill_work_queue(model, P):
+    """Tiles and attention items claimed from a per-stage work queue instead of the static deal:
+    the same parity, and the same KV cache bit for bit (each tile is computed the same way
+    whichever workgroup claims it)."""
+    w = inputs.make_weights(model, seed=0)
+    st, err, _, t0, log_q, _ = _run(model, P, 2, w=w, work_queue=1)
+    assert st["prefill_positions"] == P - 1
+    _, _, _, t0_s, log_s, _ = _run(model, P, 2, w=w)
+    assert t0 == t0_s
+    assert np.array_equal(log_q.view(np.uint32), log_s.view(np.uint32))
+    print(f"{model.name} P={P} work queue: max |dlogit| {err:.2e}")
 
 
 def test_prefill_token_by_token_agrees(monkeypatch):

@@ -80,7 +80,7 @@ def test_ctypes_struct_layout_matches_header(tmp_path):
 def test_default_options():
     o = mk.mk_default_options()
     assert (o.sync_mode, o.xcd_replicas, o.attn_splits, o.grid) == (mk.MK_SYNC_SENTINEL, 8, 0, 0)
-    assert o.watchdog_us > 0 and o.trace_steps == 0
+    assert o.watchdog_us > 0 and o.trace_steps == 0 and o.work_queue == 0
 
 
 def _matrix_params(m: inputs.ModelConfig) -> int:
@@ -172,7 +172,7 @@ def test_plan_rejects(model, max_seq, grid, opts, reason):
 
 
 @pytest.mark.parametrize("field,value", [("xcd_replicas", 3), ("attn_splits", 65), ("sync_mode", 2),
-                                         ("watchdog_us", 0), ("grid", -1), ("attn_splits", -1)])
+                                         ("watchdog_us", 0), ("work_queue", 2), ("grid", -1), ("attn_splits", -1)])
 def test_plan_rejects_options(field, value):
     w = inputs.WORKLOADS["tiny"]
     with pytest.raises(mk.MkError) as e:
