@@ -187,13 +187,21 @@ def time_prefill(mk, ctx, model, ids, reps: int = 3) -> dict:
         kern.append(st["prefill_ms"])
         last.append(st["gpu_ms"])
     n = st["prefill_positions"]
+    stages = None
+    if n:
+        # device-clock (100 MHz) marks of the last launch's grid barriers: embedding, then 5 stages per layer
+        marks = mk.mk_debug_prefill_marks(ctx, model.n_layers).astype(np.int64)
+        per = (np.diff(marks) / 100.0).reshape(model.n_layers, 5)
+        stages = {name: float(per[:, i].mean()) for i, name in
+                  enumerate(["qkv", "attention", "o_proj", "up_gate", "down"])}
+        log("[bench] prefill stages, mean us per layer: " + ", ".join(f"{k} {v:.1f}" for k, v in stages.items()))
     qd, kvd, d, f = model.n_heads * model.head_dim, model.n_kv_heads * model.head_dim, model.d_model, model.ffn
     per_pos = 2 * model.n_layers * ((qd + 2 * kvd) * d + d * qd + 3 * f * d)  # GEMM flops per position
     gemm_flops = per_pos * n
     k_ms = float(np.median(kern))
     out = {"prompt_len": P, "ttft_ms": float(np.median(walls)), "prefill_kernel_ms": k_ms,
            "last_token_decode_ms": float(np.median(last)), "prefill_positions": n, "t0": t0,
-           "prefill_grid": st["prefill_grid"],
+           "prefill_grid": st["prefill_grid"], "stage_us_per_layer": stages,
            "gemm": {"bound": "mfma", "algorithmic_flops": gemm_flops,
                     "achieved": gemm_flops / (k_ms * 1e-3) / 1e12 if n else None, "unit": "TFLOP/s",
                     "peak": MFMA_PEAK_TFLOPS, "frac": gemm_flops / (k_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS if n else None,
