@@ -161,6 +161,7 @@ struct Ring {
   uint32_t n;            // chunks per step
   uint32_t issue;        // next chunk (mod n) to request
   uint32_t slot;         // ring slot holding the next chunk to consume
+  uint32_t owed;         // slots read but not yet refilled (the `owed` slots before `slot`)
 };
 
 // The ring is touched only through inline asm (the DMA that fills a slot and
@@ -217,9 +218,11 @@ __device__ __forceinline__ void ring_load(const uint32_t (&a)[4], u4 (&v)[4]) {
 }
 
 // Next N chunks (N <= 4) with one LDS wait: vmcnt(kRing-N) means the N
-// oldest DMAs (these slots) have landed.  Then refill the N slots.
+// oldest DMAs (these slots) have landed.  Then refill the N slots, or (refill
+// false) leave them owed until ring_settle; no slot may be read while refills
+// are owed.
 template <int N>
-__device__ __forceinline__ void ring_read(Ring& r, u4 (&v)[4]) {
+__device__ __forceinline__ void ring_read(Ring& r, u4 (&v)[4], bool refill = true) {
   static_assert(N >= 1 && N <= 4 && N <= kRing, "ring_read reads 1..4 chunks");
   uint32_t a[4];
   uint32_t slot = r.slot;
@@ -229,12 +232,30 @@ __device__ __forceinline__ void ring_read(Ring& r, u4 (&v)[4]) {
     slot = (slot + 1 == kRing) ? 0 : slot + 1;
   }
   ring_load<N, kRing - N>(a, v);
+  if (!refill) {
+    r.slot = slot;
+    r.owed += N;
+    return;
+  }
 #pragma unroll
   for (int k = 0; k < N; ++k) {
     dma_chunk(r.lds + r.slot * 1024, r.g, r.issue * 1024 + lane_id() * 16);
     r.issue = (r.issue + 1 == r.n) ? 0 : r.issue + 1;
     r.slot = (r.slot + 1 == kRing) ? 0 : r.slot + 1;
   }
+}
+
+// Issue the refills ring_read left owed, oldest slot first, so the ring's
+// DMAs stay in slot order.
+__device__ __forceinline__ void ring_settle(Ring& r) {
+  uint32_t s = r.slot + kRing - r.owed;
+  if (s >= (uint32_t)kRing) s -= kRing;
+  for (uint32_t k = 0; k < r.owed; ++k) {
+    dma_chunk(r.lds + s * 1024, r.g, r.issue * 1024 + lane_id() * 16);
+    r.issue = (r.issue + 1 == r.n) ? 0 : r.issue + 1;
+    s = (s + 1 == (uint32_t)kRing) ? 0 : s + 1;
+  }
+  r.owed = 0;
 }
 
 

@@ -411,14 +411,22 @@ __device__ __forceinline__ bool staged_rows(const Ins& in) {
 
 // ---------------------------------------------------------------- GEMV core
 // The next n (1..4, uniform) chunks of the ring.
-__device__ __forceinline__ void ring_read_n(Ring& ring, u4 (&w)[4], int n) {
+__device__ __forceinline__ void ring_read_n(Ring& ring, u4 (&w)[4], int n, bool refill) {
   switch (n) {
-    case 4: ring_read<4>(ring, w); break;
-    case 3: ring_read<3>(ring, w); break;
-    case 2: ring_read<2>(ring, w); break;
-    default: ring_read<1>(ring, w); break;
+    case 4: ring_read<4>(ring, w, refill); break;
+    case 3: ring_read<3>(ring, w, refill); break;
+    case 2: ring_read<2>(ring, w, refill); break;
+    default: ring_read<1>(ring, w, refill); break;
   }
 }
+
+// The refills of a wavefront's last ring read in an instruction (the second
+// read of a two-row unit) are left owed until the instruction's outputs are
+// published (ring_settle at the end of the op).  A CU's sync stores and loads
+// wait behind the weight requests that CU has in flight: a handoff between two
+// CUs that stream takes about 1.8 us, between two that do not 0.6-0.8 us, with
+// the rest of the chip streaming in both cases.  Issuing the last refills after
+// the stores lets the outputs leave first.
 
 // GEMV body.  CPS = 4: slices of four chunks, the widest and the common case
 // (rows of 2048 or more columns); CPS = 0: any width in.cps = 1..4 with
@@ -426,6 +434,7 @@ __device__ __forceinline__ void ring_read_n(Ring& ring, u4 (&w)[4], int n) {
 // width: the monokernel's code is far larger than the instruction cache.
 template <int CPS, typename Epi>
 __device__ __forceinline__ void gemv(Cx& c, Ring& ring, const Ins& in, const float* vec, float scale, Epi epi) {
+  ring_settle(ring);  // refills an earlier instruction left owed (none unless it deferred them)
   const int ks = in.ks, rg = kWaves / ks, ki = c.wave % ks, gi = c.wave / ks;
   const int upr = in.upr, cps = CPS ? CPS : in.cps;
   float act[4][8];
@@ -446,15 +455,17 @@ __device__ __forceinline__ void gemv(Cx& c, Ring& ring, const Ins& in, const flo
   for (int u = gi; u < in.nu; u += rg) {
     float r0 = 0.f, r1 = 0.f;
     u4 w[4];
-    if constexpr (CPS > 0) ring_read<CPS>(ring, w);
-    else ring_read_n(ring, w, cps);
+    const bool refill = u + rg < in.nu;  // false: this wavefront's last unit
+    const bool refill0 = refill || upr == 2;
+    if constexpr (CPS > 0) ring_read<CPS>(ring, w, refill0);
+    else ring_read_n(ring, w, cps, refill0);
     if (u == gi) ts_mark(c, 7);
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       if (CPS ? k < CPS : k < cps) r0 += dot8(w[k], act[k]);
     if (upr == 2) {
-      if constexpr (CPS > 0) ring_read<CPS>(ring, w);
-      else ring_read_n(ring, w, cps);
+      if constexpr (CPS > 0) ring_read<CPS>(ring, w, refill);
+      else ring_read_n(ring, w, cps, refill);
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         if (CPS ? k < CPS : k < cps) r1 += dot8(w[k], act[k]);
@@ -613,6 +624,7 @@ __device__ __forceinline__ void op_qkv(Cx& c, Ring& ring, const Ins& in) {
     cta_sync(c);
     for (int t = c.tid; t < 2 * in.nu; t += kThreads) store_out(in.u0 + t % in.nu, t / in.nu, outs[t]);
   }
+  ring_settle(ring);
   counter_signal(c, in.sync_out);
 }
 
@@ -1166,6 +1178,7 @@ __device__ __forceinline__ void op_oproj(Cx& c, Ring& ring, const Ins& in) {
     cta_sync(c);
     publish_rows(c, kp.xa, c.e, l, in.u0, in.nu, c.sm.resid, true);
   }
+  ring_settle(ring);
   counter_signal(c, in.sync_out);
 }
 
@@ -1187,6 +1200,7 @@ __device__ __forceinline__ void op_upgate(Cx& c, Ring& ring, const Ins& in) {
     cta_sync(c);
     publish_rows(c, kp.m, c.e, l, in.u0, in.nu, c.sm.resid, true);
   }
+  ring_settle(ring);
   counter_signal(c, in.sync_out);
 }
 
@@ -1210,6 +1224,7 @@ __device__ __forceinline__ void op_down(Cx& c, Ring& ring, const Ins& in) {
     cta_sync(c);
     publish_rows(c, kp.xm, c.e, l, in.u0, in.nu, c.sm.resid, true);
   }
+  ring_settle(ring);
   counter_signal(c, in.sync_out);
 }
 
@@ -1367,6 +1382,7 @@ __device__ __forceinline__ void op_lmhead(Cx& c, Ring& ring, const Ins& in) {
       if (c.lane == 0) __hip_atomic_fetch_add(gp(kp.counters + in.sync_out), 1u, __ATOMIC_RELAXED, MK_SCOPE);
     }
   }
+  ring_settle(ring);
 }
 
 // Sampling instead of the argmax: every workgroup merges the per-workgroup
@@ -1632,6 +1648,7 @@ __device__ __forceinline__ void op_chain(Cx& c, Ring& ring, const Ins& in) {
     cta_sync(c);
     publish_rows(c, kp.y, 0, i, in.u0, in.nu, c.sm.resid, false);
   }
+  ring_settle(ring);
   counter_signal(c, in.sync_out);
 }
 
@@ -1673,6 +1690,7 @@ __global__ __launch_bounds__(kThreads, 1) void MK_MONOKERNEL(const KParams* __re
     ring.g = (const uint8_t*)uniform_ptr(kp.stream + kp.wave_off[wi] * 1024);
     ring.issue = 0;
     ring.slot = 0;
+    ring.owed = 0;
     ring_start(ring);
   }
 
