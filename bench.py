@@ -324,8 +324,19 @@ def main() -> int:
         read = mk.mk_probe_read(buf, repeats=5)
         del buf
         barrier = mk.mk_probe_barrier(2000)
+        handoff = {}
+        for name, mode, same in (("idle_cross_xcd", 0, False), ("idle_same_xcd", 0, True),
+                                 ("streaming_cus_ringless_poller", 1, False),
+                                 ("streaming_cus_poller_streams_too", 2, False),
+                                 ("streaming_cus_same_xcd", 1, True),
+                                 ("quiet_pair_cus_rest_streaming", 3, False),
+                                 ("quiet_pair_cus_rest_streaming_same_xcd", 3, True)):
+            handoff[name] = mk.mk_probe_handoff(mode, same)
+            log(f"[bench] handoff probe {name}: {handoff[name]['us_per_handoff']:.3f} us, "
+                f"{handoff[name]['stream_GB_per_s']:.0f} GB/s streamed, same-XCD pairs {handoff[name]['same_xcd_pairs']:.2f}")
         out = {"probes": "calibration", "launch": launch, "read_4GiB_GB_per_s": read,
                "read_frac_of_8TBps": read / HBM_PEAK_GBS, "naive_grid_barrier_us": barrier,
+               "handoff_under_streaming": handoff,
                "note": "pages' MI300X context: ~4.5 us launch, 7.59-7.88 us atomic grid sync"}
         log(f"[bench] probes: launch {launch['us_per_launch_pipelined']:.2f} us pipelined / "
             f"{launch['us_per_launch_round_trip']:.2f} us round trip; read {read:.0f} GB/s; barrier {barrier:.2f} us")

@@ -83,6 +83,8 @@ SIGNATURES = [
     ("mk_probe_launch", C.c_int, [C.c_int, C.c_void_p, C.c_int32, C.POINTER(C.c_double), C.POINTER(C.c_double)]),
     ("mk_probe_read", C.c_int, [C.c_int, C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.POINTER(C.c_double)]),
     ("mk_probe_barrier", C.c_int, [C.c_int, C.c_void_p, C.c_int32, C.POINTER(C.c_double)]),
+    ("mk_probe_handoff", C.c_int, [C.c_int, C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_double),
+                                   C.POINTER(C.c_double), C.POINTER(C.c_double)]),
     ("mk_position", C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
     ("mk_stats", C.c_int, [C.c_void_p, C.POINTER(mk_stats_t)]),
     ("mk_count_sentinels", C.c_int, [C.c_void_p, C.POINTER(C.c_int64)]),
@@ -259,6 +261,14 @@ def mk_probe_read(buf, repeats: int = 5, device: int = 0, stream=None) -> float:
     _check(lib().mk_probe_read(device, _stream_handle(stream), C.c_void_p(buf.data_ptr()),
                                buf.numel() * buf.element_size(), repeats, C.byref(g)))
     return g.value
+
+
+def mk_probe_handoff(mode: int, same_xcd: bool = False, rounds: int = 2000, device: int = 0, stream=None) -> dict:
+    """Cross-workgroup handoff latency under weight streaming (see include/mk_diag.h)."""
+    us, gbs, same = C.c_double(), C.c_double(), C.c_double()
+    _check(lib().mk_probe_handoff(device, _stream_handle(stream), int(mode), int(bool(same_xcd)), int(rounds),
+                                  C.byref(us), C.byref(gbs), C.byref(same)))
+    return {"us_per_handoff": us.value, "stream_GB_per_s": gbs.value, "same_xcd_pairs": same.value}
 
 
 def mk_probe_barrier(rounds: int = 1000, device: int = 0, stream=None) -> float:

@@ -39,6 +39,11 @@ hipError_t mk_launch_probe_read(const void* p, int64_t n16, void* sink, int grid
 hipError_t mk_launch_probe_barrier(uint32_t* counter, int rounds, uint64_t deadline_ticks, uint64_t* out, int grid,
                                    hipStream_t s);
 hipError_t mk_probe_barrier_occupancy(int* occupancy);
+hipError_t mk_launch_probe_handoff(const void* buf, uint32_t n_chunks, int mode, int same_xcd, int rounds,
+                                   int stream_chunks, uint32_t* flags, uint64_t* ticks, int32_t* xcc,
+                                   uint32_t* timeouts, void* sink, int grid, hipStream_t s);
+hipError_t mk_probe_handoff_occupancy(int* occupancy);
+int mk_probe_handoff_pairs();
 hipError_t mk_launch_count64(const uint64_t* p, int64_t n, int stride, int width, uint64_t v, unsigned long long* out,
                              hipStream_t s);
 hipError_t mk_scratch_address(int device, void** out, size_t* bytes);
@@ -1292,6 +1297,71 @@ int mk_probe_barrier(int device, void* hip_stream, int32_t rounds, double* us_pe
   if (e != hipSuccess) return probe_fail(MK_EHIP, "barrier probe", e);
   if (h[1]) return probe_fail(MK_ETIMEOUT, "a barrier round did not complete within 1 s");
   *us_per_barrier = (double)h[0] * 0.01 / rounds;  // 100 MHz device clock
+  return MK_OK;
+}
+
+int mk_probe_handoff(int device, void* hip_stream, int32_t mode, int32_t same_xcd, int32_t rounds, double* us_handoff,
+                     double* stream_gb_per_s, double* same_xcd_fraction) {
+  if (mode < 0 || mode > 3 || rounds < 1 || rounds > 100000 || !us_handoff || !stream_gb_per_s || !same_xcd_fraction)
+    return probe_fail(MK_EINVAL, "bad probe arguments");
+  g_create_error.clear();
+  hipStream_t s = (hipStream_t)hip_stream;
+  PROBE_HIP(hipSetDevice(device), "hipSetDevice");
+  hipDeviceProp_t prop;
+  PROBE_HIP(hipGetDeviceProperties(&prop, device), "device properties");
+  const int grid = prop.multiProcessorCount, pairs = mk_probe_handoff_pairs();
+  int occ = 0;
+  PROBE_HIP(mk_probe_handoff_occupancy(&occ), "occupancy");
+  if (occ < 1) return probe_fail(MK_EOCC, "handoff probe does not fit a CU");
+  if (grid < 2 * pairs) return probe_fail(MK_EOCC, "handoff probe needs 32 CUs");
+  const int64_t buf_bytes = 1LL << 30;
+  const int stream_chunks = 24000;
+  void *buf = nullptr, *sink = nullptr;
+  uint32_t* words = nullptr;  // flags [pairs][2][64], then timeouts
+  uint64_t* ticks = nullptr;
+  int32_t* xcc = nullptr;
+  const int64_t n_words = (int64_t)pairs * 2 * 64 + 1;
+  hipError_t e = hipMalloc(&buf, buf_bytes);
+  if (e == hipSuccess) e = hipMalloc(&sink, (size_t)grid * 512 * 16);
+  if (e == hipSuccess) e = hipMalloc((void**)&words, n_words * 4);
+  if (e == hipSuccess) e = hipMalloc((void**)&ticks, pairs * 8);
+  if (e == hipSuccess) e = hipMalloc((void**)&xcc, pairs * 2 * 4);
+  if (e == hipSuccess) e = mk_launch_fill32(words, n_words, 0u, s);
+  if (e == hipSuccess) e = mk_launch_fill32((uint32_t*)ticks, pairs * 2, 0u, s);
+  if (e == hipSuccess) e = mk_launch_fill32((uint32_t*)xcc, pairs * 2, 0xFFFFFFFFu, s);
+  hipEvent_t a = nullptr, b = nullptr;
+  if (e == hipSuccess) e = hipEventCreate(&a);
+  if (e == hipSuccess) e = hipEventCreate(&b);
+  if (e == hipSuccess) e = hipEventRecord(a, s);
+  if (e == hipSuccess)
+    e = mk_launch_probe_handoff(buf, (uint32_t)(buf_bytes / 1024), mode, same_xcd ? 1 : 0, rounds, stream_chunks, words,
+                                ticks, xcc, words + n_words - 1, sink, grid, s);
+  if (e == hipSuccess) e = hipEventRecord(b, s);
+  std::vector<uint64_t> h_ticks(pairs);
+  std::vector<int32_t> h_xcc(pairs * 2);
+  uint32_t h_timeouts = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(h_ticks.data(), ticks, pairs * 8, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(h_xcc.data(), xcc, pairs * 8, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(&h_timeouts, words + n_words - 1, 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  float ms = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
+  if (a) hipEventDestroy(a);
+  if (b) hipEventDestroy(b);
+  hipFree(buf);
+  hipFree(sink);
+  hipFree(words);
+  hipFree(ticks);
+  hipFree(xcc);
+  if (e != hipSuccess) return probe_fail(MK_EHIP, "handoff probe", e);
+  if (h_timeouts) return probe_fail(MK_ETIMEOUT, "a handoff of the probe hit its spin limit");
+  std::sort(h_ticks.begin(), h_ticks.end());
+  *us_handoff = (double)h_ticks[pairs / 2] * 0.01 / rounds / 2.0;  // median pair, 100 MHz clock, half a round trip
+  int same = 0;
+  for (int i = 0; i < pairs; ++i) same += h_xcc[2 * i] == h_xcc[2 * i + 1];
+  *same_xcd_fraction = (double)same / pairs;
+  const double waves = mode == 1 ? grid * 7.0 : mode == 2 ? grid * 8.0 - pairs * 2 : mode == 3 ? (grid - 2.0 * pairs) * 8 : 0.0;
+  *stream_gb_per_s = waves * stream_chunks * 1024.0 / (ms * 1e-3) / 1e9;
   return MK_OK;
 }
 

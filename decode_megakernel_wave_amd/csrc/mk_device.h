@@ -218,9 +218,10 @@ __device__ __forceinline__ void ring_load(const uint32_t (&a)[4], u4 (&v)[4]) {
 }
 
 // Next N chunks (N <= 4) with one LDS wait: vmcnt(kRing-N) means the N
-// oldest DMAs (these slots) have landed.  Then refill the N slots, or (refill
-// false) leave them owed until ring_settle; no slot may be read while refills
-// are owed.
+// oldest DMAs (these slots) have landed, which holds only while all kRing
+// slots have a DMA issued (owed == 0).  Then refill the N slots, or (refill
+// false) leave them owed until ring_settle: no slot may be read while
+// refills are owed, so only an instruction's last read defers them.
 template <int N>
 __device__ __forceinline__ void ring_read(Ring& r, u4 (&v)[4], bool refill = true) {
   static_assert(N >= 1 && N <= 4 && N <= kRing, "ring_read reads 1..4 chunks");

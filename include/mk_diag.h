@@ -111,10 +111,23 @@ int mk_chain_debug_ts(mk_chain* ch, uint64_t* host, int64_t capacity);
  * mk_probe_barrier: `rounds` (1..1e6) grid barriers of one workgroup per CU, each a release,
  *   an atomic add to one counter and system-scope polls until every workgroup has arrived;
  *   microseconds per barrier on the device clock.  A round that does not complete within 1 s
- *   ends every wait and returns MK_ETIMEOUT. */
+ *   ends every wait and returns MK_ETIMEOUT.
+ * mk_probe_handoff: the latency of one cross-workgroup handoff (a system-scope store seen by
+ *   a system-scope poll, "7 - AMD et le monokernel", section 7.3) while the chip streams 1 KB
+ *   weight chunks through per-wavefront LDS rings (12 slots, nontemporal), one workgroup per
+ *   CU, 16 workgroup pairs ping-ponging `rounds` (1..1e5) times.  mode 0: nothing streams;
+ *   1: every CU streams on 7 wavefronts and the pairs' 8th wavefront only polls; 2: all 8
+ *   wavefronts stream and the pairs' 8th consumes 4 chunks of its ring before each handoff;
+ *   3: the pairs' CUs stream nothing and every other CU streams on 8 wavefronts.  same_xcd
+ *   pairs workgroups k and k+8 (one XCD under round-robin dispatch), else 2k and 2k+1.
+ *   Outputs: median microseconds per handoff (half a round trip), GB/s streamed over the
+ *   launch, and the fraction of pairs whose two members reported the same XCC_ID.  Allocates
+ *   and frees 1 GiB of device memory; a wait beyond its spin limit returns MK_ETIMEOUT. */
 int mk_probe_launch(int device, void* hip_stream, int32_t n_launches, double* us_pipelined, double* us_round_trip);
 int mk_probe_read(int device, void* hip_stream, const void* buf, int64_t bytes, int32_t repeats, double* gb_per_s);
 int mk_probe_barrier(int device, void* hip_stream, int32_t rounds, double* us_per_barrier);
+int mk_probe_handoff(int device, void* hip_stream, int32_t mode, int32_t same_xcd, int32_t rounds, double* us_handoff,
+                     double* stream_gb_per_s, double* same_xcd_fraction);
 
 #ifdef __cplusplus
 }
