@@ -15,11 +15,19 @@ from decode_megakernel_wave_amd import inputs  # noqa: E402
 
 def test_cpu_baseline_record_on_the_tiny_decoder():
     w = inputs.make_weights(inputs.TINY, seed=0)
-    r = bench.cpu_baseline(inputs.TINY, w, 32, 16, prompt_len=8, steps=2, steps_1t=1)
+    r = bench.cpu_baseline(inputs.TINY, w, 32, 16, steps=2, steps_1t=1)
     assert r["kind"] == "oracle" and r["unit"] == "tokens/s" and r["value"] > 0
     assert r["cores"] >= 1
     assert r["one_thread"]["cores"] == 1 and r["one_thread"]["value"] > 0
-    assert "tiny decoder" in r["sample"] and "32..48" in r["sample"]
+    assert r["prefill_tokens"] == 32 and r["prefill_s"] > 0
+    assert "tiny decoder" in r["sample"] and "33..34" in r["sample"] and "33..48" in r["sample"]
+
+
+def test_cpu_baseline_cuts_long_prompts():
+    w = inputs.make_weights(inputs.TINY, seed=0)
+    r = bench.cpu_baseline(inputs.TINY, w, 40, 16, steps=1, steps_1t=1, max_prompt=16)
+    assert r["prefill_tokens"] == 16
+    assert "16-token prompt" in r["sample"] and "instead of 40..56" in r["sample"]
 
 
 def test_traffic_lookup_needs_the_same_sources_and_launch(tmp_path, monkeypatch):
