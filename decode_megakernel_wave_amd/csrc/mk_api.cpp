@@ -370,6 +370,11 @@ struct mk_ctx {
   uint32_t* d_pbar = nullptr;
   uint64_t* d_pmarks = nullptr;     // [1 + 5 L + 1]: start, then each grid barrier (device clock)
   uint32_t* d_pqueue = nullptr;     // [1 + 5 L] work-queue counters
+  float* d_ppart = nullptr;         // [grid][kPartFloats] split-K partial tiles
+  float* d_pXhl = nullptr;          // [2][P][d] fp16 hi / lo halves of x times the next gain
+  float* d_pssp = nullptr;          // [ceil(d / 128)][P] partial sums of squares of x
+  int pf_ldo = 0, pf_ldm = 0;       // row strides (halves) of the attention-output and MLP planes
+  uint32_t* d_ptile = nullptr;      // [grid] split-K arrival counters
   PParams* d_pp = nullptr;
   PParams h_pp{};
 };
@@ -440,7 +445,12 @@ int ctx_alloc_prefill(mk_ctx* c) {
   Engine& g = c->g;
   const mk_config& k = c->cfg;
   const int qd = k.n_heads * k.head_dim, kvd = k.n_kv_heads * k.head_dim;
-  c->pf_ok = k.d_model % 8 == 0 && k.ffn % 8 == 0 && qd % 8 == 0;
+  // d_model a multiple of 32 and at most 8192: the normed GEMMs (K = d_model) take whole
+  // 32-column steps and stage their gain in LDS; the GEMM tiles address an activation matrix
+  // with 32-bit byte offsets
+  const int64_t widest = std::max<int64_t>(std::max(k.d_model, k.ffn), qd);
+  c->pf_ok = k.d_model % 32 == 0 && k.d_model <= 8192 && k.ffn % 8 == 0 && qd % 8 == 0 &&
+             (int64_t)std::max(1, k.max_seq - 1) * widest * 4 < (1LL << 32);
   if (!c->pf_ok) return MK_OK;
   c->pf_lds = mk_prefill_lds_bytes(k.head_dim);
   int occ = 0;
@@ -456,12 +466,21 @@ int ctx_alloc_prefill(mk_ctx* c) {
   CHK(g.alloc(&c->d_canon, (size_t)per_layer * k.n_layers * 2));
   CHK(g.alloc(&c->d_pX, (size_t)P * k.d_model * 4));
   CHK(g.alloc(&c->d_pQ, (size_t)P * qd * 4));
-  CHK(g.alloc(&c->d_pO, (size_t)P * qd * 4));
-  CHK(g.alloc(&c->d_pM, (size_t)P * k.ffn * 4));
+  c->pf_ldo = (qd + 31) / 32 * 32;
+  c->pf_ldm = (k.ffn + 31) / 32 * 32;
+  CHK(g.alloc(&c->d_pO, (size_t)P * c->pf_ldo * 4));   // hi and lo planes
+  CHK(g.alloc(&c->d_pM, (size_t)P * c->pf_ldm * 4));
+  CHK(g.alloc(&c->d_pXhl, (size_t)P * k.d_model * 4));
+  CHK(g.alloc(&c->d_pssp, (size_t)((k.d_model + 127) / 128) * P * 4));
+  // the pad columns of the A planes stay zero (no producer writes them)
+  HIPCHK(g, mk_launch_fill32((uint32_t*)c->d_pO, P * c->pf_ldo, 0u, g.stream));
+  HIPCHK(g, mk_launch_fill32((uint32_t*)c->d_pM, P * c->pf_ldm, 0u, g.stream));
   CHK(g.alloc(&c->d_pids, (size_t)P * 4));
   CHK(g.alloc(&c->d_pbar, 256));
   CHK(g.alloc(&c->d_pmarks, (size_t)(5 * k.n_layers + 2) * 8));
   CHK(g.alloc(&c->d_pqueue, (size_t)(5 * k.n_layers + 2) * 4));
+  CHK(g.alloc(&c->d_ppart, (size_t)c->pf_grid * kPartFloats * 4));
+  CHK(g.alloc(&c->d_ptile, (size_t)c->pf_grid * 4));
   CHK(g.alloc(&c->d_pp, sizeof(PParams)));
   return MK_OK;
 }
@@ -497,8 +516,16 @@ int ctx_prefill_mfma(mk_ctx* c, const int32_t* ids, int n) {
   pp.vc = c->d_vc;
   pp.X = c->d_pX;
   pp.Q = c->d_pQ;
-  pp.O = c->d_pO;
-  pp.M = c->d_pM;
+  const int64_t Pa = std::max(1, k.max_seq - 1);
+  pp.Oh = (uint16_t*)c->d_pO;
+  pp.Ol = pp.Oh + Pa * c->pf_ldo;
+  pp.Mh = (uint16_t*)c->d_pM;
+  pp.Ml = pp.Mh + Pa * c->pf_ldm;
+  pp.Xh = (uint16_t*)c->d_pXhl;
+  pp.Xl = pp.Xh + Pa * k.d_model;
+  pp.ssp = c->d_pssp;
+  pp.ldo = c->pf_ldo;
+  pp.ldm = c->pf_ldm;
   pp.barrier = c->d_pbar;
   pp.abort_flag = g.d_abort;
   pp.fault = g.d_fault;
@@ -507,7 +534,10 @@ int ctx_prefill_mfma(mk_ctx* c, const int32_t* ids, int n) {
   pp.marks = c->d_pmarks;
   pp.queue = c->d_pqueue;
   pp.dynamic = g.opt.work_queue;
+  pp.part = c->d_ppart;
+  pp.tile_cnt = c->d_ptile;
   HIPCHK(g, mk_launch_fill32(c->d_pqueue, 5 * k.n_layers + 2, 0u, g.stream));
+  HIPCHK(g, mk_launch_fill32(c->d_ptile, c->pf_grid, 0u, g.stream));
   HIPCHK(g, mk_launch_fill32((uint32_t*)c->d_pmarks, 2 * (5 * k.n_layers + 2), 0u, g.stream));
   HIPCHK(g, hipMemcpyAsync(c->d_pp, &pp, sizeof(PParams), hipMemcpyHostToDevice, g.stream));
   HIPCHK(g, hipEventRecord(g.ev0, g.stream));

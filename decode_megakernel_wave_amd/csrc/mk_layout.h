@@ -152,8 +152,16 @@ struct PParams {
   uint16_t* vc;
   float* X;                 // [P][d] residual stream
   float* Q;                 // [P][nq hd] rotated queries
-  float* O;                 // [P][nq hd] attention output
-  float* M;                 // [P][f] silu(gate) * up
+  // GEMM A operands as fp16 hi + lo halves of fp32 values (a = hi + lo to 2^-22), written by their
+  // producers; rows padded with zeros to a multiple of 32 columns
+  uint16_t* Oh;             // [P][ldo] attention output, hi halves
+  uint16_t* Ol;             //          lo halves
+  uint16_t* Mh;             // [P][ldm] silu(gate) * up
+  uint16_t* Ml;
+  uint16_t* Xh;             // [P][d] x times the gain of the next RMSNorm
+  uint16_t* Xl;
+  float* ssp;               // [ceil(d / 128)][P] sums of x^2 over 128-column blocks (for 1 / rms)
+  int32_t ldo, ldm;
   uint32_t* barrier;        // grid barrier counter (zero at launch)
   uint32_t* abort_flag;
   Fault* fault;
@@ -163,6 +171,10 @@ struct PParams {
   uint32_t* queue;          // [1 + 5 L] work-queue counters, one per stage (zero at launch)
   int32_t dynamic;          // 1: workgroups / wavefronts claim their tiles from the queue; 0: static deal
   int32_t pad1;
+  float* part;              // split-K partial tiles: [grid][kPartFloats]
+  uint32_t* tile_cnt;       // [grid] split-K arrivals per output tile (zero at launch and between stages)
 };
+// One split-K partial: a 128 x 128 tile of fp32 accumulators plus its 128 row sums of squares.
+constexpr int kPartFloats = 128 * 128 + 128;
 
 }  // namespace mk

@@ -40,14 +40,22 @@ constexpr int kPW = kPT / 64;          // wavefronts per workgroup
 constexpr int kTM = 128;               // GEMM tile: rows (positions)
 constexpr int kTN = 128;               // GEMM tile: weight rows (64 units of two rows, or 128 columns)
 constexpr int kTK = 32;                // K per pipeline step (two MFMA steps of 16)
-constexpr int kLS = kTK + 8;           // LDS row stride in halves (padding spreads the banks)
-constexpr int kOpHalves = kTM * kLS;   // one staged operand tile
-// LDS: A hi, A lo, B, each double-buffered, then the row scales
-constexpr int kGemmLdsBytes = 6 * kOpHalves * 2 + kTM * 4;
+// LDS of a GEMM tile: kNst stages of operands as the DMA leaves them (A hi,
+// A lo and B, each [128 rows][32 halves] with the rows' 16-byte chunks
+// XOR-swizzled), the row scales, the epilogue's row-sum scratch, a flag word,
+// then the work-queue slot.
+constexpr int kNst = 6;
+constexpr int kOpBytes = kTM * kTK * 2;           // one operand of one step: 8 KB
+constexpr int kStage = 3 * kOpBytes;
+constexpr int kRsOff = kNst * kStage;
+constexpr int kRedOff = kRsOff + kTM * 4;         // [2][128] row sums of squares of the two column halves
+constexpr int kFlagOff = kRedOff + 2 * kTM * 4;
+constexpr int kGemmLdsBytes = kFlagOff + 16;
 // The work-queue slot a workgroup reads its claimed tile from, past every
-// stage's own LDS use (the largest: 8 wavefronts' V^T blocks at head_dim 128).
-constexpr int kClaimOff = 8 * 128 * 40 * 2;
-static_assert(kClaimOff >= kGemmLdsBytes, "claim slot overlaps the GEMM staging");
+// stage's own LDS use.
+constexpr int kClaimOff = kGemmLdsBytes;
+static_assert(kClaimOff + 16 <= 160 * 1024, "prefill LDS exceeds a CU's 160 KB");
+static_assert(kTM == 128 && kTN == 128 && kTK == 32, "a stage is 3 x 8 DMAs of 1 KB: 3 per wavefront");
 
 enum Epi { EPI_QKV = 0, EPI_UG = 1, EPI_RESID = 2 };
 
@@ -86,7 +94,7 @@ __device__ __forceinline__ bool grid_barrier(PCx& c, int op, int layer) {
   // one release then writes them back to memory for the other XCDs
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  uint32_t* flag = (uint32_t*)(pf_smem + kGemmLdsBytes - 4);
+  uint32_t* flag = (uint32_t*)(pf_smem + kFlagOff);
   if (c.tid == 0) {
     const PParams& p = *c.pp;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
@@ -112,7 +120,9 @@ __device__ __forceinline__ bool grid_barrier(PCx& c, int op, int layer) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     *flag = failed;
     stc32(p.progress + c.cta, c.epoch + 1);
+#ifndef MK_PF_STEPMARKS
     if (p.marks && c.cta == 0) *gp(p.marks + c.epoch) = __builtin_amdgcn_s_memrealtime();
+#endif
   }
   __syncthreads();
   const uint32_t failed = __builtin_amdgcn_readfirstlane(*flag);
@@ -133,14 +143,17 @@ __device__ __forceinline__ bool grid_barrier(PCx& c, int op, int layer) {
 struct Gemm {
   int ep;                  // Epi
   int layer;
-  const float* A;          // activations
-  int lda, K;              // row stride and columns of A (= weight row length)
-  const uint16_t* gain;    // RMSNorm gain (fp16 [K]) or null: no norm
+  const uint16_t* Ah;      // A operand: fp16 hi halves [rows][lda]
+  const uint16_t* Al;      //            lo halves
+  int lda;                 // row stride of A in halves, a multiple of 32: the K steps cover [0, lda)
+  int K;                   // weight row length (A's columns K .. lda are zero)
+  int norm;                // RMSNorm: output rows scaled by 1/rms(x), from p.ssp
   const uint16_t* W;       // weights: [rows][K] fp16
   int n_out;               // units (QKV, UG) or output columns (RESID)
-  float* out;              // RESID: x [rows][ld_out], added to; UG: m [rows][ld_out]
+  float* out;              // RESID: x [rows][ld_out], added to
   int ld_out;
   const uint16_t* W2;      // UG: the up rows (W holds the gate rows)
+  const uint16_t* gnext;   // RESID: gain of the next RMSNorm (its x halves and sums of squares), or null
 };
 
 // Weight row (within g.W / g.W2) of tile row j of tile tn; null when j is past the matrix.
@@ -158,89 +171,165 @@ __device__ __forceinline__ const uint16_t* b_row(const PParams& p, const Gemm& g
   return g.W + (int64_t)(head * p.hd + i + mem * hh) * g.K;
 }
 
-__device__ __forceinline__ void gemm_tile(PCx& c, const Gemm& g, int tm, int tn) {
-  const PParams& p = *c.pp;
-  _Float16* Ahi = (_Float16*)pf_smem;
-  _Float16* Alo = Ahi + 2 * kOpHalves;
-  _Float16* Bt = Alo + 2 * kOpHalves;
-  float* rs = (float*)(Bt + 2 * kOpHalves);
-  const int m0 = tm * kTM;
-  // staging: thread t loads row t / 4, columns (t % 4) * 8 .. + 8 of the K step (A and B alike)
-  const int srow = c.tid >> 2, skq = (c.tid & 3) * 8;
-  const bool arow_ok = m0 + srow < p.P;
-  const float* arow = g.A + (int64_t)(m0 + srow) * g.lda;
-  const uint16_t* brow = b_row(p, g, tn, srow);
-  const int nsteps = (g.K + kTK - 1) / kTK;
-  float ss = 0.f;
-  f4 av0, av1;
-  u4 bv, gv;
+// One split-K item of a tile: K columns [k0, k0 + kc) of tile (tm, tn).  With
+// S = 1 the item is the whole tile and applies the epilogue itself.  With S > 1
+// every split stores its accumulators and row sums of squares to its slot of
+// p.part and counts itself in at the tile's counter; the split that arrives
+// last adds the S partials in split order (so the result does not depend on
+// which workgroup arrives last) and applies the epilogue.
+// 1 KB global -> LDS transfer of one wavefront (lane i's 16 bytes at LDS
+// lds_addr + 16 i), default cache policy: the operands are re-read by other tiles.
+__device__ __forceinline__ void dma16(uint32_t lds_addr, const void* base, uint32_t voff) {
+  uint32_t save;
+  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
+  base = uniform_ptr(base);
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds_addr), "v"(voff), "s"(base));
+}
 
-  auto load = [&](int s) {
-    const int k = s * kTK + skq;
-    const bool kin = k < g.K;  // K is a multiple of 8: an 8-group is wholly in or out
-    if (arow_ok && kin) {
-      av0 = *gp((const f4*)(arow + k));
-      av1 = *gp((const f4*)(arow + k + 4));
-    } else {
-      av0 = f4{0.f, 0.f, 0.f, 0.f};
-      av1 = av0;
-    }
-    bv = (brow && kin) ? *gp((const u4*)(brow + k)) : u4{0u, 0u, 0u, 0u};
-    if (g.gain) gv = kin ? *gp((const u4*)(g.gain + k)) : u4{0u, 0u, 0u, 0u};
-  };
-  auto stage = [&](int buf) {
-    float a[8] = {av0[0], av0[1], av0[2], av0[3], av1[0], av1[1], av1[2], av1[3]};
-    h8 hi, lo;
-    if (g.gain) {
-      const h8 gh = __builtin_bit_cast(h8, gv);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        ss = fmaf(a[e], a[e], ss);
-        a[e] *= (float)gh[e];
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      hi[e] = (_Float16)a[e];
-      lo[e] = (_Float16)(a[e] - (float)hi[e]);
-    }
-    const int o = buf * kOpHalves + srow * kLS + skq;
-    *(h8*)(Ahi + o) = hi;
-    *(h8*)(Alo + o) = lo;
-    *(u4*)(Bt + o) = bv;
+// Wait until at most 3 n of this wavefront's DMAs are in flight (n = 0 .. kNst - 2).
+__device__ __forceinline__ void dma_wait(int n) {
+  static_assert(kNst - 2 <= 4, "dma_wait covers up to 4 later steps");
+  switch (n) {
+    case 4: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+
+// Byte offset in a stage operand of row r's 16-byte chunk q (8 halves): the
+// chunks of a 64-byte row are XOR-swizzled by (r / 4) % 4, so that the MFMA
+// fragment reads of 8 consecutive lanes (8 consecutive rows) hit distinct banks.
+__device__ __forceinline__ int op_chunk(int r, int q) { return r * 64 + ((q ^ ((r >> 2) & 3)) << 4); }
+
+// One split-K item of a tile: K columns [k0, k0 + kc) of tile (tm, tn).  With
+// S = 1 the item is the whole tile and applies the epilogue itself.  With S > 1
+// every split stores its accumulators to its slot of p.part and counts itself
+// in at the tile's counter; the split that arrives last adds the S partials in
+// split order (so the result does not depend on which workgroup arrives last)
+// and applies the epilogue.
+//
+// The operands stream through kNst LDS stages by global -> LDS DMA, kNst - 1 K
+// steps ahead of the matrix cores: per step each wavefront moves 1 KB of A hi,
+// A lo and B (16 rows x 64 bytes each), which the MFMAs read as they landed.
+__device__ __forceinline__ void gemm_tile(PCx& c, const Gemm& g, int tm, int tn, int split, int S, int tile, int tiles) {
+  const PParams& p = *c.pp;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)pf_smem;
+  float* rs = (float*)(pf_smem + kRsOff);
+  const int m0 = tm * kTM;
+  const int kc = g.lda / S, k0 = split * kc;
+  const int nsteps = kc / kTK;
+  // DMA lanes: transfer of wavefront w covers rows 16 w .. 16 w + 15 of an operand; lane i -> row
+  // 16 w + i / 4, LDS chunk i % 4, which holds the row's chunk (i % 4) ^ ((row / 4) % 4)
+  const int drow = 16 * c.wave + (c.lane >> 2);
+  const int dq = (c.lane & 3) ^ ((drow >> 2) & 3);
+  const uint32_t a_off = (uint32_t)((int64_t)min(m0 + drow, p.P - 1) * g.lda * 2) + (uint32_t)dq * 16u;
+  const uint16_t* br = b_row(p, g, tn, drow);
+  const uint32_t b_off = (uint32_t)((br ? br - g.W : 0) * 2);
+  auto issue = [&](int s) {
+    const uint32_t st = lds0 + (uint32_t)((s % kNst) * kStage) + c.wave * 1024;
+    const int k = k0 + s * kTK;
+    dma16(st, g.Ah, a_off + (uint32_t)k * 2u);
+    dma16(st + kOpBytes, g.Al, a_off + (uint32_t)k * 2u);
+    // B rows have K columns: past K (the zero columns of A) the chunk is clamped to the row's last one
+    const uint32_t kb = (uint32_t)min(k + dq * 8, g.K - 8);
+    dma16(st + 2 * kOpBytes, g.W, b_off + kb * 2u);
   };
 
   f32x16 acc0 = {}, acc1 = {};
   const int rb = c.wave & 3, cb = c.wave >> 2;
   const int l32 = c.lane & 31, lh = c.lane >> 5;
-  load(0);
-  stage(0);
-  __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nsteps) load(s + 1);
+  const int ar = rb * 32 + l32, br0 = cb * 64 + l32;  // this lane's A row and B rows (b1: br0 + 32, same swizzle)
+  auto mfma_step = [&](int s) {
+    const uint8_t* st = pf_smem + (s % kNst) * kStage;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-      const int ko = sub * 16 + lh * 8;
-      const int oa = buf * kOpHalves + (rb * 32 + l32) * kLS + ko;
-      const int ob = buf * kOpHalves + (cb * 64 + l32) * kLS + ko;
-      const h8 ahi = *(const h8*)(Ahi + oa);
-      const h8 alo = *(const h8*)(Alo + oa);
-      const h8 b0 = *(const h8*)(Bt + ob);
-      const h8 b1 = *(const h8*)(Bt + ob + 32 * kLS);
+      const int q = sub * 2 + lh;
+      const h8 ahi = *(const h8*)(st + op_chunk(ar, q));
+      const h8 alo = *(const h8*)(st + kOpBytes + op_chunk(ar, q));
+      const h8 b0 = *(const h8*)(st + 2 * kOpBytes + op_chunk(br0, q));
+      const h8 b1 = *(const h8*)(st + 2 * kOpBytes + op_chunk(br0 + 32, q));
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, b0, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, b1, acc1, 0, 0, 0);
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, b0, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, b1, acc1, 0, 0, 0);
     }
-    if (s + 1 < nsteps) stage(buf ^ 1);
+  };
+  // prologue: steps 0 .. kNst - 2 in flight
+  for (int s = 0; s < kNst - 1 && s < nsteps; ++s) issue(s);
+  // step s: wait for step s's DMAs (the later ones may stay in flight), then issue step s + kNst - 1
+  // into the stage step s - 1 used, and multiply step s
+#ifdef MK_PF_STEPMARKS
+  const bool mk_rec = g.ep == EPI_UG && g.layer == 0 && c.cta == 0 && c.tid == 0 && tm == 0 && p.marks;
+#define PF_MARK(i) \
+  if (mk_rec && s < 20) *gp(p.marks + s * 6 + (i)) = __builtin_amdgcn_s_memrealtime();
+#else
+#define PF_MARK(i)
+#endif
+  for (int s = 0; s < nsteps; ++s) {
+    PF_MARK(0)
+    dma_wait(min(s + kNst - 2, nsteps - 1) - s);
+    PF_MARK(1)
     __syncthreads();
+    PF_MARK(2)
+    if (s + kNst - 1 < nsteps) issue(s + kNst - 1);
+    PF_MARK(3)
+    mfma_step(s);
+    PF_MARK(4)
+    PF_MARK(5)
   }
-  // RMSNorm row scales: the 4 threads of a staged row hold its partial sums
-  if (g.gain) {
-    ss += __shfl_xor(ss, 1);
-    ss += __shfl_xor(ss, 2);
-    if ((c.tid & 3) == 0) rs[srow] = 1.0f / __builtin_sqrtf(ss / (float)g.K + p.eps);
+  __syncthreads();  // every wavefront's MFMAs are done with the stages
+  if (S > 1) {
+    float* mine = p.part + (int64_t)(split * tiles + tile) * kPartFloats;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      *gp(mine + (c.wave * 32 + v) * 64 + c.lane) = acc0[v];
+      *gp(mine + (c.wave * 32 + 16 + v) * 64 + c.lane) = acc1[v];
+    }
+    // release this partial, then count it in; the last split of the tile goes on
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    uint32_t* last = (uint32_t*)(pf_smem + kClaimOff + 8);
+    if (c.tid == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      const uint32_t before = __hip_atomic_fetch_add(gp(p.tile_cnt + tile), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      const uint32_t is_last = before == (uint32_t)S - 1;
+      if (is_last) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __hip_atomic_store(gp(p.tile_cnt + tile), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);  // for the next stage
+      }
+      *last = is_last;
+    }
+    __syncthreads();
+    const uint32_t is_last = __builtin_amdgcn_readfirstlane(*last);
+    __syncthreads();
+    if (!is_last) return;
+    acc0 = f32x16{};
+    acc1 = f32x16{};
+    for (int sp = 0; sp < S; ++sp) {
+      const float* src = p.part + (int64_t)(sp * tiles + tile) * kPartFloats;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        acc0[v] += *gp(src + (c.wave * 32 + v) * 64 + c.lane);
+        acc1[v] += *gp(src + (c.wave * 32 + 16 + v) * 64 + c.lane);
+      }
+    }
+  }
+  if (g.norm) {
+    // 1 / rms of each row from its 128-column sums of squares (fixed order)
+    if (c.tid < kTM) {
+      const int pos = min(m0 + c.tid, p.P - 1), nblk = (p.d + 127) / 128;
+      float t = 0.f;
+      for (int j = 0; j < nblk; ++j) t += *gp(p.ssp + (int64_t)j * p.P + pos);
+      rs[c.tid] = 1.0f / __builtin_sqrtf(t / (float)p.d + p.eps);
+    }
     __syncthreads();
   }
   // epilogue: accumulator register v of lane l holds tile row 32 rb + 8 (v / 4) + 4 (l / 32) + v % 4,
@@ -251,19 +340,49 @@ __device__ __forceinline__ void gemm_tile(PCx& c, const Gemm& g, int tm, int tn)
     const int pos = m0 + r;
     if (pos >= p.P) continue;
     float a = acc0[v], b = acc1[v];
-    if (g.gain) {
+    if (g.norm) {
       const float sc = rs[r];
       a *= sc;
       b *= sc;
     }
     if (g.ep == EPI_RESID) {
+      // x += a; then x times the next gain as hi + lo halves, and x^2 towards the row's block sum
       const int n = tn * kTN + cb * 64 + l32;
       float* xo = g.out + (int64_t)pos * g.ld_out;
-      if (n < g.n_out) *gp(xo + n) += a;
-      if (n + 32 < g.n_out) *gp(xo + n + 32) += b;
+      float sq = 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int nn = n + 32 * h;
+        if (nn < g.n_out) {
+          const float x = *gp(xo + nn) + (h ? b : a);
+          *gp(xo + nn) = x;
+          if (g.gnext) {
+            const float xg = x * (float)__builtin_bit_cast(_Float16, *gp(g.gnext + nn));
+            const _Float16 hi = (_Float16)xg;
+            *gp(p.Xh + (int64_t)pos * g.ld_out + nn) = __builtin_bit_cast(uint16_t, hi);
+            *gp(p.Xl + (int64_t)pos * g.ld_out + nn) = __builtin_bit_cast(uint16_t, (_Float16)(xg - (float)hi));
+            sq = fmaf(x, x, sq);
+          }
+        }
+      }
+      if (g.gnext) {
+        // the tile's 128 columns of row r: 32 lanes x 2 columns here, the other wavefront of the row
+        // (cb ^ 1) holds the other 64 columns
+        sq += __shfl_xor(sq, 1);
+        sq += __shfl_xor(sq, 2);
+        sq += __shfl_xor(sq, 4);
+        sq += __shfl_xor(sq, 8);
+        sq += __shfl_xor(sq, 16);
+        if (l32 == 0) ((float*)(pf_smem + kRedOff))[cb * kTM + r] = sq;
+      }
     } else if (g.ep == EPI_UG) {
       const int u = tn * 64 + cb * 32 + l32;
-      if (u < g.n_out) *gp(g.out + (int64_t)pos * g.ld_out + u) = a / (1.0f + __expf(-a)) * b;
+      if (u < g.n_out) {
+        const float m = a / (1.0f + __expf(-a)) * b;
+        const _Float16 hi = (_Float16)m;
+        *gp(p.Mh + (int64_t)pos * p.ldm + u) = __builtin_bit_cast(uint16_t, hi);
+        *gp(p.Ml + (int64_t)pos * p.ldm + u) = __builtin_bit_cast(uint16_t, (_Float16)(m - (float)hi));
+      }
     } else {
       const int u = tn * 64 + cb * 32 + l32;
       if (u >= g.n_out) continue;
@@ -288,7 +407,15 @@ __device__ __forceinline__ void gemm_tile(PCx& c, const Gemm& g, int tm, int tn)
       }
     }
   }
-  __syncthreads();  // the staging buffers and scales are reused by the next tile
+  if (g.ep == EPI_RESID && g.gnext) {
+    __syncthreads();
+    // note: rows past P kept their partial sums out of the loop above (it skips them)
+    if (c.tid < kTM && m0 + c.tid < p.P) {
+      const float* red = (const float*)(pf_smem + kRedOff);
+      *gp(p.ssp + (int64_t)tn * p.P + m0 + c.tid) = red[c.tid] + red[kTM + c.tid];
+    }
+  }
+  __syncthreads();  // the stages, scales and sums are reused by the next tile
 }
 
 // Work distribution of a stage whose items a whole workgroup processes.
@@ -320,11 +447,47 @@ __device__ __forceinline__ void wg_items(PCx& c, int items, F&& work) {
   }
 }
 
+// Split-K factor of a stage: the largest S <= 4 (a power of two) whose
+// tiles x S items still fit the grid, with K a multiple of 32 S, so that a
+// stage of few tiles (short prompts) still keeps every CU busy.
+__device__ __forceinline__ int split_k(int tiles, int K, int grid) {
+  int S = 1;
+  while (S < 4 && tiles * S * 2 <= grid && K % (kTK * S * 2) == 0) S *= 2;
+  return S;
+}
+
+// Order of a stage's items, for the caches: item t of the static deal runs on
+// workgroup t % grid, and consecutive workgroups sit on different XCDs
+// (round-robin dispatch), so t is first mapped to a position in which the
+// grid / 8 workgroups of one XCD hold consecutive positions; positions then
+// run down bands of kGroupM row tiles, so the 32 tiles one XCD works on at a
+// time are 4 row tiles x 8 weight tiles and share their A rows and weight rows
+// in that XCD's L2 (instead of every workgroup streaming the whole activation
+// matrix past its own weight tile).  The split index is outermost.
+constexpr int kGroupM = 4;
+
+// A bijection of [0, items): full rounds of `grid` items are permuted within
+// themselves, the last partial round keeps its order.
+__device__ __forceinline__ int item_position(int t, int items, int grid, bool xcd_blocks) {
+  const int r = t / grid, w = t - r * grid;
+  if (!xcd_blocks || (r + 1) * grid > items) return t;
+  return r * grid + (w & 7) * (grid >> 3) + (w >> 3);
+}
+
 __device__ __forceinline__ void gemm_stage(PCx& c, const Gemm& g) {
   const int n_tm = (c.pp->P + kTM - 1) / kTM;
   const int n_tn = g.ep == EPI_RESID ? (g.n_out + kTN - 1) / kTN : (g.n_out + 63) / 64;
-  // consecutive items are the row tiles of one weight tile: workgroups working at the same time share its weight rows in L2
-  wg_items(c, n_tm * n_tn, [&](int t) { gemm_tile(c, g, t % n_tm, t / n_tm); });
+  const int tiles = n_tm * n_tn, S = split_k(tiles, g.lda, c.grid), items = tiles * S;
+  const bool xcd_blocks = !c.pp->dynamic && (c.grid & 7) == 0;
+  wg_items(c, items, [&](int t) {
+    const int pos = item_position(t, items, c.grid, xcd_blocks);
+    const int split = pos / tiles, tile = pos - split * tiles;
+    // tile -> (row tile, weight tile): bands of kGroupM row tiles, column-major inside a band
+    const int band = tile / (kGroupM * n_tn), first = band * kGroupM;
+    const int gm = min(n_tm - first, kGroupM), in = tile - band * kGroupM * n_tn;
+    const int tm = first + in % gm, tn = in / gm;
+    gemm_tile(c, g, tm, tn, split, S, tm + tn * n_tm, tiles);
+  });
 }
 
 // ---------------------------------------------------------------- causal attention
@@ -444,7 +607,11 @@ __device__ void att_stage(PCx& c, int l) {
       const float M = fmaxf(r0[0], r1[0]);
       const float a0 = r0[0] == -INFINITY ? 0.f : exp2f(r0[0] - M);
       const float a1 = r1[0] == -INFINITY ? 0.f : exp2f(r1[0] - M);
-      *gp(p.O + (int64_t)pos * p.nq * HD + h * HD + dd) = (a0 * r0[2 + dd] + a1 * r1[2 + dd]) / (a0 * r0[1] + a1 * r1[1]);
+      const float ov = (a0 * r0[2 + dd] + a1 * r1[2 + dd]) / (a0 * r0[1] + a1 * r1[1]);
+      const _Float16 hi = (_Float16)ov;
+      const int64_t oi = (int64_t)pos * p.ldo + h * HD + dd;
+      *gp(p.Oh + oi) = __builtin_bit_cast(uint16_t, hi);
+      *gp(p.Ol + oi) = __builtin_bit_cast(uint16_t, (_Float16)(ov - (float)hi));
     }
     __syncthreads();
   });
@@ -580,15 +747,24 @@ __device__ __attribute__((noinline)) void att_stage_mfma(PCx& c, int l) {
     // the query's sum over all keys: this lane's keys plus those of lane l ^ 32
     const float lt = ls + __shfl_xor(ls, 32);
     if (pq < P) {
-      float* orow = p.O + (int64_t)pq * p.nq * HD + h * HD;
+      const int64_t orow = (int64_t)pq * p.ldo + h * HD;
       const float inv = 1.0f / lt;
 #pragma unroll
       for (int b = 0; b < DB; ++b)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          // dims 32 b + 8 a + 4 hh + {0..3}: registers 4 a .. 4 a + 3
-          const f4 v = {o[b][4 * a] * inv, o[b][4 * a + 1] * inv, o[b][4 * a + 2] * inv, o[b][4 * a + 3] * inv};
-          *gp((f4*)(orow + 32 * b + 8 * a + 4 * hh)) = v;
+          // dims 32 b + 8 a + 4 hh + {0..3}: registers 4 a .. 4 a + 3, as fp16 hi and lo halves
+          typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+          h4 hi, lo;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float v = o[b][4 * a + e] * inv;
+            hi[e] = (_Float16)v;
+            lo[e] = (_Float16)(v - (float)hi[e]);
+          }
+          const int64_t oi = orow + 32 * b + 8 * a + 4 * hh;
+          *gp((u2*)(p.Oh + oi)) = __builtin_bit_cast(u2, hi);
+          *gp((u2*)(p.Ol + oi)) = __builtin_bit_cast(u2, lo);
         }
     }
     it = p.dynamic ? __builtin_amdgcn_readfirstlane(nxt_raw) : nxt_raw;
@@ -607,12 +783,32 @@ __global__ __launch_bounds__(kPT, 1) void mk_prefill_kernel(const PParams* __res
   c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   c.lane = threadIdx.x & 63;
   c.epoch = 0;
-  // the residual stream starts as the embedding rows of the prompt
+  // the residual stream starts as the embedding rows of the prompt; with it, x times layer 0's
+  // first gain as fp16 hi + lo halves and x^2 summed over each 128-column block (one wavefront
+  // per (position, block), two columns per lane)
   {
-    const int64_t n = (int64_t)p.P * p.d;
-    for (int64_t i = (int64_t)c.cta * kPT + c.tid; i < n; i += (int64_t)c.grid * kPT) {
-      const int64_t pos = i / p.d, k = i - pos * p.d;
-      *gp(p.X + i) = (float)__builtin_bit_cast(_Float16, *gp(p.embed + (int64_t)*gp(p.ids + pos) * p.d + k));
+    const int nblk = (p.d + 127) / 128, items = p.P * nblk;
+    const uint16_t* g1 = p.norms;
+    for (int it = c.cta * kPW + c.wave; it < items; it += c.grid * kPW) {
+      const int pos = it / nblk, blk = it - pos * nblk;
+      const uint16_t* erow = p.embed + (int64_t)*gp(p.ids + pos) * p.d;
+      float sq = 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = blk * 128 + h * 64 + c.lane;
+        if (k < p.d) {
+          const float x = (float)__builtin_bit_cast(_Float16, *gp(erow + k));
+          const int64_t i = (int64_t)pos * p.d + k;
+          *gp(p.X + i) = x;
+          const float xg = x * (float)__builtin_bit_cast(_Float16, *gp(g1 + k));
+          const _Float16 hi = (_Float16)xg;
+          *gp(p.Xh + i) = __builtin_bit_cast(uint16_t, hi);
+          *gp(p.Xl + i) = __builtin_bit_cast(uint16_t, (_Float16)(xg - (float)hi));
+          sq = fmaf(x, x, sq);
+        }
+      }
+      sq = wave_sum(sq);
+      if (c.lane == 0) *gp(p.ssp + (int64_t)blk * p.P + pos) = sq;
     }
   }
   if (grid_barrier(c, OP_QKV, 0)) return;
@@ -626,17 +822,20 @@ __global__ __launch_bounds__(kPT, 1) void mk_prefill_kernel(const PParams* __res
     const uint16_t* wd = wu + (int64_t)p.f * p.d;
     const uint16_t* g1 = p.norms + (int64_t)l * 2 * p.d;
     const uint16_t* g2 = g1 + p.d;
-    gemm_stage(c, Gemm{EPI_QKV, l, p.X, p.d, p.d, g1, wl, (p.nq + 2 * p.nkv) * (p.hd / 2), nullptr, 0, nullptr});
+    gemm_stage(c, Gemm{EPI_QKV, l, p.Xh, p.Xl, p.d, p.d, 1, wl, (p.nq + 2 * p.nkv) * (p.hd / 2), nullptr, 0, nullptr,
+                       nullptr});
     if (grid_barrier(c, OP_QKV, l)) return;
     if (p.hd == 64) att_stage_mfma<64>(c, l);
     else if (p.hd == 128) att_stage_mfma<128>(c, l);
     else att_stage<256>(c, l);
     if (grid_barrier(c, OP_ATT, l)) return;
-    gemm_stage(c, Gemm{EPI_RESID, l, p.O, qd, qd, nullptr, wo, p.d, p.X, p.d, nullptr});
+    gemm_stage(c, Gemm{EPI_RESID, l, p.Oh, p.Ol, p.ldo, qd, 0, wo, p.d, p.X, p.d, nullptr, g2});
     if (grid_barrier(c, OP_OPROJ, l)) return;
-    gemm_stage(c, Gemm{EPI_UG, l, p.X, p.d, p.d, g2, wg, p.f, p.M, p.f, wu});
+    gemm_stage(c, Gemm{EPI_UG, l, p.Xh, p.Xl, p.d, p.d, 1, wg, p.f, nullptr, 0, wu, nullptr});
     if (grid_barrier(c, OP_UPGATE, l)) return;
-    gemm_stage(c, Gemm{EPI_RESID, l, p.M, p.f, p.f, nullptr, wd, p.d, p.X, p.d, nullptr});
+    // the next layer's first gain (none after the last layer: its x feeds no GEMM here)
+    const uint16_t* gn = l + 1 < p.L ? p.norms + (int64_t)(l + 1) * 2 * p.d : nullptr;
+    gemm_stage(c, Gemm{EPI_RESID, l, p.Mh, p.Ml, p.ldm, p.f, 0, wd, p.d, p.X, p.d, nullptr, gn});
     if (grid_barrier(c, OP_DOWN, l)) return;
   }
 }
