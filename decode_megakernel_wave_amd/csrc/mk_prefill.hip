@@ -771,6 +771,175 @@ __device__ __attribute__((noinline)) void att_stage_mfma(PCx& c, int l) {
   }
 }
 
+// ---------------------------------------------------------------- causal attention, workgroup-cooperative
+// Work item of a workgroup: kv head g and a super-block of 32 QPW consecutive
+// queries, QPW = 8 / G for G query heads per kv head; wavefront w takes query
+// head g G + w / QPW and the 32 queries (w % QPW) of the super-block.  All 8
+// wavefronts walk the same key blocks of 32, which the workgroup stages once:
+// the K and V blocks by global -> LDS DMA kAttNst - 1 blocks ahead (each row's
+// 16-byte chunks XOR-swizzled by the row, so that 8 consecutive key rows read
+// at one dim hit distinct banks), V transposed to V^T once per block by all
+// threads.  Per block, every wavefront whose queries reach it computes
+// S^T = K Q^T and O^T += V^T P^T as the per-wavefront version does (lane l
+// owns query l % 32; online softmax in the exp2 domain).
+constexpr int kAttNst = 3;
+
+template <int HD>
+__device__ __attribute__((noinline)) void att_stage_wg(PCx& c, int l) {
+  constexpr int KS = HD / 16;              // MFMA K-steps over the head dims
+  constexpr int DB = HD / 32;              // 32-dim blocks of O^T
+  constexpr int CPR = HD / 8;              // 16-byte chunks per K / V row
+  constexpr int BLK = 32 * HD * 2;         // bytes of a K or V block of 32 keys
+  constexpr int TPB = 2 * BLK / 1024;      // 1 KB transfers per block (K and V)
+  constexpr int DPW = TPB / kPW;           // transfers per wavefront per block
+  constexpr int RPT = 1024 / (HD * 2);     // key rows per transfer
+  static_assert(DPW * kPW == TPB && DPW >= 1 && DPW <= 2, "K and V blocks split evenly over the wavefronts");
+  static_assert(kAttNst * 2 * BLK + 2 * HD * kVtStride * 2 <= kClaimOff, "attention staging overlaps the claim slot");
+  const PParams& p = *c.pp;
+  const int G = p.nq / p.nkv, QPW = kPW / G, SB = 32 * QPW;
+  const int P = p.P, nsb = (P + SB - 1) / SB, items = p.nkv * nsb;
+  const int i32 = c.lane & 31, hh = c.lane >> 5;
+  const float qscale = kLog2e / __builtin_sqrtf((float)HD);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)pf_smem;
+  _Float16* vt_base = (_Float16*)(pf_smem + kAttNst * 2 * BLK);  // [2][HD][kVtStride]
+  wg_items(c, items, [&](int it) {
+    // the longest items (latest query super-blocks) first
+    const int sbi = nsb - 1 - it / p.nkv, g = it - (it / p.nkv) * p.nkv;
+    const int h = g * G + c.wave / QPW;
+    const int q0 = sbi * SB + (c.wave % QPW) * 32, pq = q0 + i32;
+    const bool active = q0 < P;
+    const int lim = min(pq, P - 1);                    // last key this lane's query attends
+    const int kmax_w = min(q0 + 31, P - 1);            // last key of this wavefront's queries
+    const int kmax = min(sbi * SB + SB - 1, P - 1);    // last key of the workgroup's queries
+    const int nblk = kmax / 32 + 1;
+    // Q^T operands: dims 16 s + 8 hh + e of query pq, as hi and lo halves
+    h8 qh[KS], ql[KS];
+    {
+      const float* qrow = p.Q + (int64_t)min(pq, P - 1) * p.nq * HD + h * HD + 8 * hh;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const f4 a = *gp((const f4*)(qrow + 16 * s)), b = *gp((const f4*)(qrow + 16 * s + 4));
+        const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = v[e] * qscale;
+          qh[s][e] = (_Float16)x;
+          ql[s][e] = (_Float16)(x - (float)qh[s][e]);
+        }
+      }
+    }
+    // DMA lanes: transfer j of a block (K: j < TPB / 2, V: the rest) covers key rows RPT (j % (TPB / 2)) ..;
+    // lane i -> row rr = that + i / CPR, LDS chunk i % CPR, which holds the row's chunk (i % CPR) ^ (rr % CPR)
+    const int64_t head_row = ((int64_t)l * p.nkv + g) * p.max_seq;
+    auto issue = [&](int b) {
+      const uint32_t st = lds0 + (uint32_t)((b % kAttNst) * 2 * BLK);
+#pragma unroll
+      for (int d = 0; d < DPW; ++d) {
+        const int j = c.wave * DPW + d, isv = j >= TPB / 2, jj = isv ? j - TPB / 2 : j;
+        const int rr = jj * RPT + c.lane / CPR, cc = c.lane % CPR, gq = cc ^ (rr % CPR);
+        const int key = min(b * 32 + rr, kmax);  // rows past the last key repeat it: finite, and masked
+        const uint32_t voff = (uint32_t)((head_row + key) * HD * 2) + (uint32_t)gq * 16u;
+        dma16(st + isv * BLK + jj * 1024, isv ? (const void*)p.vc : (const void*)p.kc, voff);
+      }
+    };
+    auto wait_block = [&](int later) {  // later blocks of DMAs that may stay in flight (0 or 1)
+      const int n = later * DPW;
+      if (n >= 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+      else if (n == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+    f32x16 o[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) o[b] = f32x16{};
+    float m = -INFINITY, ls = 0.f;
+    for (int b = 0; b < kAttNst - 1 && b < nblk; ++b) issue(b);
+    for (int b = 0; b < nblk; ++b) {
+      wait_block(min(b + kAttNst - 2, nblk - 1) - b);
+      __syncthreads();  // block b landed (every wavefront's DMAs); block b - 1's stage and V^T b - 2 are free
+      if (b + kAttNst - 1 < nblk) issue(b + kAttNst - 1);
+      const uint8_t* kst = pf_smem + (b % kAttNst) * 2 * BLK;
+      _Float16* vt = vt_base + (b & 1) * HD * kVtStride;
+      // V block -> V^T: thread t takes key t / CPR, dims 8 (t % CPR) .. + 8
+      if (c.tid < 32 * CPR) {
+        const int rr = c.tid / CPR, gq = c.tid % CPR;
+        const h8 vh = *(const h8*)(kst + BLK + rr * HD * 2 + ((gq ^ (rr % CPR)) << 4));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vt[(gq * 8 + e) * kVtStride + rr] = vh[e];
+      }
+      __syncthreads();
+      const int kb0 = b * 32;
+      if (!active || kb0 > kmax_w) continue;  // no query of this wavefront reaches the block
+      // S^T block: lane l holds query pq and keys kb0 + 8 (v / 4) + 4 hh + v % 4
+      f32x16 st = {};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int gq = 2 * s + hh;
+        const h8 ka = *(const h8*)(kst + i32 * HD * 2 + ((gq ^ (i32 % CPR)) << 4));
+        st = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qh[s], st, 0, 0, 0);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, ql[s], st, 0, 0, 0);
+      }
+      float mb = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int kk = kb0 + (v >> 2) * 8 + hh * 4 + (v & 3);
+        st[v] = kk <= lim ? st[v] : -INFINITY;
+        mb = fmaxf(mb, st[v]);
+      }
+      mb = fmaxf(mb, __shfl_xor(mb, 32));
+      const float mn = fmaxf(m, mb);
+      const float al = mn == -INFINITY ? 1.f : exp2f(m - mn);
+      ls *= al;
+#pragma unroll
+      for (int d = 0; d < DB; ++d) o[d] *= al;
+      m = mn;
+      h8 ph[2], pl[2];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float w = st[v] == -INFINITY ? 0.f : exp2f(st[v] - mn);
+        ls += w;
+        const _Float16 hi = (_Float16)w;
+        ph[v >> 3][v & 7] = hi;
+        pl[v >> 3][v & 7] = (_Float16)(w - (float)hi);
+      }
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+        const _Float16* row = vt + (d * 32 + i32) * kVtStride;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+          const h4 x0 = *(const h4*)(row + 16 * t + 4 * hh);
+          const h4 x1 = *(const h4*)(row + 16 * t + 8 + 4 * hh);
+          const h8 va = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, ph[t], o[d], 0, 0, 0);
+          o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pl[t], o[d], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();  // the next item's DMAs reuse the stages
+    const float lt = ls + __shfl_xor(ls, 32);
+    if (active && pq < P) {
+      const int64_t orow = (int64_t)pq * p.ldo + h * HD;
+      const float inv = 1.0f / lt;
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+          h4 hi, lo;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float v = o[d][4 * a + e] * inv;
+            hi[e] = (_Float16)v;
+            lo[e] = (_Float16)(v - (float)hi[e]);
+          }
+          const int64_t oi = orow + 32 * d + 8 * a + 4 * hh;
+          *gp((u2*)(p.Oh + oi)) = __builtin_bit_cast(u2, hi);
+          *gp((u2*)(p.Ol + oi)) = __builtin_bit_cast(u2, lo);
+        }
+    }
+  });
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(kPT, 1) void mk_prefill_kernel(const PParams* __restrict__ ppp) {
@@ -825,9 +994,17 @@ __global__ __launch_bounds__(kPT, 1) void mk_prefill_kernel(const PParams* __res
     gemm_stage(c, Gemm{EPI_QKV, l, p.Xh, p.Xl, p.d, p.d, 1, wl, (p.nq + 2 * p.nkv) * (p.hd / 2), nullptr, 0, nullptr,
                        nullptr});
     if (grid_barrier(c, OP_QKV, l)) return;
-    if (p.hd == 64) att_stage_mfma<64>(c, l);
-    else if (p.hd == 128) att_stage_mfma<128>(c, l);
-    else att_stage<256>(c, l);
+    const int G = p.nq / p.nkv;
+    const bool wg_att = G == 1 || G == 2 || G == 4 || G == 8;  // query heads of a kv head split the 8 wavefronts
+    if (p.hd == 64) {
+      if (wg_att) att_stage_wg<64>(c, l);
+      else att_stage_mfma<64>(c, l);
+    } else if (p.hd == 128) {
+      if (wg_att) att_stage_wg<128>(c, l);
+      else att_stage_mfma<128>(c, l);
+    } else {
+      att_stage<256>(c, l);
+    }
     if (grid_barrier(c, OP_ATT, l)) return;
     gemm_stage(c, Gemm{EPI_RESID, l, p.Oh, p.Ol, p.ldo, qd, 0, wo, p.d, p.X, p.d, nullptr, g2});
     if (grid_barrier(c, OP_OPROJ, l)) return;
