@@ -372,7 +372,7 @@ struct mk_ctx {
   uint32_t* d_pqueue = nullptr;     // [1 + 5 L] work-queue counters
   float* d_ppart = nullptr;         // [grid][kPartFloats] split-K partial tiles
   float* d_pXhl = nullptr;          // [2][P][d] fp16 hi / lo halves of x times the next gain
-  float* d_pssp = nullptr;          // [ceil(d / 128)][P] partial sums of squares of x
+  float* d_pssp = nullptr;          // [ceil(d / 64)][P] partial sums of squares of x
   int pf_ldo = 0, pf_ldm = 0;       // row strides (halves) of the attention-output and MLP planes
   uint32_t* d_ptile = nullptr;      // [grid] split-K arrival counters
   PParams* d_pp = nullptr;
@@ -471,7 +471,7 @@ int ctx_alloc_prefill(mk_ctx* c) {
   CHK(g.alloc(&c->d_pO, (size_t)P * c->pf_ldo * 4));   // hi and lo planes
   CHK(g.alloc(&c->d_pM, (size_t)P * c->pf_ldm * 4));
   CHK(g.alloc(&c->d_pXhl, (size_t)P * k.d_model * 4));
-  CHK(g.alloc(&c->d_pssp, (size_t)((k.d_model + 127) / 128) * P * 4));
+  CHK(g.alloc(&c->d_pssp, (size_t)((k.d_model + 63) / 64) * P * 4));
   // the pad columns of the A planes stay zero (no producer writes them)
   HIPCHK(g, mk_launch_fill32((uint32_t*)c->d_pO, P * c->pf_ldo, 0u, g.stream));
   HIPCHK(g, mk_launch_fill32((uint32_t*)c->d_pM, P * c->pf_ldm, 0u, g.stream));

@@ -160,7 +160,7 @@ struct PParams {
   uint16_t* Ml;
   uint16_t* Xh;             // [P][d] x times the gain of the next RMSNorm
   uint16_t* Xl;
-  float* ssp;               // [ceil(d / 128)][P] sums of x^2 over 128-column blocks (for 1 / rms)
+  float* ssp;               // [ceil(d / 64)][P] sums of x^2 over 64-column blocks (for 1 / rms)
   int32_t ldo, ldm;
   uint32_t* barrier;        // grid barrier counter (zero at launch)
   uint32_t* abort_flag;
@@ -174,7 +174,7 @@ struct PParams {
   float* part;              // split-K partial tiles: [grid][kPartFloats]
   uint32_t* tile_cnt;       // [grid] split-K arrivals per output tile (zero at launch and between stages)
 };
-// One split-K partial: a 128 x 128 tile of fp32 accumulators plus its 128 row sums of squares.
-constexpr int kPartFloats = 128 * 128 + 128;
+// One split-K partial: a tile of up to 128 x 256 fp32 accumulators.
+constexpr int kPartFloats = 128 * 256;
 
 }  // namespace mk

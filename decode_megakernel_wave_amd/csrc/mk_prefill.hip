@@ -38,24 +38,25 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kPT = 512;               // threads per workgroup
 constexpr int kPW = kPT / 64;          // wavefronts per workgroup
 constexpr int kTM = 128;               // GEMM tile: rows (positions)
-constexpr int kTN = 128;               // GEMM tile: weight rows (64 units of two rows, or 128 columns)
+constexpr int kTNmax = 256;            // GEMM tile: weight rows, 128 or 256 (64 or 128 units of two rows)
 constexpr int kTK = 32;                // K per pipeline step (two MFMA steps of 16)
-// LDS of a GEMM tile: kNst stages of operands as the DMA leaves them (A hi,
-// A lo and B, each [128 rows][32 halves] with the rows' 16-byte chunks
-// XOR-swizzled), the row scales, the epilogue's row-sum scratch, a flag word,
-// then the work-queue slot.
-constexpr int kNst = 6;
-constexpr int kOpBytes = kTM * kTK * 2;           // one operand of one step: 8 KB
-constexpr int kStage = 3 * kOpBytes;
-constexpr int kRsOff = kNst * kStage;
-constexpr int kRedOff = kRsOff + kTM * 4;         // [2][128] row sums of squares of the two column halves
-constexpr int kFlagOff = kRedOff + 2 * kTM * 4;
+// LDS of a GEMM tile: kNst stages of operands as the DMA leaves them (A hi and
+// A lo [128 rows][32 halves], B [TN rows][32 halves], each row's 16-byte
+// chunks XOR-swizzled), the row scales, a flag word, then the work-queue slot.
+constexpr int kNstMax = 4;                        // stages of the widest tile
+constexpr int kOpA = kTM * kTK * 2;               // A hi or A lo of one step: 8 KB
+constexpr int stage_bytes(int tn) { return 2 * kOpA + tn * kTK * 2; }
+constexpr int kRsOff = kNstMax * stage_bytes(kTNmax);
+constexpr int kFlagOff = kRsOff + kTM * 4;
 constexpr int kGemmLdsBytes = kFlagOff + 16;
 // The work-queue slot a workgroup reads its claimed tile from, past every
 // stage's own LDS use.
 constexpr int kClaimOff = kGemmLdsBytes;
 static_assert(kClaimOff + 16 <= 160 * 1024, "prefill LDS exceeds a CU's 160 KB");
-static_assert(kTM == 128 && kTN == 128 && kTK == 32, "a stage is 3 x 8 DMAs of 1 KB: 3 per wavefront");
+static_assert(kTM == 128 && kTK == 32, "a stage is 8 + 8 + TN / 16 DMAs of 1 KB: 3 or 4 per wavefront");
+static_assert(kPartFloats == kTM * kTNmax, "a split-K partial slot holds one tile");
+// RMSNorm sums of squares are kept per 64-column block of x
+constexpr int kSsCols = 64;
 
 enum Epi { EPI_QKV = 0, EPI_UG = 1, EPI_RESID = 2 };
 
@@ -157,13 +158,16 @@ struct Gemm {
 };
 
 // Weight row (within g.W / g.W2) of tile row j of tile tn; null when j is past the matrix.
+// Paired outputs: a tile's rows are groups of 64, each 32 units' first members then their
+// second members.
+template <int TN>
 __device__ __forceinline__ const uint16_t* b_row(const PParams& p, const Gemm& g, int tn, int j) {
-  const int cb = j >> 6, mem = (j >> 5) & 1, uu = j & 31;
+  const int grp = j >> 6, mem = (j >> 5) & 1, uu = j & 31;
   if (g.ep == EPI_RESID) {
-    const int n = tn * kTN + j;
+    const int n = tn * TN + j;
     return n < g.n_out ? g.W + (int64_t)n * g.K : nullptr;
   }
-  const int u = tn * 64 + cb * 32 + uu;
+  const int u = tn * (TN / 2) + grp * 32 + uu;
   if (u >= g.n_out) return nullptr;
   if (g.ep == EPI_UG) return (mem ? g.W2 : g.W) + (int64_t)u * g.K;
   // QKV: unit u is pair (i, i + hd/2) of head u / (hd/2) in the stacked [q; k; v] rows
@@ -171,12 +175,6 @@ __device__ __forceinline__ const uint16_t* b_row(const PParams& p, const Gemm& g
   return g.W + (int64_t)(head * p.hd + i + mem * hh) * g.K;
 }
 
-// One split-K item of a tile: K columns [k0, k0 + kc) of tile (tm, tn).  With
-// S = 1 the item is the whole tile and applies the epilogue itself.  With S > 1
-// every split stores its accumulators and row sums of squares to its slot of
-// p.part and counts itself in at the tile's counter; the split that arrives
-// last adds the S partials in split order (so the result does not depend on
-// which workgroup arrives last) and applies the epilogue.
 // 1 KB global -> LDS transfer of one wavefront (lane i's 16 bytes at LDS
 // lds_addr + 16 i), default cache policy: the operands are re-read by other tiles.
 __device__ __forceinline__ void dma16(uint32_t lds_addr, const void* base, uint32_t voff) {
@@ -192,16 +190,14 @@ __device__ __forceinline__ void dma16(uint32_t lds_addr, const void* base, uint3
       : "s"(lds_addr), "v"(voff), "s"(base));
 }
 
-// Wait until at most 3 n of this wavefront's DMAs are in flight (n = 0 .. kNst - 2).
+// Wait until at most D n of this wavefront's DMAs are in flight (D DMAs per step, n = 0 .. 3).
+template <int D>
 __device__ __forceinline__ void dma_wait(int n) {
-  static_assert(kNst - 2 <= 4, "dma_wait covers up to 4 later steps");
-  switch (n) {
-    case 4: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
-    case 3: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
-    case 1: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-  }
+  static_assert(D == 3 || D == 4, "3 or 4 DMAs per step");
+  if (n >= 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * D) : "memory");
+  else if (n == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * D) : "memory");
+  else if (n == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // Byte offset in a stage operand of row r's 16-byte chunk q (8 halves): the
@@ -219,80 +215,98 @@ __device__ __forceinline__ int op_chunk(int r, int q) { return r * 64 + ((q ^ ((
 // The operands stream through kNst LDS stages by global -> LDS DMA, kNst - 1 K
 // steps ahead of the matrix cores: per step each wavefront moves 1 KB of A hi,
 // A lo and B (16 rows x 64 bytes each), which the MFMAs read as they landed.
+template <int TN>
 __device__ __forceinline__ void gemm_tile(PCx& c, const Gemm& g, int tm, int tn, int split, int S, int tile, int tiles) {
+  constexpr int NB = TN / 128;            // B transfers per wavefront per step
+  constexpr int NJ = TN / 64;             // accumulators per wavefront: 32 weight rows each
+  constexpr int kStage = stage_bytes(TN);
+  constexpr int kNst = kRsOff / kStage;   // stages that fit: 4 of 32 KB (TN 256), 5 of 24 KB (TN 128)
+  static_assert(kNst >= 3 && kNst - 2 <= 3, "dma_wait covers the later steps in flight");
   const PParams& p = *c.pp;
+  // the values the K loop uses, as locals: the structs sit in memory, and the loop's waits clobber it
+  const int wave = c.wave, lane = c.lane;
+  const void* const Ah = uniform_ptr(g.Ah);
+  const void* const Al = uniform_ptr(g.Al);
+  const void* const W = uniform_ptr(g.W);
+  const int K = g.K, lda = g.lda;
   const uint32_t lds0 = (uint32_t)(uintptr_t)pf_smem;
   float* rs = (float*)(pf_smem + kRsOff);
   const int m0 = tm * kTM;
-  const int kc = g.lda / S, k0 = split * kc;
+  const int kc = lda / S, k0 = split * kc;
   const int nsteps = kc / kTK;
-  // DMA lanes: transfer of wavefront w covers rows 16 w .. 16 w + 15 of an operand; lane i -> row
-  // 16 w + i / 4, LDS chunk i % 4, which holds the row's chunk (i % 4) ^ ((row / 4) % 4)
-  const int drow = 16 * c.wave + (c.lane >> 2);
-  const int dq = (c.lane & 3) ^ ((drow >> 2) & 3);
-  const uint32_t a_off = (uint32_t)((int64_t)min(m0 + drow, p.P - 1) * g.lda * 2) + (uint32_t)dq * 16u;
-  const uint16_t* br = b_row(p, g, tn, drow);
-  const uint32_t b_off = (uint32_t)((br ? br - g.W : 0) * 2);
+  // DMA lanes: a transfer covers 16 rows of an operand; lane i -> row 16 j + i / 4, LDS chunk i % 4, which
+  // holds the row's chunk (i % 4) ^ ((row / 4) % 4).  Wavefront w moves A hi and A lo transfer w and
+  // B transfers NB w .. NB w + NB - 1.
+  const int arow = 16 * wave + (lane >> 2);
+  const int aq = (lane & 3) ^ ((arow >> 2) & 3);
+  const uint32_t a_off = (uint32_t)((int64_t)min(m0 + arow, p.P - 1) * lda * 2) + (uint32_t)aq * 16u;
+  uint32_t b_off[NB];
+  int bq[NB];
+#pragma unroll
+  for (int h = 0; h < NB; ++h) {
+    const int brow = 16 * (NB * wave + h) + (lane >> 2);
+    bq[h] = (lane & 3) ^ ((brow >> 2) & 3);
+    const uint16_t* br = b_row<TN>(p, g, tn, brow);
+    b_off[h] = (uint32_t)((br ? br - g.W : 0) * 2);
+  }
   auto issue = [&](int s) {
-    const uint32_t st = lds0 + (uint32_t)((s % kNst) * kStage) + c.wave * 1024;
+    const uint32_t st = lds0 + (uint32_t)((s % kNst) * kStage);
     const int k = k0 + s * kTK;
-    dma16(st, g.Ah, a_off + (uint32_t)k * 2u);
-    dma16(st + kOpBytes, g.Al, a_off + (uint32_t)k * 2u);
+    dma16(st + wave * 1024, Ah, a_off + (uint32_t)k * 2u);
+    dma16(st + kOpA + wave * 1024, Al, a_off + (uint32_t)k * 2u);
     // B rows have K columns: past K (the zero columns of A) the chunk is clamped to the row's last one
-    const uint32_t kb = (uint32_t)min(k + dq * 8, g.K - 8);
-    dma16(st + 2 * kOpBytes, g.W, b_off + kb * 2u);
+#pragma unroll
+    for (int h = 0; h < NB; ++h) {
+      const uint32_t kb = (uint32_t)min(k + bq[h] * 8, K - 8);
+      dma16(st + 2 * kOpA + (NB * wave + h) * 1024, W, b_off[h] + kb * 2u);
+    }
   };
 
-  f32x16 acc0 = {}, acc1 = {};
-  const int rb = c.wave & 3, cb = c.wave >> 2;
-  const int l32 = c.lane & 31, lh = c.lane >> 5;
-  const int ar = rb * 32 + l32, br0 = cb * 64 + l32;  // this lane's A row and B rows (b1: br0 + 32, same swizzle)
+  // wavefront (rb, cb) owns tile rows 32 rb .. + 32 and weight rows (TN / 2) cb .. + TN / 2: accumulator
+  // j the 32 weight rows (TN / 2) cb + 32 j ..
+  f32x16 acc[NJ] = {};
+  const int rb = wave & 3, cb = wave >> 2;
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int ar = rb * 32 + l32, br0 = cb * (TN / 2) + l32;
   auto mfma_step = [&](int s) {
     const uint8_t* st = pf_smem + (s % kNst) * kStage;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int q = sub * 2 + lh;
       const h8 ahi = *(const h8*)(st + op_chunk(ar, q));
-      const h8 alo = *(const h8*)(st + kOpBytes + op_chunk(ar, q));
-      const h8 b0 = *(const h8*)(st + 2 * kOpBytes + op_chunk(br0, q));
-      const h8 b1 = *(const h8*)(st + 2 * kOpBytes + op_chunk(br0 + 32, q));
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, b0, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, b1, acc1, 0, 0, 0);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, b0, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, b1, acc1, 0, 0, 0);
+      const h8 alo = *(const h8*)(st + kOpA + op_chunk(ar, q));
+      h8 bf[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) bf[j] = *(const h8*)(st + 2 * kOpA + op_chunk(br0 + 32 * j, q));
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, bf[j], acc[j], 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, bf[j], acc[j], 0, 0, 0);
     }
   };
   // prologue: steps 0 .. kNst - 2 in flight
   for (int s = 0; s < kNst - 1 && s < nsteps; ++s) issue(s);
   // step s: wait for step s's DMAs (the later ones may stay in flight), then issue step s + kNst - 1
   // into the stage step s - 1 used, and multiply step s
-#ifdef MK_PF_STEPMARKS
-  const bool mk_rec = g.ep == EPI_UG && g.layer == 0 && c.cta == 0 && c.tid == 0 && tm == 0 && p.marks;
-#define PF_MARK(i) \
-  if (mk_rec && s < 20) *gp(p.marks + s * 6 + (i)) = __builtin_amdgcn_s_memrealtime();
-#else
-#define PF_MARK(i)
-#endif
   for (int s = 0; s < nsteps; ++s) {
-    PF_MARK(0)
-    dma_wait(min(s + kNst - 2, nsteps - 1) - s);
-    PF_MARK(1)
+    dma_wait<2 + NB>(min(s + kNst - 2, nsteps - 1) - s);
     __syncthreads();
-    PF_MARK(2)
     if (s + kNst - 1 < nsteps) issue(s + kNst - 1);
-    PF_MARK(3)
     mfma_step(s);
-    PF_MARK(4)
-    PF_MARK(5)
   }
   __syncthreads();  // every wavefront's MFMAs are done with the stages
+  // the accumulators into LDS as the fp32 tile T[128][TN] (over the free stages), so that the split-K
+  // exchange and the epilogue run as short loops over (row, column) with coalesced global accesses
+  float* T = (float*)pf_smem;
+  static_assert(kTM * kTNmax * 4 <= kRsOff, "the accumulator tile fits the stages");
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) T[(rb * 32 + (v >> 2) * 8 + lh * 4 + (v & 3)) * TN + cb * (TN / 2) + 32 * j + l32] = acc[j][v];
+  __syncthreads();
   if (S > 1) {
     float* mine = p.part + (int64_t)(split * tiles + tile) * kPartFloats;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      *gp(mine + (c.wave * 32 + v) * 64 + c.lane) = acc0[v];
-      *gp(mine + (c.wave * 32 + 16 + v) * 64 + c.lane) = acc1[v];
-    }
+    for (int e = c.tid * 4; e < kTM * TN; e += kPT * 4) *gp((f4*)(mine + e)) = *(const f4*)(T + e);
     // release this partial, then count it in; the last split of the tile goes on
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -311,111 +325,126 @@ __device__ __forceinline__ void gemm_tile(PCx& c, const Gemm& g, int tm, int tn,
     const uint32_t is_last = __builtin_amdgcn_readfirstlane(*last);
     __syncthreads();
     if (!is_last) return;
-    acc0 = f32x16{};
-    acc1 = f32x16{};
-    for (int sp = 0; sp < S; ++sp) {
-      const float* src = p.part + (int64_t)(sp * tiles + tile) * kPartFloats;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        acc0[v] += *gp(src + (c.wave * 32 + v) * 64 + c.lane);
-        acc1[v] += *gp(src + (c.wave * 32 + 16 + v) * 64 + c.lane);
-      }
+    // the S partials in split order
+    for (int e = c.tid * 4; e < kTM * TN; e += kPT * 4) {
+      f4 t = {0.f, 0.f, 0.f, 0.f};
+      for (int sp = 0; sp < S; ++sp) t += *gp((const f4*)(p.part + (int64_t)(sp * tiles + tile) * kPartFloats + e));
+      *(f4*)(T + e) = t;
     }
+    __syncthreads();
   }
   if (g.norm) {
-    // 1 / rms of each row from its 128-column sums of squares (fixed order)
+    // 1 / rms of each row from its 64-column sums of squares (fixed order)
     if (c.tid < kTM) {
-      const int pos = min(m0 + c.tid, p.P - 1), nblk = (p.d + 127) / 128;
+      const int pos = min(m0 + c.tid, p.P - 1), nblk = (p.d + kSsCols - 1) / kSsCols;
       float t = 0.f;
       for (int j = 0; j < nblk; ++j) t += *gp(p.ssp + (int64_t)j * p.P + pos);
       rs[c.tid] = 1.0f / __builtin_sqrtf(t / (float)p.d + p.eps);
     }
     __syncthreads();
   }
-  // epilogue: accumulator register v of lane l holds tile row 32 rb + 8 (v / 4) + 4 (l / 32) + v % 4,
-  // unit / column l % 32 of the wavefront's block
+  // epilogue: wavefront w takes tile rows w, w + 8, ..., in groups of kEr rows whose global loads are
+  // issued together (the loop would otherwise wait for each row's loads behind the previous row's stores)
+  constexpr int kEr = 4;
+  static_assert((kTM / kPW) % kEr == 0, "row groups");
+  const int nblk = (p.d + kSsCols - 1) / kSsCols;
+  if (g.ep == EPI_RESID) {
+    // 64-column blocks, a column per lane: x += a, then x times the next gain as hi + lo halves and the
+    // block's sum of x^2 for the next RMSNorm
+    for (int b = 0; b < TN / kSsCols; ++b) {
+      const int n = tn * TN + b * kSsCols + c.lane;
+      const bool col = n < g.n_out;
+      const int blk = (tn * TN) / kSsCols + b;
+      const float gn = g.gnext && col ? (float)__builtin_bit_cast(_Float16, *gp(g.gnext + n)) : 0.f;
+      for (int r0 = c.wave; r0 < kTM; r0 += kPW * kEr) {
+        float x[kEr];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int r = rb * 32 + (v >> 2) * 8 + lh * 4 + (v & 3);
-    const int pos = m0 + r;
-    if (pos >= p.P) continue;
-    float a = acc0[v], b = acc1[v];
-    if (g.norm) {
-      const float sc = rs[r];
-      a *= sc;
-      b *= sc;
-    }
-    if (g.ep == EPI_RESID) {
-      // x += a; then x times the next gain as hi + lo halves, and x^2 towards the row's block sum
-      const int n = tn * kTN + cb * 64 + l32;
-      float* xo = g.out + (int64_t)pos * g.ld_out;
-      float sq = 0.f;
+        for (int e = 0; e < kEr; ++e) {
+          const int r = r0 + e * kPW, pos = m0 + r;
+          x[e] = pos < p.P && col ? *gp(g.out + (int64_t)pos * g.ld_out + n) : 0.f;
+        }
+        float sq[kEr];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int nn = n + 32 * h;
-        if (nn < g.n_out) {
-          const float x = *gp(xo + nn) + (h ? b : a);
-          *gp(xo + nn) = x;
-          if (g.gnext) {
-            const float xg = x * (float)__builtin_bit_cast(_Float16, *gp(g.gnext + nn));
-            const _Float16 hi = (_Float16)xg;
-            *gp(p.Xh + (int64_t)pos * g.ld_out + nn) = __builtin_bit_cast(uint16_t, hi);
-            *gp(p.Xl + (int64_t)pos * g.ld_out + nn) = __builtin_bit_cast(uint16_t, (_Float16)(xg - (float)hi));
-            sq = fmaf(x, x, sq);
+        for (int e = 0; e < kEr; ++e) {
+          const int r = r0 + e * kPW, pos = m0 + r;
+          const float sc = g.norm ? rs[r] : 1.0f;
+          x[e] += T[r * TN + b * kSsCols + c.lane] * sc;
+          sq[e] = x[e] * x[e];
+          if (pos < p.P && col) {
+            *gp(g.out + (int64_t)pos * g.ld_out + n) = x[e];
+            if (g.gnext) {
+              const float xg = x[e] * gn;
+              const _Float16 hi = (_Float16)xg;
+              *gp(p.Xh + (int64_t)pos * g.ld_out + n) = __builtin_bit_cast(uint16_t, hi);
+              *gp(p.Xl + (int64_t)pos * g.ld_out + n) = __builtin_bit_cast(uint16_t, (_Float16)(xg - (float)hi));
+            }
+          } else {
+            sq[e] = 0.f;
+          }
+        }
+        if (g.gnext && blk < nblk) {
+#pragma unroll
+          for (int e = 0; e < kEr; ++e) sq[e] = wave_sum(sq[e]);
+          if (c.lane == 0) {
+#pragma unroll
+            for (int e = 0; e < kEr; ++e) {
+              const int pos = m0 + r0 + e * kPW;
+              if (pos < p.P) *gp(p.ssp + (int64_t)blk * p.P + pos) = sq[e];
+            }
           }
         }
       }
-      if (g.gnext) {
-        // the tile's 128 columns of row r: 32 lanes x 2 columns here, the other wavefront of the row
-        // (cb ^ 1) holds the other 64 columns
-        sq += __shfl_xor(sq, 1);
-        sq += __shfl_xor(sq, 2);
-        sq += __shfl_xor(sq, 4);
-        sq += __shfl_xor(sq, 8);
-        sq += __shfl_xor(sq, 16);
-        if (l32 == 0) ((float*)(pf_smem + kRedOff))[cb * kTM + r] = sq;
-      }
-    } else if (g.ep == EPI_UG) {
-      const int u = tn * 64 + cb * 32 + l32;
-      if (u < g.n_out) {
-        const float m = a / (1.0f + __expf(-a)) * b;
-        const _Float16 hi = (_Float16)m;
-        *gp(p.Mh + (int64_t)pos * p.ldm + u) = __builtin_bit_cast(uint16_t, hi);
-        *gp(p.Ml + (int64_t)pos * p.ldm + u) = __builtin_bit_cast(uint16_t, (_Float16)(m - (float)hi));
-      }
-    } else {
-      const int u = tn * 64 + cb * 32 + l32;
+    }
+  } else {
+    // paired outputs: groups of 64 weight rows (32 units' first members, then their second members);
+    // lanes 0-31 take units of an even group, lanes 32-63 of the next
+    const int hh = p.hd >> 1;
+    for (int gp2 = 0; gp2 < TN / 128; ++gp2) {
+      const int grp = 2 * gp2 + (c.lane >> 5), uu = c.lane & 31;
+      const int u = tn * (TN / 2) + grp * 32 + uu;
       if (u >= g.n_out) continue;
-      const int hh = p.hd >> 1, head = u / hh, i = u - head * hh;
-      if (head < p.nq + p.nkv) {  // q or k head: rotate the pair (i, i + hd/2) by the position's angle
-        const float* cs = p.rope + ((int64_t)pos * hh + i) * 2;
-        const float co = *gp(cs), sn = *gp(cs + 1);
-        const float ra = a * co - b * sn, rb2 = a * sn + b * co;
-        a = ra;
-        b = rb2;
-      }
-      if (head < p.nq) {
-        float* qo = p.Q + (int64_t)pos * p.nq * p.hd + head * p.hd + i;
-        *gp(qo) = a;
-        *gp(qo + hh) = b;
-      } else {
-        const bool isk = head < p.nq + p.nkv;
-        const int kvh = head - p.nq - (isk ? 0 : p.nkv);
-        uint16_t* dst = (isk ? p.kc : p.vc) + (((int64_t)g.layer * p.nkv + kvh) * p.max_seq + pos) * p.hd + i;
-        *gp(dst) = __builtin_bit_cast(uint16_t, (_Float16)a);
-        *gp(dst + hh) = __builtin_bit_cast(uint16_t, (_Float16)b);
+      // QKV: unit u is the pair (i, i + hd/2) of head u / (hd/2); q and k heads rotate it by the position's angle
+      const int head = u / hh, i = u - head * hh;
+      const bool rot = g.ep == EPI_QKV && head < p.nq + p.nkv;
+      for (int r0 = c.wave; r0 < kTM; r0 += kPW * kEr) {
+        float co[kEr], sn[kEr];
+#pragma unroll
+        for (int e = 0; e < kEr; ++e) {
+          const int pos = min(m0 + r0 + e * kPW, p.P - 1);
+          const float* cs = p.rope + ((int64_t)pos * hh + i) * 2;
+          co[e] = rot ? *gp(cs) : 1.f;
+          sn[e] = rot ? *gp(cs + 1) : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < kEr; ++e) {
+          const int r = r0 + e * kPW, pos = m0 + r;
+          if (pos >= p.P) continue;
+          const float sc = g.norm ? rs[r] : 1.0f;
+          const float a = T[r * TN + grp * 64 + uu] * sc, b = T[r * TN + grp * 64 + 32 + uu] * sc;
+          if (g.ep == EPI_UG) {
+            const float m = a / (1.0f + __expf(-a)) * b;
+            const _Float16 hi = (_Float16)m;
+            *gp(p.Mh + (int64_t)pos * p.ldm + u) = __builtin_bit_cast(uint16_t, hi);
+            *gp(p.Ml + (int64_t)pos * p.ldm + u) = __builtin_bit_cast(uint16_t, (_Float16)(m - (float)hi));
+            continue;
+          }
+          const float ra = a * co[e] - b * sn[e], rb2 = a * sn[e] + b * co[e];
+          if (head < p.nq) {
+            float* qo = p.Q + (int64_t)pos * p.nq * p.hd + head * p.hd + i;
+            *gp(qo) = ra;
+            *gp(qo + hh) = rb2;
+          } else {
+            const bool isk = head < p.nq + p.nkv;
+            const int kvh = head - p.nq - (isk ? 0 : p.nkv);
+            uint16_t* dst = (isk ? p.kc : p.vc) + (((int64_t)g.layer * p.nkv + kvh) * p.max_seq + pos) * p.hd + i;
+            *gp(dst) = __builtin_bit_cast(uint16_t, (_Float16)ra);
+            *gp(dst + hh) = __builtin_bit_cast(uint16_t, (_Float16)rb2);
+          }
+        }
       }
     }
   }
-  if (g.ep == EPI_RESID && g.gnext) {
-    __syncthreads();
-    // note: rows past P kept their partial sums out of the loop above (it skips them)
-    if (c.tid < kTM && m0 + c.tid < p.P) {
-      const float* red = (const float*)(pf_smem + kRedOff);
-      *gp(p.ssp + (int64_t)tn * p.P + m0 + c.tid) = red[c.tid] + red[kTM + c.tid];
-    }
-  }
-  __syncthreads();  // the stages, scales and sums are reused by the next tile
+  __syncthreads();  // the stages and scales are reused by the next tile
 }
 
 // Work distribution of a stage whose items a whole workgroup processes.
@@ -426,24 +455,29 @@ __device__ __forceinline__ void gemm_tile(PCx& c, const Gemm& g, int tm, int tn,
 template <typename F>
 __device__ __forceinline__ void wg_items(PCx& c, int items, F&& work) {
   const PParams& p = *c.pp;
-  if (!p.dynamic) {
-    for (int t = c.cta; t < items; t += c.grid) work(t);
-    return;
-  }
+  // one call site of `work` for both distributions (the work is inlined once)
+  const bool dyn = p.dynamic != 0;
   int* slot = (int*)(pf_smem + kClaimOff);
   uint32_t* ctr = p.queue + c.epoch;
-  if (c.tid == 0) *slot = (int)__hip_atomic_fetch_add(gp(ctr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  __syncthreads();
-  int t = *slot;
-  __syncthreads();
-  while (t < items) {
-    uint32_t nxt = 0;
-    if (c.tid == 0) nxt = __hip_atomic_fetch_add(gp(ctr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    work(t);
-    if (c.tid == 0) *slot = (int)nxt;
+  int t = c.cta;
+  if (dyn) {
+    if (c.tid == 0) *slot = (int)__hip_atomic_fetch_add(gp(ctr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     __syncthreads();
     t = *slot;
     __syncthreads();
+  }
+  while (t < items) {
+    uint32_t nxt = 0;
+    if (dyn && c.tid == 0) nxt = __hip_atomic_fetch_add(gp(ctr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    work(t);
+    if (dyn) {
+      if (c.tid == 0) *slot = (int)nxt;
+      __syncthreads();
+      t = *slot;
+      __syncthreads();
+    } else {
+      t += c.grid;
+    }
   }
 }
 
@@ -474,9 +508,10 @@ __device__ __forceinline__ int item_position(int t, int items, int grid, bool xc
   return r * grid + (w & 7) * (grid >> 3) + (w >> 3);
 }
 
-__device__ __forceinline__ void gemm_stage(PCx& c, const Gemm& g) {
+template <int TN>
+__device__ __forceinline__ void gemm_stage_tn(PCx& c, const Gemm& g) {
   const int n_tm = (c.pp->P + kTM - 1) / kTM;
-  const int n_tn = g.ep == EPI_RESID ? (g.n_out + kTN - 1) / kTN : (g.n_out + 63) / 64;
+  const int n_tn = g.ep == EPI_RESID ? (g.n_out + TN - 1) / TN : (g.n_out + TN / 2 - 1) / (TN / 2);
   const int tiles = n_tm * n_tn, S = split_k(tiles, g.lda, c.grid), items = tiles * S;
   const bool xcd_blocks = !c.pp->dynamic && (c.grid & 7) == 0;
   wg_items(c, items, [&](int t) {
@@ -486,8 +521,16 @@ __device__ __forceinline__ void gemm_stage(PCx& c, const Gemm& g) {
     const int band = tile / (kGroupM * n_tn), first = band * kGroupM;
     const int gm = min(n_tm - first, kGroupM), in = tile - band * kGroupM * n_tn;
     const int tm = first + in % gm, tn = in / gm;
-    gemm_tile(c, g, tm, tn, split, S, tm + tn * n_tm, tiles);
+    gemm_tile<TN>(c, g, tm, tn, split, S, tm + tn * n_tm, tiles);
   });
+}
+
+// Tiles of 256 weight rows when the stage has rows enough (16 row tiles) to keep every workgroup
+// busy without deep split-K: half the A traffic per output of 128-row tiles; shorter prompts keep
+// 128-row tiles, whose split-K partials are half the size.
+__device__ __forceinline__ void gemm_stage(PCx& c, const Gemm& g) {
+  if ((c.pp->P + kTM - 1) / kTM >= 16) gemm_stage_tn<256>(c, g);
+  else gemm_stage_tn<128>(c, g);
 }
 
 // ---------------------------------------------------------------- causal attention
@@ -497,7 +540,7 @@ __device__ __forceinline__ void gemm_stage(PCx& c, const Gemm& g) {
 // keeps an online softmax in the exp2 domain (q pre-scaled by log2(e)/sqrt(hd))
 // and the two key halves are merged through LDS.  Query p attends keys 0..p.
 template <int HD>
-__device__ void att_stage(PCx& c, int l) {
+__device__ __attribute__((noinline)) void att_stage(PCx& c, int l) {
   constexpr int DL = HD / 16;          // dims per lane
   constexpr int EV = DL < 8 ? DL : 8;  // fp16 values per load
   constexpr int NV = DL / EV;          // loads per key row slice (16 bytes, or 8 for head_dim 64)
@@ -953,18 +996,17 @@ __global__ __launch_bounds__(kPT, 1) void mk_prefill_kernel(const PParams* __res
   c.lane = threadIdx.x & 63;
   c.epoch = 0;
   // the residual stream starts as the embedding rows of the prompt; with it, x times layer 0's
-  // first gain as fp16 hi + lo halves and x^2 summed over each 128-column block (one wavefront
-  // per (position, block), two columns per lane)
+  // first gain as fp16 hi + lo halves and x^2 summed over each 64-column block (one wavefront
+  // per (position, block), a column per lane)
   {
-    const int nblk = (p.d + 127) / 128, items = p.P * nblk;
+    const int nblk = (p.d + kSsCols - 1) / kSsCols, items = p.P * nblk;
     const uint16_t* g1 = p.norms;
     for (int it = c.cta * kPW + c.wave; it < items; it += c.grid * kPW) {
       const int pos = it / nblk, blk = it - pos * nblk;
       const uint16_t* erow = p.embed + (int64_t)*gp(p.ids + pos) * p.d;
       float sq = 0.f;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int k = blk * 128 + h * 64 + c.lane;
+      {
+        const int k = blk * kSsCols + c.lane;
         if (k < p.d) {
           const float x = (float)__builtin_bit_cast(_Float16, *gp(erow + k));
           const int64_t i = (int64_t)pos * p.d + k;
@@ -983,37 +1025,43 @@ __global__ __launch_bounds__(kPT, 1) void mk_prefill_kernel(const PParams* __res
   if (grid_barrier(c, OP_QKV, 0)) return;
   const int qd = p.nq * p.hd, kvd = p.nkv * p.hd;
   const int64_t per_layer = (int64_t)(qd + 2 * kvd) * p.d + (int64_t)p.d * qd + 3LL * p.f * p.d;
-  for (int l = 0; l < p.L; ++l) {
+  const int G = p.nq / p.nkv;
+  const bool wg_att = G == 1 || G == 2 || G == 4 || G == 8;  // query heads of a kv head split the 8 wavefronts
+  // 5 stages per layer; every GEMM runs from one call site (its code is in the kernel once)
+  for (int st = 0; st < 5 * p.L; ++st) {
+    const int l = st / 5, kind = st - 5 * l;
     const uint16_t* wl = p.canon + l * per_layer;
     const uint16_t* wo = wl + (int64_t)(qd + 2 * kvd) * p.d;
     const uint16_t* wg = wo + (int64_t)p.d * qd;
     const uint16_t* wu = wg + (int64_t)p.f * p.d;
     const uint16_t* wd = wu + (int64_t)p.f * p.d;
-    const uint16_t* g1 = p.norms + (int64_t)l * 2 * p.d;
-    const uint16_t* g2 = g1 + p.d;
-    gemm_stage(c, Gemm{EPI_QKV, l, p.Xh, p.Xl, p.d, p.d, 1, wl, (p.nq + 2 * p.nkv) * (p.hd / 2), nullptr, 0, nullptr,
-                       nullptr});
-    if (grid_barrier(c, OP_QKV, l)) return;
-    const int G = p.nq / p.nkv;
-    const bool wg_att = G == 1 || G == 2 || G == 4 || G == 8;  // query heads of a kv head split the 8 wavefronts
-    if (p.hd == 64) {
-      if (wg_att) att_stage_wg<64>(c, l);
-      else att_stage_mfma<64>(c, l);
-    } else if (p.hd == 128) {
-      if (wg_att) att_stage_wg<128>(c, l);
-      else att_stage_mfma<128>(c, l);
-    } else {
-      att_stage<256>(c, l);
-    }
-    if (grid_barrier(c, OP_ATT, l)) return;
-    gemm_stage(c, Gemm{EPI_RESID, l, p.Oh, p.Ol, p.ldo, qd, 0, wo, p.d, p.X, p.d, nullptr, g2});
-    if (grid_barrier(c, OP_OPROJ, l)) return;
-    gemm_stage(c, Gemm{EPI_UG, l, p.Xh, p.Xl, p.d, p.d, 1, wg, p.f, nullptr, 0, wu, nullptr});
-    if (grid_barrier(c, OP_UPGATE, l)) return;
+    const uint16_t* g2 = p.norms + ((int64_t)l * 2 + 1) * p.d;
     // the next layer's first gain (none after the last layer: its x feeds no GEMM here)
     const uint16_t* gn = l + 1 < p.L ? p.norms + (int64_t)(l + 1) * 2 * p.d : nullptr;
-    gemm_stage(c, Gemm{EPI_RESID, l, p.Mh, p.Ml, p.ldm, p.f, 0, wd, p.d, p.X, p.d, nullptr, gn});
-    if (grid_barrier(c, OP_DOWN, l)) return;
+    if (kind == 1) {
+      if (p.hd == 64) {
+        if (wg_att) att_stage_wg<64>(c, l);
+        else att_stage_mfma<64>(c, l);
+      } else if (p.hd == 128) {
+        if (wg_att) att_stage_wg<128>(c, l);
+        else att_stage_mfma<128>(c, l);
+      } else {
+        att_stage<256>(c, l);
+      }
+    } else {
+      Gemm g;
+      if (kind == 0)
+        g = Gemm{EPI_QKV, l, p.Xh, p.Xl, p.d, p.d, 1, wl, (p.nq + 2 * p.nkv) * (p.hd / 2), nullptr, 0, nullptr, nullptr};
+      else if (kind == 2)
+        g = Gemm{EPI_RESID, l, p.Oh, p.Ol, p.ldo, qd, 0, wo, p.d, p.X, p.d, nullptr, g2};
+      else if (kind == 3)
+        g = Gemm{EPI_UG, l, p.Xh, p.Xl, p.d, p.d, 1, wg, p.f, nullptr, 0, wu, nullptr};
+      else
+        g = Gemm{EPI_RESID, l, p.Mh, p.Ml, p.ldm, p.f, 0, wd, p.d, p.X, p.d, nullptr, gn};
+      gemm_stage(c, g);
+    }
+    const int op = kind == 0 ? OP_QKV : kind == 1 ? OP_ATT : kind == 2 ? OP_OPROJ : kind == 3 ? OP_UPGATE : OP_DOWN;
+    if (grid_barrier(c, op, l)) return;
   }
 }
 

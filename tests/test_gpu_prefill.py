@@ -13,8 +13,9 @@ attention tiles) and the last prompt token as one decode step.  Checked here:
 - t0 and the teacher-forced decode after it against the oracle, with the
   prefill kernel's position count reported by mk_stats;
 - prompts that leave ragged GEMM and attention tiles (1, 2, 33, 129, 200
-  positions), and the token-by-token prefill (MK_PREFILL_STEPS) giving the
-  same first token and the same decode within the acceptance rule;
+  positions; 2100, long enough for the 256-row weight tiles), and the
+  token-by-token prefill (MK_PREFILL_STEPS) giving the same first token and the
+  same decode within the acceptance rule;
 - the dynamic work queue (option work_queue) giving bitwise the results of
   the static deal.
 """
@@ -84,8 +85,9 @@ def _run(model, P, n, seed=1, w=None, env_steps=False, monkeypatch=None, **opts)
     return st, err, (mism, total), t0, logits, m0
 
 
-@pytest.mark.parametrize("P", [1, 2, 33, 129, 200])
+@pytest.mark.parametrize("P", [1, 2, 33, 129, 200, 2100])
 def test_tiny_prefill_ragged_prompts(P):
+    """P = 2100 has 17 row tiles: the stages take the 256-row weight tiles of long prompts."""
     st, err, (mism, total), _, _, _ = _run(inputs.TINY, P, 4)
     assert st["prefill_positions"] == P - 1
     assert (st["prefill_grid"] > 0) == (P >= 2)
