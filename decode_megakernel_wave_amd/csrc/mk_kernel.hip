@@ -88,6 +88,7 @@ namespace {
 #endif
 constexpr bool kSliceStaging = MK_SLICE_STAGING != 0;
 
+
 // head_dim and query heads per kv head: compile-time constants in the specialised build
 __device__ __forceinline__ int head_dim(const KParams& kp) { return kSpecHd ? kSpecHd : kp.hd; }
 __device__ __forceinline__ int q_group(const KParams& kp) { return kSpecGroup ? kSpecGroup : kp.nq / kp.nkv; }
@@ -507,7 +508,12 @@ __device__ __forceinline__ void ring_read_n(Ring& ring, u4 (&w)[4], int n, bool 
 // wait behind the weight requests that CU has in flight: a handoff between two
 // CUs that stream takes about 1.8 us, between two that do not 0.6-0.8 us, with
 // the rest of the chip streaming in both cases.  Issuing the last refills after
-// the stores lets the outputs leave first.
+// the stores lets the outputs leave first.  QKV's are issued later still, in
+// the attention stage after its q polls and K/V loads (the attention reads no
+// weights, so they still land before the next GEMV): 2 % faster decode than
+// issuing them after QKV's stores, where they sat ahead of those polls.  The
+// other GEMVs' could not wait that long: issued only after the next GEMV had
+// staged its inputs, they arrived late for it (4 % slower).
 
 // GEMV body.  CPS = 4: slices of four chunks, the widest and the common case
 // (rows of 2048 or more columns); CPS = 0: any width in.cps = 1..4 with
@@ -705,7 +711,8 @@ __device__ __forceinline__ void op_qkv(Cx& c, Ring& ring, const Ins& in) {
     cta_sync(c);
     for (int t = c.tid; t < 2 * in.nu; t += kThreads) store_out(in.u0 + t % in.nu, t / in.nu, outs[t]);
   }
-  ring_settle(ring);
+  // the refills left owed go out in the attention stage, after its q polls and K/V loads (a workgroup
+  // without attention units issues them at its next GEMV)
   counter_signal(c, in.sync_out);
 }
 
@@ -1128,7 +1135,7 @@ __device__ __forceinline__ float half_at(const typename RawHalves<DPL>::T& r, in
 // Short split: this wavefront's cached K/V rows are loaded before q is
 // polled, so their latency hides behind the wait for the QKV stage.
 template <int GP, int DPL>
-__device__ __forceinline__ void att_short(Cx& c, int l, int g, int sp, int t0, int t1, int G, bool has_cur, bool first) {
+__device__ __forceinline__ void att_short(Cx& c, Ring& ring, int l, int g, int sp, int t0, int t1, int G, bool has_cur, bool first) {
   const KParams& kp = *c.kp;
   const int hd = head_dim(kp);
   typedef typename RawHalves<DPL>::T Raw;
@@ -1157,10 +1164,12 @@ __device__ __forceinline__ void att_short(Cx& c, int l, int g, int sp, int t0, i
       vv[b][k] = cur ? vcur[c.lane * DPL + k] : half_at<DPL>(vr[b], k);
     }
   }
+  // the refills QKV left owed go out behind the q polls and the K/V loads
+  ring_settle(ring);
   for (int j0 = 0; j0 < G; j0 += GP) att_pos_core<GP, DPL>(c, l, g, sp, j0, min(GP, G - j0), t0, t1, G, kv, vv);
 }
 
-__device__ __forceinline__ void op_att(Cx& c, const Ins& in) {
+__device__ __forceinline__ void op_att(Cx& c, Ring& ring, const Ins& in) {
   const KParams& kp = *c.kp;
   const int l = in.layer;
   const int G = q_group(kp), hd = head_dim(kp), S = kp.S;
@@ -1177,16 +1186,17 @@ __device__ __forceinline__ void op_att(Cx& c, const Ins& in) {
       const int dpl = hd / 64;
 #ifdef MK_SPECIALIZED
       (void)dpl;
-      att_short<kSpecGroup, 2>(c, l, g, sp, t0, t1, G, has_cur, ui == 0);
+      att_short<kSpecGroup, 2>(c, ring, l, g, sp, t0, t1, G, has_cur, ui == 0);
 #else
-      if (dpl == 1) att_short<8, 1>(c, l, g, sp, t0, t1, G, has_cur, ui == 0);
-      else if (dpl == 2) att_short<4, 2>(c, l, g, sp, t0, t1, G, has_cur, ui == 0);
-      else att_short<2, 4>(c, l, g, sp, t0, t1, G, has_cur, ui == 0);
+      if (dpl == 1) att_short<8, 1>(c, ring, l, g, sp, t0, t1, G, has_cur, ui == 0);
+      else if (dpl == 2) att_short<4, 2>(c, ring, l, g, sp, t0, t1, G, has_cur, ui == 0);
+      else att_short<2, 4>(c, ring, l, g, sp, t0, t1, G, has_cur, ui == 0);
 #endif
     } else {
       // (no prefetch of the split's K/V rows before the wait: pulling them
       // towards L2 first was measured slower at 2048 and 8192 positions)
       att_stage(c, l, g, has_cur, ui == 0);
+      ring_settle(ring);  // the refills QKV left owed go out behind the q polls
 #ifdef MK_SPECIALIZED
       att_heads<128>(c, l, g, sp, t0, t1, G);
 #else
@@ -1817,7 +1827,7 @@ __global__ __launch_bounds__(kThreads, 1) void MK_MONOKERNEL(const KParams* __re
       ts_mark(c, 0);
       switch (in.op) {
         case OP_QKV: op_qkv(c, ring, in); break;
-        case OP_ATT: op_att(c, in); break;
+        case OP_ATT: op_att(c, ring, in); break;
         case OP_OPROJ: op_oproj(c, ring, in); break;
         case OP_UPGATE: op_upgate(c, ring, in); break;
         case OP_DOWN: op_down(c, ring, in); break;
