@@ -526,10 +526,15 @@ __device__ __forceinline__ void gemm_stage_tn(PCx& c, const Gemm& g) {
 }
 
 // Tiles of 256 weight rows when the stage has rows enough (16 row tiles) to keep every workgroup
-// busy without deep split-K: half the A traffic per output of 128-row tiles; shorter prompts keep
-// 128-row tiles, whose split-K partials are half the size.
+// busy without deep split-K, or when its 256-row tiles alone fill the grid (up/gate at 512
+// tokens: 117 -> 101 us per layer): half the A traffic per output of 128-row tiles.  Other
+// stages keep 128-row tiles, whose split-K partials are half the size (QKV at 512 tokens with
+// 256-row tiles split 4 ways: 69 -> 92 us).
 __device__ __forceinline__ void gemm_stage(PCx& c, const Gemm& g) {
-  if ((c.pp->P + kTM - 1) / kTM >= 16) gemm_stage_tn<256>(c, g);
+  const int n_tm = (c.pp->P + kTM - 1) / kTM;
+  const int rows = g.ep == EPI_RESID ? g.n_out : 2 * g.n_out;  // weight rows
+  const bool wide = n_tm >= 16 || n_tm * ((rows + 255) / 256) >= c.grid;
+  if (wide) gemm_stage_tn<256>(c, g);
   else gemm_stage_tn<128>(c, g);
 }
 
