@@ -850,7 +850,15 @@ __device__ __attribute__((noinline)) void att_stage_wg(PCx& c, int l) {
   const float qscale = kLog2e / __builtin_sqrtf((float)HD);
   const uint32_t lds0 = (uint32_t)(uintptr_t)pf_smem;
   _Float16* vt_base = (_Float16*)(pf_smem + kAttNst * 2 * BLK);  // [2][HD][kVtStride]
+  // static deal in rounds of `grid` items: every other round takes its super-blocks in reverse, so a
+  // workgroup that drew one of the longest items in one round draws one of the shortest in the next
+  // (with grid a multiple of n_kv the kv head of a workgroup's items stays the same)
+  const bool snake = !p.dynamic && c.grid % p.nkv == 0;
   wg_items(c, items, [&](int it) {
+    if (snake && (it / c.grid) % 2 == 1) {
+      const int r0 = it - it % c.grid, j = it - r0, nr = min(c.grid, items - r0);
+      it = r0 + (nr / p.nkv - 1 - j / p.nkv) * p.nkv + j % p.nkv;
+    }
     // the longest items (latest query super-blocks) first
     const int sbi = nsb - 1 - it / p.nkv, g = it - (it / p.nkv) * p.nkv;
     const int h = g * G + c.wave / QPW;
