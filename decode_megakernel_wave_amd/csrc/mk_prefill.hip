@@ -545,7 +545,10 @@ __device__ __forceinline__ void gemm_stage(PCx& c, const Gemm& g) {
 // keeps an online softmax in the exp2 domain (q pre-scaled by log2(e)/sqrt(hd))
 // and the two key halves are merged through LDS.  Query p attends keys 0..p.
 template <int HD>
-__device__ __attribute__((noinline)) void att_stage(PCx& c, int l) {
+__device__ __attribute__((noinline)) void att_stage(PCx& c_ref, int l) {
+  // a local copy: read through the reference, its fields would be reloaded from memory (vector
+  // loads that wait behind the block DMAs in flight) after every asm statement that clobbers memory
+  PCx c = c_ref;
   constexpr int DL = HD / 16;          // dims per lane
   constexpr int EV = DL < 8 ? DL : 8;  // fp16 values per load
   constexpr int NV = DL / EV;          // loads per key row slice (16 bytes, or 8 for head_dim 64)
@@ -682,11 +685,20 @@ constexpr int kVtStride = 40;  // halves per V^T row in LDS (32 keys + padding)
 static_assert(kPW * 128 * kVtStride * 2 <= kClaimOff && 2 * 16 * (256 + 2) * 4 <= kClaimOff, "claim slot overlaps attention LDS");
 
 template <int HD>
-__device__ __attribute__((noinline)) void att_stage_mfma(PCx& c, int l) {
+__device__ __attribute__((noinline)) void att_stage_mfma(PCx& c_ref, int l) {
+  // a local copy: read through the reference, its fields would be reloaded from memory (vector
+  // loads that wait behind the block DMAs in flight) after every asm statement that clobbers memory
+  PCx c = c_ref;
   constexpr int KS = HD / 16;  // MFMA K-steps over the head dims
   constexpr int DB = HD / 32;  // 32-dim blocks of O^T
   const PParams& p = *c.pp;
-  const int P = p.P, nqb = (P + 31) / 32, items = p.nq * nqb;
+  // the fields the item loop uses, as locals: p is read through a pointer, and every asm statement
+  // that clobbers memory would make the compiler reload them (loads that wait behind the DMAs)
+  uint16_t* const Ohp = (uint16_t*)uniform_ptr(p.Oh);
+  uint16_t* const Olp = (uint16_t*)uniform_ptr(p.Ol);
+  const float* const Qp = (const float*)uniform_ptr(p.Q);
+  const int ldo = p.ldo, nq = p.nq, nkv = p.nkv, max_seq = p.max_seq;
+  const int P = p.P, nqb = (P + 31) / 32, items = nq * nqb;
   const int i32 = c.lane & 31, hh = c.lane >> 5;
   const float qscale = kLog2e / __builtin_sqrtf((float)HD);
   _Float16* vt = (_Float16*)pf_smem + c.wave * HD * kVtStride;  // this wavefront's V^T block [HD][kVtStride]
@@ -703,15 +715,15 @@ __device__ __attribute__((noinline)) void att_stage_mfma(PCx& c, int l) {
   while (it < items) {
     const int nxt_raw = p.dynamic ? claim() : it + nw;
     // the longest items (latest query blocks) first
-    const int qb = nqb - 1 - it / p.nq, h = it - (it / p.nq) * p.nq;
-    const int g = h * p.nkv / p.nq;
+    const int qb = nqb - 1 - it / nq, h = it - (it / nq) * nq;
+    const int g = h * nkv / nq;
     const int q0 = qb * 32, pq = q0 + i32;           // this lane's query
     const int lim = min(pq, P - 1);                  // last key it attends
     const int kmax = min(q0 + 31, P - 1);            // last key of any query of the block
     // Q^T operands: dims 16 s + 8 hh + e of query pq, as hi and lo halves
     h8 qh[KS], ql[KS];
     {
-      const float* qrow = p.Q + (int64_t)min(pq, P - 1) * p.nq * HD + h * HD + 8 * hh;
+      const float* qrow = Qp + (int64_t)min(pq, P - 1) * nq * HD + h * HD + 8 * hh;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const f4 a = *gp((const f4*)(qrow + 16 * s)), b = *gp((const f4*)(qrow + 16 * s + 4));
@@ -728,7 +740,7 @@ __device__ __attribute__((noinline)) void att_stage_mfma(PCx& c, int l) {
 #pragma unroll
     for (int b = 0; b < DB; ++b) o[b] = f32x16{};
     float m = -INFINITY, ls = 0.f;
-    const int64_t hbase = ((int64_t)l * p.nkv + g) * p.max_seq * HD;
+    const int64_t hbase = ((int64_t)l * nkv + g) * max_seq * HD;
     const uint16_t* kbase = p.kc + hbase;
     const uint16_t* vbase = p.vc + hbase;
     for (int kb0 = 0; kb0 <= kmax; kb0 += 32) {
@@ -795,7 +807,7 @@ __device__ __attribute__((noinline)) void att_stage_mfma(PCx& c, int l) {
     // the query's sum over all keys: this lane's keys plus those of lane l ^ 32
     const float lt = ls + __shfl_xor(ls, 32);
     if (pq < P) {
-      const int64_t orow = (int64_t)pq * p.ldo + h * HD;
+      const int64_t orow = (int64_t)pq * ldo + h * HD;
       const float inv = 1.0f / lt;
 #pragma unroll
       for (int b = 0; b < DB; ++b)
@@ -811,8 +823,8 @@ __device__ __attribute__((noinline)) void att_stage_mfma(PCx& c, int l) {
             lo[e] = (_Float16)(v - (float)hi[e]);
           }
           const int64_t oi = orow + 32 * b + 8 * a + 4 * hh;
-          *gp((u2*)(p.Oh + oi)) = __builtin_bit_cast(u2, hi);
-          *gp((u2*)(p.Ol + oi)) = __builtin_bit_cast(u2, lo);
+          *gp((u2*)(Ohp + oi)) = __builtin_bit_cast(u2, hi);
+          *gp((u2*)(Olp + oi)) = __builtin_bit_cast(u2, lo);
         }
     }
     it = p.dynamic ? __builtin_amdgcn_readfirstlane(nxt_raw) : nxt_raw;
@@ -833,7 +845,10 @@ __device__ __attribute__((noinline)) void att_stage_mfma(PCx& c, int l) {
 constexpr int kAttNst = 3;
 
 template <int HD>
-__device__ __attribute__((noinline)) void att_stage_wg(PCx& c, int l) {
+__device__ __attribute__((noinline)) void att_stage_wg(PCx& c_ref, int l) {
+  // a local copy: read through the reference, its fields would be reloaded from memory (vector
+  // loads that wait behind the block DMAs in flight) after every asm statement that clobbers memory
+  PCx c = c_ref;
   constexpr int KS = HD / 16;              // MFMA K-steps over the head dims
   constexpr int DB = HD / 32;              // 32-dim blocks of O^T
   constexpr int CPR = HD / 8;              // 16-byte chunks per K / V row
@@ -844,8 +859,14 @@ __device__ __attribute__((noinline)) void att_stage_wg(PCx& c, int l) {
   static_assert(DPW * kPW == TPB && DPW >= 1 && DPW <= 2, "K and V blocks split evenly over the wavefronts");
   static_assert(kAttNst * 2 * BLK + 2 * HD * kVtStride * 2 <= kClaimOff, "attention staging overlaps the claim slot");
   const PParams& p = *c.pp;
-  const int G = p.nq / p.nkv, QPW = kPW / G, SB = 32 * QPW;
-  const int P = p.P, nsb = (P + SB - 1) / SB, items = p.nkv * nsb;
+  // the fields the item loop uses, as locals: p is read through a pointer, and every asm statement
+  // that clobbers memory would make the compiler reload them (loads that wait behind the DMAs)
+  uint16_t* const Ohp = (uint16_t*)uniform_ptr(p.Oh);
+  uint16_t* const Olp = (uint16_t*)uniform_ptr(p.Ol);
+  const float* const Qp = (const float*)uniform_ptr(p.Q);
+  const int ldo = p.ldo, nq = p.nq, nkv = p.nkv, max_seq = p.max_seq;
+  const int G = nq / nkv, QPW = kPW / G, SB = 32 * QPW;
+  const int P = p.P, nsb = (P + SB - 1) / SB, items = nkv * nsb;
   const int i32 = c.lane & 31, hh = c.lane >> 5;
   const float qscale = kLog2e / __builtin_sqrtf((float)HD);
   const uint32_t lds0 = (uint32_t)(uintptr_t)pf_smem;
@@ -853,14 +874,14 @@ __device__ __attribute__((noinline)) void att_stage_wg(PCx& c, int l) {
   // static deal in rounds of `grid` items: every other round takes its super-blocks in reverse, so a
   // workgroup that drew one of the longest items in one round draws one of the shortest in the next
   // (with grid a multiple of n_kv the kv head of a workgroup's items stays the same)
-  const bool snake = !p.dynamic && c.grid % p.nkv == 0;
+  const bool snake = !p.dynamic && c.grid % nkv == 0;
   wg_items(c, items, [&](int it) {
     if (snake && (it / c.grid) % 2 == 1) {
       const int r0 = it - it % c.grid, j = it - r0, nr = min(c.grid, items - r0);
-      it = r0 + (nr / p.nkv - 1 - j / p.nkv) * p.nkv + j % p.nkv;
+      it = r0 + (nr / nkv - 1 - j / nkv) * nkv + j % nkv;
     }
     // the longest items (latest query super-blocks) first
-    const int sbi = nsb - 1 - it / p.nkv, g = it - (it / p.nkv) * p.nkv;
+    const int sbi = nsb - 1 - it / nkv, g = it - (it / nkv) * nkv;
     const int h = g * G + c.wave / QPW;
     const int q0 = sbi * SB + (c.wave % QPW) * 32, pq = q0 + i32;
     const bool active = q0 < P;
@@ -871,7 +892,7 @@ __device__ __attribute__((noinline)) void att_stage_wg(PCx& c, int l) {
     // Q^T operands: dims 16 s + 8 hh + e of query pq, as hi and lo halves
     h8 qh[KS], ql[KS];
     {
-      const float* qrow = p.Q + (int64_t)min(pq, P - 1) * p.nq * HD + h * HD + 8 * hh;
+      const float* qrow = Qp + (int64_t)min(pq, P - 1) * nq * HD + h * HD + 8 * hh;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const f4 a = *gp((const f4*)(qrow + 16 * s)), b = *gp((const f4*)(qrow + 16 * s + 4));
@@ -886,7 +907,9 @@ __device__ __attribute__((noinline)) void att_stage_wg(PCx& c, int l) {
     }
     // DMA lanes: transfer j of a block (K: j < TPB / 2, V: the rest) covers key rows RPT (j % (TPB / 2)) ..;
     // lane i -> row rr = that + i / CPR, LDS chunk i % CPR, which holds the row's chunk (i % CPR) ^ (rr % CPR)
-    const int64_t head_row = ((int64_t)l * p.nkv + g) * p.max_seq;
+    const int64_t head_row = ((int64_t)l * nkv + g) * max_seq;
+    const void* const kcp = uniform_ptr(p.kc);
+    const void* const vcp = uniform_ptr(p.vc);
     auto issue = [&](int b) {
       const uint32_t st = lds0 + (uint32_t)((b % kAttNst) * 2 * BLK);
 #pragma unroll
@@ -895,7 +918,7 @@ __device__ __attribute__((noinline)) void att_stage_wg(PCx& c, int l) {
         const int rr = jj * RPT + c.lane / CPR, cc = c.lane % CPR, gq = cc ^ (rr % CPR);
         const int key = min(b * 32 + rr, kmax);  // rows past the last key repeat it: finite, and masked
         const uint32_t voff = (uint32_t)((head_row + key) * HD * 2) + (uint32_t)gq * 16u;
-        dma16(st + isv * BLK + jj * 1024, isv ? (const void*)p.vc : (const void*)p.kc, voff);
+        dma16(st + isv * BLK + jj * 1024, isv ? vcp : kcp, voff);
       }
     };
     auto wait_block = [&](int later) {  // later blocks of DMAs that may stay in flight (0 or 1)
@@ -974,7 +997,7 @@ __device__ __attribute__((noinline)) void att_stage_wg(PCx& c, int l) {
     __syncthreads();  // the next item's DMAs reuse the stages
     const float lt = ls + __shfl_xor(ls, 32);
     if (active && pq < P) {
-      const int64_t orow = (int64_t)pq * p.ldo + h * HD;
+      const int64_t orow = (int64_t)pq * ldo + h * HD;
       const float inv = 1.0f / lt;
 #pragma unroll
       for (int d = 0; d < DB; ++d)
@@ -989,8 +1012,8 @@ __device__ __attribute__((noinline)) void att_stage_wg(PCx& c, int l) {
             lo[e] = (_Float16)(v - (float)hi[e]);
           }
           const int64_t oi = orow + 32 * d + 8 * a + 4 * hh;
-          *gp((u2*)(p.Oh + oi)) = __builtin_bit_cast(u2, hi);
-          *gp((u2*)(p.Ol + oi)) = __builtin_bit_cast(u2, lo);
+          *gp((u2*)(Ohp + oi)) = __builtin_bit_cast(u2, hi);
+          *gp((u2*)(Olp + oi)) = __builtin_bit_cast(u2, lo);
         }
     }
   });
