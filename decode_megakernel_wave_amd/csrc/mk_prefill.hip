@@ -215,15 +215,39 @@ __device__ __forceinline__ int op_chunk(int r, int q) { return r * 64 + ((q ^ ((
 // The operands stream through kNst LDS stages by global -> LDS DMA, kNst - 1 K
 // steps ahead of the matrix cores: per step each wavefront moves 1 KB of A hi,
 // A lo and B (16 rows x 64 bytes each), which the MFMAs read as they landed.
+// Not inlined: its registers are allocated apart from the rest of the kernel's, so the kernel's
+// spills never land in the K loop (a spill reload there is a vector load whose wait also waits for
+// every DMA in flight).  It works on local copies of the context and the GEMM description.
 template <int TN>
-__device__ __forceinline__ void gemm_tile(PCx& c, const Gemm& g, int tm, int tn, int split, int S, int tile, int tiles) {
+__device__ __attribute__((noinline)) void gemm_tile(PCx& c_ref, const Gemm& g_ref, int tm, int tn, int split, int S,
+                                                    int tile, int tiles) {
+  PCx c = c_ref;
+  Gemm g = g_ref;
+  // arguments arrive in vector registers: make the loop bounds and the epilogue's choices scalar
+  tm = __builtin_amdgcn_readfirstlane(tm);
+  tn = __builtin_amdgcn_readfirstlane(tn);
+  split = __builtin_amdgcn_readfirstlane(split);
+  S = __builtin_amdgcn_readfirstlane(S);
+  tile = __builtin_amdgcn_readfirstlane(tile);
+  tiles = __builtin_amdgcn_readfirstlane(tiles);
+  g.ep = __builtin_amdgcn_readfirstlane(g.ep);
+  g.layer = __builtin_amdgcn_readfirstlane(g.layer);
+  g.lda = __builtin_amdgcn_readfirstlane(g.lda);
+  g.K = __builtin_amdgcn_readfirstlane(g.K);
+  g.norm = __builtin_amdgcn_readfirstlane(g.norm);
+  g.n_out = __builtin_amdgcn_readfirstlane(g.n_out);
+  g.ld_out = __builtin_amdgcn_readfirstlane(g.ld_out);
+  c.wave = __builtin_amdgcn_readfirstlane(c.wave);
   constexpr int NB = TN / 128;            // B transfers per wavefront per step
   constexpr int NJ = TN / 64;             // accumulators per wavefront: 32 weight rows each
   constexpr int kStage = stage_bytes(TN);
   constexpr int kNst = kRsOff / kStage;   // stages that fit: 4 of 32 KB (TN 256), 5 of 24 KB (TN 128)
   static_assert(kNst >= 3 && kNst - 2 <= 3, "dma_wait covers the later steps in flight");
-  const PParams& p = *c.pp;
-  // the values the K loop uses, as locals: the structs sit in memory, and the loop's waits clobber it
+  // the parameters as a local copy, loaded once: read through the pointer, the epilogue would reload
+  // them after each of its stores, and each reload waits for the stores before it
+  const PParams pcopy = *c.pp;
+  const PParams& p = pcopy;
+  // the values the K loop uses, as locals
   const int wave = c.wave, lane = c.lane;
   const void* const Ah = uniform_ptr(g.Ah);
   const void* const Al = uniform_ptr(g.Al);
@@ -938,9 +962,11 @@ __device__ __attribute__((noinline)) void att_stage_wg(PCx& c_ref, int l) {
       if (b + kAttNst - 1 < nblk) issue(b + kAttNst - 1);
       const uint8_t* kst = pf_smem + (b % kAttNst) * 2 * BLK;
       _Float16* vt = vt_base + (b & 1) * HD * kVtStride;
-      // V block -> V^T: thread t takes key t / CPR, dims 8 (t % CPR) .. + 8
+      // V block -> V^T: thread t takes key t % 32, dims 8 (t / 32) .. + 8, so the lanes of a 2-byte
+      // store write consecutive keys of one V^T row (keys split over the lanes instead hit the same
+      // LDS banks 8-16 ways: the V^T rows sit 80 bytes apart)
       if (c.tid < 32 * CPR) {
-        const int rr = c.tid / CPR, gq = c.tid % CPR;
+        const int rr = c.tid % 32, gq = c.tid / 32;
         const h8 vh = *(const h8*)(kst + BLK + rr * HD * 2 + ((gq ^ (rr % CPR)) << 4));
 #pragma unroll
         for (int e = 0; e < 8; ++e) vt[(gq * 8 + e) * kVtStride + rr] = vh[e];
