@@ -668,8 +668,12 @@ __device__ __forceinline__ void op_qkv(Cx& c, Ring& ring, const Ins& in) {
   // epilogue does not wait on a global load per unit
   const int hh = head_dim(kp) / 2, nqh = kp.nq * hh, nkh = kp.nkv * hh;
   float* rope = c.sm.resid;
-  for (int i = c.tid; i < 2 * hh; i += kThreads) rope[i] = *gp(kp.rope + (int64_t)c.pos * hh * 2 + i);
+  // loaded before the input is polled but stored to LDS after it: a wait for this load right away
+  // would also wait for every weight DMA in flight before the polls are even issued
+  static_assert(kThreads >= 2 * 128, "one RoPE value per thread (head_dim <= 256)");
+  const float rv = c.tid < 2 * hh ? *gp(kp.rope + (int64_t)c.pos * hh * 2 + c.tid) : 0.f;
   const float ss = stage_layer_input(c, l, in.kpad, g1, OP_QKV);
+  if (c.tid < 2 * hh) rope[c.tid] = rv;
   const float scale = finish_staging(c, kp.d, true, ss);
   // Output element `half` (0: row i, 1: row i + hd/2) of global unit g: a
   // rotary pair of a q head (fp32, one copy, the other epoch re-armed) or a
