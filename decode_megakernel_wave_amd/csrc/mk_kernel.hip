@@ -78,15 +78,6 @@ using namespace mk;
 
 namespace {
 
-// Per-slice staging of split-K GEMV inputs (stage_slice): off by default.  On
-// the ~2B decode (512-token prompt, 512 tokens per launch) it measured 464.6-
-// 465.0 ms per launch against 462.0-462.5 with the workgroup barrier: a slice
-// whose wavefronts start early issues its ring refills ahead of the other
-// slices' polls, and a CU's memory requests are served in order.
-#ifndef MK_SLICE_STAGING
-#define MK_SLICE_STAGING 0
-#endif
-constexpr bool kSliceStaging = MK_SLICE_STAGING != 0;
 
 
 // head_dim and query heads per kv head: compile-time constants in the specialised build
@@ -103,7 +94,6 @@ struct Smem {
   float* wsum;       // [kWaves] partial sums of squares
   uint64_t* keys;    // [kWaves]
   uint32_t* misc;    // [16]
-  uint32_t* slice;   // [kWaves] K-slice staging tokens
 };
 
 struct Cx {
@@ -353,76 +343,6 @@ __device__ __forceinline__ float stage_vec(Cx& c, const float* src, float* dst, 
     }
   }
   return ss;
-}
-
-// Dependencies in pieces ("8 - Ecrire son megakernel", section 8.8, item 2):
-// a GEMV whose K is split over ks wavefront slices needs, in each wavefront,
-// only the slice it multiplies.  The rg = kWaves / ks wavefronts of a slice
-// stage it between them (wavefront part p of rg takes the 16-byte groups p,
-// p + rg, ... of each 64-group row, n values in all, zero past n) and wait
-// only for each other, through per-wavefront tokens in LDS, instead of for
-// the whole vector behind a workgroup barrier.
-__device__ __forceinline__ void stage_slice(Cx& c, const float* src, float* dst, int n, int s0, int len, int part, int nparts,
-                                            int op, int layer) {
-  constexpr int kGroups = 4;  // 16-byte groups a lane stages per round
-  const Rsrc rs = sync_rsrc(src, (uint32_t)n * 4u);
-  const int stride = 64 * nparts * 4;  // floats between a lane's groups
-  for (int base = s0 + (part * 64 + c.lane) * 4; base < s0 + len; base += stride * kGroups) {
-    u4 v[kGroups];
-#pragma unroll
-    for (int k = 0; k < kGroups; ++k) {
-      const int i = base + k * stride;
-      v[k] = i < s0 + len && i < n ? ldc128(rs, (uint32_t)i * 4u) : u4{0u, 0u, 0u, 0u};
-    }
-    if (sentinel_mode(c)) {
-      for (;;) {
-        bool pending = false;
-#pragma unroll
-        for (int k = 0; k < kGroups; ++k) {
-          const int i = base + k * stride;
-          pending |= i < s0 + len && i < n && any_sent(v[k]);
-        }
-        if (!pending || c.fail) break;
-        if (expired(c, op, layer, base)) {
-          c.fail = true;
-          break;
-        }
-        poll_pause(c);
-#pragma unroll
-        for (int k = 0; k < kGroups; ++k) {
-          const int i = base + k * stride;
-          if (i < s0 + len && i < n && any_sent(v[k])) v[k] = ldc128(rs, (uint32_t)i * 4u);
-        }
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kGroups; ++k) {
-      const int i = base + k * stride;
-      if (i < s0 + len)
-        *(f4*)(dst + i) = f4{__uint_as_float(v[k][0]), __uint_as_float(v[k][1]), __uint_as_float(v[k][2]), __uint_as_float(v[k][3])};
-    }
-  }
-}
-
-// This wavefront's part of its slice is in LDS: post its token, then wait for
-// the tokens of the other wavefronts of the slice (waves ki, ki + ks, ...).
-// A token names the step and the instruction, so none is ever reset.
-__device__ __forceinline__ void slice_ready(Cx& c, int ks) {
-  const uint32_t token = ((uint32_t)c.step << 16) | (uint32_t)(c.pc + 1);
-  volatile uint32_t* tok = c.sm.slice;
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the part's LDS stores are done
-  if (c.lane == 0) tok[c.wave] = token;
-  for (int w = c.wave % ks; w < kWaves; w += ks) {
-    if (w == c.wave) continue;
-    while (__builtin_amdgcn_readfirstlane(tok[w]) != token && !c.fail) {
-      if (expired(c, OP_DOWN, -1, w)) {
-        c.fail = true;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-  }
-  asm volatile("" ::: "memory");
 }
 
 // Stage an fp16 row of read-only data (an embedding row) as fp32, times the
@@ -1308,21 +1228,9 @@ __device__ __forceinline__ void op_down(Cx& c, Ring& ring, const Ins& in) {
   if (!sentinel_mode(c)) cta_sync(c);
   const float* rsrc = buf_at(kp.xa, c.e, l, c.rep);
   const uint32_t r0 = resid_issue(c, rsrc, nullptr, in.u0, in.nu);
-  if (kSliceStaging && in.ks > 1) {
-    // each K slice staged by its own wavefronts; the residual rows are read after the K-slice merge's barrier
-    const int len = in.kpad / in.ks;
-    stage_slice(c, buf_at(kp.m, c.e, l, c.rep), c.sm.vec, kp.f, (c.wave % in.ks) * len, len, c.wave / in.ks, kWaves / in.ks,
-                OP_DOWN, l);
-    resid_finish(c, r0, rsrc, nullptr, in.u0, in.nu, OP_DOWN, l);
-    slice_ready(c, in.ks);
-    ts_mark(c, 1);
-    ts_mark(c, 2);
-    mark_ready(c);
-  } else {
-    stage_vec(c, buf_at(kp.m, c.e, l, c.rep), c.sm.vec, kp.f, in.kpad, nullptr, OP_DOWN, l);
-    resid_finish(c, r0, rsrc, nullptr, in.u0, in.nu, OP_DOWN, l);
-    finish_staging(c, 0, false, 0.f);
-  }
+  stage_vec(c, buf_at(kp.m, c.e, l, c.rep), c.sm.vec, kp.f, in.kpad, nullptr, OP_DOWN, l);
+  resid_finish(c, r0, rsrc, nullptr, in.u0, in.nu, OP_DOWN, l);
+  finish_staging(c, 0, false, 0.f);
   const bool staged = staged_rows(in);
   gemv_dispatch(c, ring, in, c.sm.vec, 1.f, [&](int u, float y, float) {
     const float v = c.sm.resid[u] + y;
@@ -1790,8 +1698,6 @@ __global__ __launch_bounds__(kThreads, 1) void MK_MONOKERNEL(const KParams* __re
   c.sm.wsum = (float*)(small + kOffWsum);
   c.sm.keys = (uint64_t*)(small + kOffKeys);
   c.sm.misc = (uint32_t*)(small + kOffMisc);
-  c.sm.slice = (uint32_t*)(small + kOffSlice);
-  if (c.tid < kWaves) c.sm.slice[c.tid] = 0u;  // no token is 0; the first instruction's barriers publish this
 
   Ring ring;
   {

@@ -34,8 +34,7 @@ constexpr int kOffFlags = 0;              // u32 [2][kWaves] failure flags (doub
 constexpr int kOffWsum = 64;              // f32 [kWaves] partial sums of squares
 constexpr int kOffKeys = 96;              // u64 [kWaves] argmax keys
 constexpr int kOffMisc = 160;             // u32 [16] trace scratch
-constexpr int kOffSlice = 224;            // u32 [kWaves] K-slice staging tokens
-static_assert(kOffSlice + 4 * kWaves <= kSmallBytes, "small LDS fields overflow");
+static_assert(kOffMisc + 64 <= kSmallBytes, "small LDS fields overflow");
 
 // Sentinels: bit patterns no computed value takes.  A quiet NaN whose low
 // payload bits can come neither from arithmetic (default NaN 0x7FC00000) nor
