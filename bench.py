@@ -137,9 +137,11 @@ def traced_decode(model, w, ids, P: int, n: int, opts, trace_steps: int, top_k: 
         + ", ".join(f"{k} {v['median_us']:.2f}/{v['p99_us']:.2f}" for k, v in res.items() if v["median_us"] is not None))
     log("[bench] critical-path span per stage (us, mean): "
         + ", ".join(f"{k} {v['span_mean_us']:.2f}" for k, v in res.items() if v["span_mean_us"] is not None))
-    return {"traced_steps": trace_steps, "definition": "last producer's publish -> a waiting consumer's inputs "
-            "staged, device wall clock (10 ns ticks); median / p99 over (stage, consumer) pairs; critical = last "
-            "consumer ready - last producer done, per stage", "per_op": res}
+    return {"traced_steps": trace_steps, "definition": "last producer's publish (its output stores issued) -> a "
+            "waiting consumer's inputs staged, device wall clock (10 ns ticks); median / p99 over (stage, consumer) "
+            "pairs; critical = last consumer ready - last producer's publish, per stage; early_consumers = consumers "
+            "staged before the last producer published (they needed only earlier producers); span = last consumer "
+            "done - last producer done", "per_op": res}
 
 
 def fine_mark_decode(model, w, ids, P: int, opts) -> dict:

@@ -1748,6 +1748,10 @@ __global__ __launch_bounds__(kThreads, 1) void MK_MONOKERNEL(const KParams* __re
         case OP_CHAIN: op_chain(c, ring, in); break;
         default: break;
       }
+      // thread 0 is past the op's last output stores (issued, not yet acknowledged): the journal's
+      // publish time, before the progress store and the failure vote
+      uint64_t t_pub = 0;
+      if (tr && c.tid == 0) t_pub = __builtin_amdgcn_s_memrealtime();
       ts_mark(c, 3);
       // written through (not left dirty in L2), so the step's release fence finds nothing to write back
       if (c.tid == 0) stc32(kp.progress + c.cta, ((uint32_t)step << 16) | (uint32_t)(c.pc + 1));
@@ -1759,11 +1763,11 @@ __global__ __launch_bounds__(kThreads, 1) void MK_MONOKERNEL(const KParams* __re
         r[0] = (uint32_t)c.cta;
         r[1] = (uint32_t)step;
         r[2] = (uint32_t)c.pc;
-        r[3] = (uint32_t)in.op | ((uint32_t)(in.layer & 0xFFFF) << 8);
+        r[3] = (uint32_t)in.op | ((uint32_t)(in.layer & 0xFFFF) << 8) | ((uint32_t)(c.xcc & 0x7F) << 24) | (1u << 31);
         r[4] = (uint32_t)t_wait;
         r[5] = c.sm.misc[0] ? c.sm.misc[0] - (uint32_t)t_wait : 0u;
         r[6] = (uint32_t)(t_done - t_wait);
-        r[7] = (uint32_t)c.xcc;
+        r[7] = (uint32_t)(t_pub - t_wait);
       }
     }
     if (kp.forced && step + 1 < kp.n_steps) c.tok = __builtin_amdgcn_readfirstlane(kp.forced[step + 1]);

@@ -1,19 +1,27 @@
 """Inter-stage handoff latency from the monokernel's time journal.
 
 The journal (``mk_read_trace`` / ``mk_chain_read_trace``) holds one record of
-8 uint32 per (workgroup, step, instruction): {cta, step, pc, op | layer << 8,
-t_wait (low 32 bits of the 100 MHz device clock), t_ready - t_wait,
-t_done - t_wait, xcc}.  Every workgroup runs the same instruction sequence and
-each instruction consumes what the one before it produced (the first QKV
-instruction of a step consumes the token every workgroup computed itself).
+8 uint32 per (workgroup, step, instruction): {cta, step, pc,
+op | layer << 8 | xcc << 24 | 1 << 31, t_wait (low 32 bits of the 100 MHz
+device clock), t_ready - t_wait, t_done - t_wait, t_pub - t_wait}: t_ready =
+inputs staged, t_pub = the instruction's output stores issued (thread 0, right
+after the op), t_done = after the workgroup's failure vote.  Records without
+bit 31 come from builds that journalled {..., op | layer << 8, ..., xcc} and
+no publish time; their done time stands in for it.  Every workgroup runs the
+same instruction sequence and each instruction consumes what the one before
+it produced (the first QKV instruction of a step consumes the token every
+workgroup computed itself).
 
 Handoff latency is measured the way "7 - AMD et le monokernel" (section 7.3)
 frames the cost of a synchronisation: from the moment the last producer of a
-stage has published (its ``t_done``) to the moment a consumer that was
-already waiting has its inputs staged (``t_ready``).  Per stage the
-critical-path handoff is the last consumer's ready time minus the last
-producer's done time.  Consumers that started waiting after the data was
-complete only pay a load round trip; they are reported apart.
+stage has published (its ``t_pub``: the stores are issued then, so this is an
+upper bound of the latency) to the moment a consumer that was already waiting
+has its inputs staged (``t_ready``).  Per stage the critical-path handoff is
+the last consumer's ready time minus the last producer's publish time.
+Consumers staged before the last producer published depended only on earlier
+producers (an attention split needs the q rows of its own kv head): they are
+counted ("early_consumers"), not timed.  Consumers that started waiting after
+the data was complete only pay a load round trip; they are reported apart.
 """
 from __future__ import annotations
 
@@ -35,7 +43,7 @@ def handoffs(records: np.ndarray) -> dict:
     """Per-op handoff statistics (microseconds) of a time journal.
 
     Returns {op_name: {"stages" (stages with a waiting consumer), "waiting_consumers",
-    "median_us", "p99_us",
+    "early_consumers", "median_us", "p99_us",
     "critical_median_us", "critical_p99_us", "late_staging_median_us",
     "span_median_us", "span_mean_us"}} plus an "all" entry pooling every op.  The
     span of a stage is its share of the critical path: from the last producer's
@@ -49,6 +57,8 @@ def handoffs(records: np.ndarray) -> dict:
     ready_rel = r[:, 5].astype(np.int64)
     done = tw + r[:, 6].astype(np.int64)
     ready = tw + ready_rel
+    has_pub = (r[:, 3] >> 31) == 1
+    pub = np.where(has_pub, tw + r[:, 7].astype(np.int64), done)
     step = r[:, 1].astype(np.int64)
     pc = r[:, 2].astype(np.int64)
     op = (r[:, 3] & 0xFF).astype(np.int64)
@@ -63,8 +73,9 @@ def handoffs(records: np.ndarray) -> dict:
         if len(cons) == 0:
             continue
         last_done = done[prod].max()
+        last_pub = pub[prod].max()
         name = OP_NAMES.get(int(op[cons[0]]), str(int(op[cons[0]])))
-        d = per_op.setdefault(name, {"lat": [], "crit": [], "late": [], "span": []})
+        d = per_op.setdefault(name, {"lat": [], "crit": [], "late": [], "span": [], "early": 0})
         # the span is every stage's share of the critical path
         d["span"].append(int(done[groups[k]].max() - last_done))
         if int(op[prod[0]]) == 8:
@@ -72,19 +83,20 @@ def handoffs(records: np.ndarray) -> dict:
             # computed itself: no handoff between workgroups
             continue
         # consumers that were waiting when the last producer published and were staged after
-        # it (a consumer that needs only some producers may be staged earlier: not a handoff
-        # from the last one)
-        waiting = cons[(tw[cons] <= last_done) & (ready[cons] >= last_done)]
-        late = cons[tw[cons] > last_done]
-        d["lat"].extend((ready[waiting] - last_done).tolist())
+        # it; one staged earlier needed only some producers: not a handoff from the last one
+        waiting = cons[(tw[cons] <= last_pub) & (ready[cons] >= last_pub)]
+        d["early"] += int(np.count_nonzero(ready[cons] < last_pub))
+        late = cons[tw[cons] > last_pub]
+        d["lat"].extend((ready[waiting] - last_pub).tolist())
         d["late"].extend(ready_rel[late].tolist())
         if len(waiting):
-            d["crit"].append(int(ready[cons].max() - last_done))
+            d["crit"].append(int(ready[cons].max() - last_pub))
     out = {}
-    pooled = {"lat": [], "crit": [], "late": [], "span": []}
+    pooled = {"lat": [], "crit": [], "late": [], "span": [], "early": 0}
     for name, d in per_op.items():
-        for k in pooled:
+        for k in ("lat", "crit", "late", "span"):
             pooled[k].extend(d[k])
+        pooled["early"] += d["early"]
         out[name] = _summary(d)
     if per_op:
         out["all"] = _summary(pooled)
@@ -95,7 +107,7 @@ def _summary(d: dict) -> dict:
     def q(v, p):
         return float(np.percentile(np.asarray(v, dtype=np.float64) * TICK_US, p)) if len(v) else None
 
-    return {"stages": len(d["crit"]), "waiting_consumers": len(d["lat"]),
+    return {"stages": len(d["crit"]), "waiting_consumers": len(d["lat"]), "early_consumers": d["early"],
             "median_us": q(d["lat"], 50), "p99_us": q(d["lat"], 99),
             "critical_median_us": q(d["crit"], 50), "critical_p99_us": q(d["crit"], 99),
             "late_staging_median_us": q(d["late"], 50), "span_median_us": q(d["span"], 50),

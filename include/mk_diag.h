@@ -37,9 +37,11 @@ int mk_count_sentinels(mk_ctx* ctx, int64_t* count);
 int mk_count_sentinels_noalloc(mk_ctx* ctx, int64_t* count);
 
 /* Copy the time journal of the last launch into host memory.  Each record is
- * 8 uint32: {cta, step, pc, op | layer << 8, t_wait_lo, t_ready - t_wait,
- * t_done - t_wait, xcc}, in ticks of the 100 MHz device wall clock; unused
- * records are zero.  *n_records receives the record count (capacity query if
+ * 8 uint32: {cta, step, pc, op | layer << 8 | xcc << 24 | 1 << 31, t_wait_lo,
+ * t_ready - t_wait, t_done - t_wait, t_pub - t_wait}, in ticks of the 100 MHz
+ * device wall clock: t_ready = inputs staged, t_pub = the instruction's output
+ * stores issued, t_done = after the workgroup's failure vote.  Unused records
+ * are zero.  *n_records receives the record count (capacity query if
  * host_buf is NULL). */
 int mk_read_trace(mk_ctx* ctx, uint32_t* host_buf, int64_t capacity_records, int64_t* n_records);
 

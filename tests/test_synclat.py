@@ -51,6 +51,30 @@ def test_consumers_staged_before_the_last_producer_are_not_handoffs():
     assert a["waiting_consumers"] == 1 and a["median_us"] == pytest.approx(0.40)
 
 
+def recp(cta, step, pc, op, t_wait, ready_rel, done_rel, pub_rel, xcc=0):
+    """A record of the current layout: op | xcc << 24 | 1 << 31, publish time in the last word."""
+    return [cta, step, pc, op | (xcc << 24) | (1 << 31), t_wait & 0xFFFFFFFF, ready_rel, done_rel, pub_rel]
+
+
+def test_publish_time_is_the_handoff_start():
+    """With a publish time in the record the latency runs from the last producer's publish (its
+    stores issued), not from its done time after the failure vote; consumers staged before that
+    publish are counted as early, not timed."""
+    r = [recp(0, 0, 0, 4, 0, 5, 100, 70, xcc=3),   # O-proj producer: published at 70, done at 100
+         recp(1, 0, 0, 4, 0, 5, 160, 130, xcc=5),  # the last producer: published at 130, done at 160
+         recp(0, 0, 1, 5, 90, 60, 300, 280),       # waiting from 90: ready at 150 -> 20 ticks after 130
+         recp(1, 0, 1, 5, 110, 70, 300, 280),      # waiting from 110: ready at 180 -> 50 ticks
+         recp(2, 0, 1, 5, 20, 100, 300, 280)]      # ready at 120, before the last publish: early
+    res = synclat.handoffs(np.array(r, dtype=np.uint32))
+    u = res["up_gate"]
+    assert u["waiting_consumers"] == 2 and u["early_consumers"] == 1
+    assert u["median_us"] == pytest.approx(0.35)           # median of 20 and 50 ticks
+    assert u["critical_median_us"] == pytest.approx(0.50)  # last ready (180) - last publish (130)
+    assert u["span_median_us"] == pytest.approx(2.50)      # last consumer done (110 + 300) - last producer done (160)
+    # op and xcc share a word: the op is still read from the low byte
+    assert "o_proj" not in res and set(res) == {"up_gate", "all"}
+
+
 def test_empty_journal():
     assert synclat.handoffs(np.zeros((4, 8), dtype=np.uint32)) == {}
 
