@@ -77,3 +77,11 @@ def test_2b_geometry_upper_half_context(P):
     """T = 771..774 (splits of 25 positions: wavefront 0 holds 4, the others 3) and T = 1021..1024
     (splits of 32: every wavefront holds the full batch of 4 positions)."""
     _parity(inputs.M2B_GEOM_L2, P=P, n=4, expect_long=False)
+
+
+def test_2b_geometry_prompt_6000_partial_attention_round():
+    """Prompt of 6000 tokens: 47 super-blocks of 128 queries x 8 kv heads = 376 prefill attention
+    items, so the second round of the static deal (dealt in reverse super-block order) is partial
+    (120 items); 47 row tiles of 128 with a ragged last one (112 positions) on the 256-row GEMM
+    tiles; then decode on the long-split path."""
+    _parity(inputs.M2B_GEOM_L2_NARROW, P=6000, n=4, expect_long=True)
