@@ -429,9 +429,10 @@ __device__ __forceinline__ void ring_read_n(Ring& ring, u4 (&w)[4], int n, bool 
 // CUs that stream takes about 1.8 us, between two that do not 0.6-0.8 us, with
 // the rest of the chip streaming in both cases.  Issuing the last refills after
 // the stores lets the outputs leave first.  QKV's are issued later still, in
-// the attention stage after its q polls and K/V loads (the attention reads no
-// weights, so they still land before the next GEMV): 2 % faster decode than
-// issuing them after QKV's stores, where they sat ahead of those polls.  The
+// the attention stage after its q polls, K/V loads and scores (the attention
+// reads no weights, so they still land before the next GEMV): 2 % faster
+// decode than issuing them after QKV's stores, where they sat ahead of those
+// polls.  The
 // other GEMVs' could not wait that long: issued only after the next GEMV had
 // staged its inputs, they arrived late for it (4 % slower).
 
@@ -724,7 +725,7 @@ __device__ __forceinline__ void red_unit(Cx& c, int l, int h, int b) {
 constexpr int kPosBatch = 4;
 
 template <int GP, int DPL>
-__device__ __forceinline__ void att_pos_core(Cx& c, int l, int g, int sp, int j0, int ng, int t0, int t1, int G,
+__device__ __forceinline__ void att_pos_core(Cx& c, Ring& ring, int l, int g, int sp, int j0, int ng, int t0, int t1, int G,
                                              const float (&kv)[kPosBatch][DPL], const float (&vv)[kPosBatch][DPL]) {
   const KParams& kp = *c.kp;
   const int hd = head_dim(kp), S = kp.S;
@@ -786,6 +787,9 @@ __device__ __forceinline__ void att_pos_core(Cx& c, int l, int g, int sp, int j0
     }
   }
   ts_mark(c, 5);
+  // the refills QKV left owed go out here, behind the q polls, the K/V loads and the scores (issued
+  // before the scores they could hold the wavefront at the issue: 456.3 vs 457.3 ms per 512 tokens)
+  ring_settle(ring);
   // combine the wavefronts: scratch [wave][ng][hd + 2]
   float* scr = c.sm.scratch;
   const int rec = hd + 2;
@@ -1088,9 +1092,7 @@ __device__ __forceinline__ void att_short(Cx& c, Ring& ring, int l, int g, int s
       vv[b][k] = cur ? vcur[c.lane * DPL + k] : half_at<DPL>(vr[b], k);
     }
   }
-  // the refills QKV left owed go out behind the q polls and the K/V loads
-  ring_settle(ring);
-  for (int j0 = 0; j0 < G; j0 += GP) att_pos_core<GP, DPL>(c, l, g, sp, j0, min(GP, G - j0), t0, t1, G, kv, vv);
+  for (int j0 = 0; j0 < G; j0 += GP) att_pos_core<GP, DPL>(c, ring, l, g, sp, j0, min(GP, G - j0), t0, t1, G, kv, vv);
 }
 
 __device__ __forceinline__ void op_att(Cx& c, Ring& ring, const Ins& in) {
