@@ -370,7 +370,7 @@ struct mk_ctx {
   uint32_t* d_pbar = nullptr;
   uint64_t* d_pmarks = nullptr;     // [1 + 5 L + 1]: start, then each grid barrier (device clock)
   uint32_t* d_pqueue = nullptr;     // [1 + 5 L] work-queue counters
-  float* d_ppart = nullptr;         // [grid][kPartFloats] split-K partial tiles
+  float* d_ppart = nullptr;         // split-K partial tiles, attention key-chunk partials
   float* d_pXhl = nullptr;          // [2][P][d] fp16 hi / lo halves of x times the next gain
   float* d_pssp = nullptr;          // [ceil(d / 64)][P] partial sums of squares of x
   int pf_ldo = 0, pf_ldm = 0;       // row strides (halves) of the attention-output and MLP planes
@@ -479,7 +479,7 @@ int ctx_alloc_prefill(mk_ctx* c) {
   CHK(g.alloc(&c->d_pbar, 256));
   CHK(g.alloc(&c->d_pmarks, (size_t)(5 * k.n_layers + 2) * 8));
   CHK(g.alloc(&c->d_pqueue, (size_t)(5 * k.n_layers + 2) * 4));
-  CHK(g.alloc(&c->d_ppart, (size_t)c->pf_grid * kPartFloats * 4));
+  CHK(g.alloc(&c->d_ppart, (size_t)c->pf_grid * std::max(kPartFloats, 2 * kAttPartFloats) * 4));
   CHK(g.alloc(&c->d_ptile, (size_t)c->pf_grid * 4));
   CHK(g.alloc(&c->d_pp, sizeof(PParams)));
   return MK_OK;

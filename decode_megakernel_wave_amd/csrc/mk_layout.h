@@ -171,10 +171,13 @@ struct PParams {
   uint32_t* queue;          // [1 + 5 L] work-queue counters, one per stage (zero at launch)
   int32_t dynamic;          // 1: workgroups / wavefronts claim their tiles from the queue; 0: static deal
   int32_t pad1;
-  float* part;              // split-K partial tiles: [grid][kPartFloats]
+  float* part;              // split-K partial tiles [grid][kPartFloats]; in the attention stage of short
+                            // prompts the key chunks' partials [2 grid][kAttPartFloats]
   uint32_t* tile_cnt;       // [grid] split-K arrivals per output tile (zero at launch and between stages)
 };
 // One split-K partial: a tile of up to 128 x 256 fp32 accumulators.
 constexpr int kPartFloats = 128 * 256;
+// one attention key chunk's partial: 8 wavefronts x 64 lanes x (m, l and head_dim 128's 4 x 16 O^T values)
+constexpr int kAttPartFloats = 8 * 64 * (2 + 4 * 16);
 
 }  // namespace mk

@@ -868,7 +868,9 @@ __device__ __attribute__((noinline)) void att_stage_mfma(PCx& c_ref, int l) {
 // owns query l % 32; online softmax in the exp2 domain).
 constexpr int kAttNst = 3;
 
-template <int HD>
+// KSPLIT: the key-chunk variant for prompts with fewer items than workgroups (a template parameter,
+// so that the long prompts' variant carries none of the chunk bookkeeping in its registers).
+template <int HD, bool KSPLIT>
 __device__ __attribute__((noinline)) void att_stage_wg(PCx& c_ref, int l) {
   // a local copy: read through the reference, its fields would be reloaded from memory (vector
   // loads that wait behind the block DMAs in flight) after every asm statement that clobbers memory
@@ -890,7 +892,21 @@ __device__ __attribute__((noinline)) void att_stage_wg(PCx& c_ref, int l) {
   const float* const Qp = (const float*)uniform_ptr(p.Q);
   const int ldo = p.ldo, nq = p.nq, nkv = p.nkv, max_seq = p.max_seq;
   const int G = nq / nkv, QPW = kPW / G, SB = 32 * QPW;
-  const int P = p.P, nsb = (P + SB - 1) / SB, items = nkv * nsb;
+  const int P = p.P, nsb = (P + SB - 1) / SB;
+  // key blocks of super-block sbi's queries (causal: up to its last query)
+  auto nblk_of = [&](int sbi) { return min(sbi * SB + SB - 1, P - 1) / 32 + 1; };
+  // Short prompts have fewer (kv head, super-block) items than workgroups, and the latest
+  // super-block's item alone takes as long as the whole stage.  Then each item's keys are split
+  // into chunks of CB blocks, so that the chunks about fill the grid; a chunk writes its unnormalised
+  // partial (m, l, O) and the last chunk of an item to finish merges them in chunk order.
+  int CB = 1 << 30;
+  if (KSPLIT) {
+    int total = 0;
+    for (int sbi = 0; sbi < nsb; ++sbi) total += nblk_of(sbi);
+    CB = max(4, (nkv * total + c.grid - 1) / c.grid);
+  }
+  int items = 0;
+  for (int sbi = 0; sbi < nsb; ++sbi) items += nkv * ((nblk_of(sbi) + CB - 1) / CB);
   const int i32 = c.lane & 31, hh = c.lane >> 5;
   const float qscale = kLog2e / __builtin_sqrtf((float)HD);
   const uint32_t lds0 = (uint32_t)(uintptr_t)pf_smem;
@@ -898,21 +914,28 @@ __device__ __attribute__((noinline)) void att_stage_wg(PCx& c_ref, int l) {
   // static deal in rounds of `grid` items: every other round takes its super-blocks in reverse, so a
   // workgroup that drew one of the longest items in one round draws one of the shortest in the next
   // (with grid a multiple of n_kv the kv head of a workgroup's items stays the same)
-  const bool snake = !p.dynamic && c.grid % nkv == 0;
+  const bool snake = !KSPLIT && !p.dynamic && c.grid % nkv == 0;
   wg_items(c, items, [&](int it) {
     if (snake && (it / c.grid) % 2 == 1) {
       const int r0 = it - it % c.grid, j = it - r0, nr = min(c.grid, items - r0);
       it = r0 + (nr / nkv - 1 - j / nkv) * nkv + j % nkv;
     }
-    // the longest items (latest query super-blocks) first
-    const int sbi = nsb - 1 - it / nkv, g = it - (it / nkv) * nkv;
+    // the longest items (latest query super-blocks) first; per super-block its key chunks, then the
+    // kv heads (one chunk per item unless the keys are split)
+    int sbi = nsb - 1, base = 0, nch = (nblk_of(sbi) + CB - 1) / CB;
+    while (it - base >= nch * nkv) {
+      base += nch * nkv;
+      --sbi;
+      nch = (nblk_of(sbi) + CB - 1) / CB;
+    }
+    const int chunk = (it - base) / nkv, g = (it - base) - chunk * nkv;
     const int h = g * G + c.wave / QPW;
     const int q0 = sbi * SB + (c.wave % QPW) * 32, pq = q0 + i32;
     const bool active = q0 < P;
     const int lim = min(pq, P - 1);                    // last key this lane's query attends
     const int kmax_w = min(q0 + 31, P - 1);            // last key of this wavefront's queries
     const int kmax = min(sbi * SB + SB - 1, P - 1);    // last key of the workgroup's queries
-    const int nblk = kmax / 32 + 1;
+    const int b0 = chunk * min(CB, kmax / 32 + 1), b1 = min(kmax / 32 + 1, b0 + CB);  // this item's key blocks
     // Q^T operands: dims 16 s + 8 hh + e of query pq, as hi and lo halves
     h8 qh[KS], ql[KS];
     {
@@ -955,11 +978,11 @@ __device__ __attribute__((noinline)) void att_stage_wg(PCx& c_ref, int l) {
 #pragma unroll
     for (int b = 0; b < DB; ++b) o[b] = f32x16{};
     float m = -INFINITY, ls = 0.f;
-    for (int b = 0; b < kAttNst - 1 && b < nblk; ++b) issue(b);
-    for (int b = 0; b < nblk; ++b) {
-      wait_block(min(b + kAttNst - 2, nblk - 1) - b);
+    for (int b = b0; b < b0 + kAttNst - 1 && b < b1; ++b) issue(b);
+    for (int b = b0; b < b1; ++b) {
+      wait_block(min(b + kAttNst - 2, b1 - 1) - b);
       __syncthreads();  // block b landed (every wavefront's DMAs); block b - 1's stage and V^T b - 2 are free
-      if (b + kAttNst - 1 < nblk) issue(b + kAttNst - 1);
+      if (b + kAttNst - 1 < b1) issue(b + kAttNst - 1);
       const uint8_t* kst = pf_smem + (b % kAttNst) * 2 * BLK;
       _Float16* vt = vt_base + (b & 1) * HD * kVtStride;
       // V block -> V^T: thread t takes key t % 32, dims 8 (t / 32) .. + 8, so the lanes of a 2-byte
@@ -1021,7 +1044,58 @@ __device__ __attribute__((noinline)) void att_stage_wg(PCx& c_ref, int l) {
       }
     }
     __syncthreads();  // the next item's DMAs reuse the stages
-    const float lt = ls + __shfl_xor(ls, 32);
+    float lt = ls + __shfl_xor(ls, 32);
+    if (KSPLIT && nch > 1) {
+      // this chunk's partial: [item][wavefront][field][lane], fields m, l, then O^T's accumulators
+      // (items < 2 grid: the chunks are sized to about fill the grid, plus one partial chunk per
+      // (kv head, super-block), of which there are fewer than the grid)
+      constexpr int NF = 2 + DB * 16;
+      static_assert(kPW * NF * 64 <= kAttPartFloats, "a chunk's partial fits its slot");
+      float* const part = p.part;
+      float* mine = part + (int64_t)it * kAttPartFloats + (int64_t)c.wave * NF * 64 + c.lane;
+      *gp(mine) = m;
+      *gp(mine + 64) = lt;
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) *gp(mine + (2 + d * 16 + v) * 64) = o[d][v];
+      // release it and count it in; the last chunk of the item merges
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      uint32_t* last = (uint32_t*)(pf_smem + kClaimOff + 8);
+      uint32_t* const cnt = p.tile_cnt + sbi * nkv + g;
+      if (c.tid == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        const uint32_t before = __hip_atomic_fetch_add(gp(cnt), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        const uint32_t is_last = before == (uint32_t)nch - 1;
+        if (is_last) {
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+          __hip_atomic_store(gp(cnt), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);  // for the next layer
+        }
+        *last = is_last;
+      }
+      __syncthreads();
+      const uint32_t is_last = __builtin_amdgcn_readfirstlane(*last);
+      __syncthreads();
+      if (!is_last) return;
+      // merge the item's chunks in chunk order: M = max m, L = sum 2^(m - M) l, O = sum 2^(m - M) O
+      const int first = base + g;  // chunk k of the item is item first + k nkv
+      float M = -INFINITY;
+      for (int k = 0; k < nch; ++k) M = fmaxf(M, *gp(part + (int64_t)(first + k * nkv) * kAttPartFloats + (int64_t)c.wave * NF * 64 + c.lane));
+      lt = 0.f;
+#pragma unroll
+      for (int d = 0; d < DB; ++d) o[d] = f32x16{};
+      for (int k = 0; k < nch; ++k) {
+        const float* src = part + (int64_t)(first + k * nkv) * kAttPartFloats + (int64_t)c.wave * NF * 64 + c.lane;
+        const float mk = *gp(src);
+        const float wk = mk == -INFINITY ? 0.f : exp2f(mk - M);
+        lt += wk * *gp(src + 64);
+#pragma unroll
+        for (int d = 0; d < DB; ++d)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[d][v] += wk * *gp(src + (2 + d * 16 + v) * 64);
+      }
+    }
     if (active && pq < P) {
       const int64_t orow = (int64_t)pq * ldo + h * HD;
       const float inv = 1.0f / lt;
@@ -1089,6 +1163,8 @@ __global__ __launch_bounds__(kPT, 1) void mk_prefill_kernel(const PParams* __res
   const int64_t per_layer = (int64_t)(qd + 2 * kvd) * p.d + (int64_t)p.d * qd + 3LL * p.f * p.d;
   const int G = p.nq / p.nkv;
   const bool wg_att = G == 1 || G == 2 || G == 4 || G == 8;  // query heads of a kv head split the 8 wavefronts
+  // fewer (kv head, super-block) attention items than workgroups: split their keys into chunks
+  const bool ksplit = wg_att && p.nkv * ((p.P + 32 * (kPW / G) - 1) / (32 * (kPW / G))) < c.grid;
   // 5 stages per layer; every GEMM runs from one call site (its code is in the kernel once)
   for (int st = 0; st < 5 * p.L; ++st) {
     const int l = st / 5, kind = st - 5 * l;
@@ -1102,10 +1178,12 @@ __global__ __launch_bounds__(kPT, 1) void mk_prefill_kernel(const PParams* __res
     const uint16_t* gn = l + 1 < p.L ? p.norms + (int64_t)(l + 1) * 2 * p.d : nullptr;
     if (kind == 1) {
       if (p.hd == 64) {
-        if (wg_att) att_stage_wg<64>(c, l);
+        if (wg_att && ksplit) att_stage_wg<64, true>(c, l);
+        else if (wg_att) att_stage_wg<64, false>(c, l);
         else att_stage_mfma<64>(c, l);
       } else if (p.hd == 128) {
-        if (wg_att) att_stage_wg<128>(c, l);
+        if (wg_att && ksplit) att_stage_wg<128, true>(c, l);
+        else if (wg_att) att_stage_wg<128, false>(c, l);
         else att_stage_mfma<128>(c, l);
       } else {
         att_stage<256>(c, l);
