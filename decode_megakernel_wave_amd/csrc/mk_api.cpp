@@ -28,6 +28,8 @@ hipError_t mk_launch_monokernel_w4h128(const KParams* kp_dev, int grid, int lds_
 hipError_t mk_kernel_attributes_w4h128(int lds_bytes, int* occupancy);
 hipError_t mk_launch_monokernel_w4h128_ctr(const KParams* kp_dev, int grid, int lds_bytes, hipStream_t s);
 hipError_t mk_kernel_attributes_w4h128_ctr(int lds_bytes, int* occupancy);
+hipError_t mk_launch_monokernel_w4h128_long(const KParams* kp_dev, int grid, int lds_bytes, hipStream_t s);
+hipError_t mk_kernel_attributes_w4h128_long(int lds_bytes, int* occupancy);
 hipError_t mk_launch_fill32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 hipError_t mk_launch_fill_kv(uint16_t* kc, uint16_t* vc, int64_t rows, int max_seq, int hd, int p0, int p1, hipStream_t s);
 hipError_t mk_launch_gather(uint16_t* dst, const void* desc, int64_t n_chunks, hipStream_t s);
@@ -72,6 +74,7 @@ struct Engine {
   Plan plan;
   int n_cu = 0, occ = 0, grid = 0;
   bool spec = false;  // every instruction fits the kernel specialised to 4-chunk slices and head_dim 128
+  int last_kind = -1;  // the kernel the last launch ran (kernel_kind), -1 before any
   std::string err;
   // device buffers
   uint8_t* d_stream = nullptr;
@@ -169,10 +172,11 @@ int engine_setup(Engine& g, int device, void* stream, const mk_options* opts, in
   g.n_cu = prop.multiProcessorCount;
   if (lds_bytes > (int)prop.sharedMemPerBlock) return g.fail(MK_EOCC, "LDS footprint exceeds the per-workgroup limit");
   HIPCHK(g, mk_kernel_attributes(lds_bytes, &g.occ));
-  int occ_spec = 0, occ_ctr = 0;
+  int occ_spec = 0, occ_ctr = 0, occ_long = 0;
   HIPCHK(g, mk_kernel_attributes_w4h128(lds_bytes, &occ_spec));
   HIPCHK(g, mk_kernel_attributes_w4h128_ctr(lds_bytes, &occ_ctr));
-  g.occ = std::min(g.occ, std::min(occ_spec, occ_ctr));  // any of the kernels may run this grid
+  HIPCHK(g, mk_kernel_attributes_w4h128_long(lds_bytes, &occ_long));
+  g.occ = std::min({g.occ, occ_spec, occ_ctr, occ_long});  // any of the kernels may run this grid
   if (g.occ < 1) return g.fail(MK_EOCC, "the monokernel does not fit on a CU (occupancy 0)");
   const int wave = g.n_cu * g.occ;
   g.grid = g.opt.grid > 0 ? g.opt.grid : wave;
@@ -272,6 +276,21 @@ void fill_common_params(Engine& g, KParams& k) {
   k.stall_word = g.d_stall;
 }
 
+// Which monokernel a launch whose first step decodes position pos0 runs: 0
+// general, 1 specialised (sentinel sync), 2 specialised (counter sync), 3
+// specialised with the DMA-fed long attention splits, taken when every split
+// of the first step is already longer than the short path's bound (the
+// context only grows within a launch; a short last split still takes the
+// short path there).  MK_GENERAL_KERNEL=1 forces the general kernel
+// (comparison runs).
+int kernel_kind(const Engine& g, int pos0) {
+  if (!g.spec || getenv("MK_GENERAL_KERNEL")) return 0;
+  if (g.plan.sync_mode != 0) return 2;
+  const int64_t T = (int64_t)pos0 + 1;
+  const bool long_splits = !g.plan.dm.chain && (T + g.plan.S - 1) / g.plan.S > kShortSplitMax;
+  return long_splits ? 3 : 1;
+}
+
 // Reset sync state, launch once, wait, collect the fault record.
 int launch(Engine& g, KParams& k, int n_steps) {
   HIPCHK(g, mk_launch_fill32(g.d_counters, std::max(1, g.plan.n_sync), 0u, g.stream));
@@ -284,11 +303,12 @@ int launch(Engine& g, KParams& k, int n_steps) {
   g.h_kp = k;
   HIPCHK(g, hipMemcpyAsync(g.d_kp, &g.h_kp, sizeof(KParams), hipMemcpyHostToDevice, g.stream));
   HIPCHK(g, hipEventRecord(g.ev0, g.stream));
-  // MK_GENERAL_KERNEL=1 forces the general kernel (comparison runs)
-  const bool spec = g.spec && !getenv("MK_GENERAL_KERNEL");
-  if (!spec) HIPCHK(g, mk_launch_monokernel(g.d_kp, g.grid, g.plan.lds_bytes, g.stream));
-  else if (g.plan.sync_mode == 0) HIPCHK(g, mk_launch_monokernel_w4h128(g.d_kp, g.grid, g.plan.lds_bytes, g.stream));
-  else HIPCHK(g, mk_launch_monokernel_w4h128_ctr(g.d_kp, g.grid, g.plan.lds_bytes, g.stream));
+  const int kind = kernel_kind(g, k.chain ? 0 : k.pos0);
+  g.last_kind = kind;
+  if (kind == 0) HIPCHK(g, mk_launch_monokernel(g.d_kp, g.grid, g.plan.lds_bytes, g.stream));
+  else if (kind == 1) HIPCHK(g, mk_launch_monokernel_w4h128(g.d_kp, g.grid, g.plan.lds_bytes, g.stream));
+  else if (kind == 2) HIPCHK(g, mk_launch_monokernel_w4h128_ctr(g.d_kp, g.grid, g.plan.lds_bytes, g.stream));
+  else HIPCHK(g, mk_launch_monokernel_w4h128_long(g.d_kp, g.grid, g.plan.lds_bytes, g.stream));
   HIPCHK(g, hipEventRecord(g.ev1, g.stream));
   HIPCHK(g, hipStreamSynchronize(g.stream));
   float ms = 0.f;
@@ -907,8 +927,10 @@ int mk_generate(mk_ctx* c, const int32_t* ids, int32_t n_prompt, int32_t n_steps
 
 const char* mk_kernel_name(const mk_ctx* c) {
   if (!c) return "";
-  if (!c->g.spec || getenv("MK_GENERAL_KERNEL")) return "mk_monokernel";
-  return c->g.plan.sync_mode == 0 ? "mk_monokernel_w4h128" : "mk_monokernel_w4h128_ctr";
+  static const char* const names[4] = {"mk_monokernel", "mk_monokernel_w4h128", "mk_monokernel_w4h128_ctr",
+                                       "mk_monokernel_w4h128_long"};
+  const int kind = c->g.last_kind >= 0 ? c->g.last_kind : kernel_kind(c->g, c->pos);
+  return names[kind];
 }
 
 int mk_set_sampling(mk_ctx* c, int32_t top_k, float temperature, uint64_t seed) {

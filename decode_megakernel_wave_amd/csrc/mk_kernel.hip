@@ -40,7 +40,7 @@
 #include "mk_device.h"
 #include "mk_layout.h"
 
-// The file is compiled three times.  The general build holds mk_monokernel
+// The file is compiled four times.  The general build holds mk_monokernel
 // (every slice width, head_dim and sync mode) and the helper kernels.  With
 // MK_SPECIALIZED it holds only one specialised interpreter, restricted to GEMV
 // slices of four chunks (rows of 2048 or more columns), head_dim 128 with two
@@ -50,7 +50,13 @@
 // Leaving the other widths, head geometries and the other sync mode out of
 // the kernel's code made the ~2B decode about 5 % faster (the interpreter's
 // code is several times larger than the instruction cache); the host picks a
-// specialised kernel when every instruction of the schedule fits it.
+// specialised kernel when every instruction of the schedule fits it.  The
+// fourth build (MK_LONG_DMA, sentinel sync, mk_monokernel_w4h128_long) streams
+// long attention splits through LDS rings by DMA; the host runs it for
+// launches whose splits are long from the first step (long contexts).  It is
+// a kernel of its own because the monokernel is one function: inlined next to
+// the short-context code, that pass changed the register allocation and code
+// layout of the rest and made the 512-token decode 0.8 % slower.
 #ifdef MK_SPECIALIZED
 // query heads per kv head and head_dim the specialised build is compiled for
 // (the host launches it only for that geometry); 0 = any
@@ -61,7 +67,11 @@ constexpr int kSpecGroup = 0;
 constexpr int kSpecHd = 0;
 #endif
 #ifdef MK_SPECIALIZED
-#if MK_SPEC_SYNC == 0
+#if MK_SPEC_SYNC == 0 && defined(MK_LONG_DMA)
+#define MK_MONOKERNEL mk_monokernel_w4h128_long
+#define MK_SPEC_LAUNCH mk_launch_monokernel_w4h128_long
+#define MK_SPEC_ATTR mk_kernel_attributes_w4h128_long
+#elif MK_SPEC_SYNC == 0
 #define MK_MONOKERNEL mk_monokernel_w4h128
 #define MK_SPEC_LAUNCH mk_launch_monokernel_w4h128
 #define MK_SPEC_ATTR mk_kernel_attributes_w4h128
@@ -722,7 +732,6 @@ __device__ __forceinline__ void red_unit(Cx& c, int l, int h, int b) {
 // w holds positions t0 + w + b * kWaves (b < kPosBatch) in kv / vv, lane i
 // dims [i*DPL, i*DPL + DPL).  GP * DPL <= 8 keeps the accumulators in 8
 // registers per lane whatever the head geometry.
-constexpr int kPosBatch = 4;
 
 template <int GP, int DPL>
 __device__ __forceinline__ void att_pos_core(Cx& c, Ring& ring, int l, int g, int sp, int j0, int ng, int t0, int t1, int G,
@@ -853,7 +862,6 @@ __device__ __forceinline__ void att_pass(Cx& c, int l, int g, int sp, int j0, in
   const KParams& kp = *c.kp;
   const int S = kp.S;
   constexpr int LPP = HD / 8, PPI = 64 / LPP;
-  constexpr int kAttBatch = GP >= 4 ? 4 : 8;  // position groups in flight (registers: 8 per group)
   const int sub = c.lane / LPP, dl = c.lane % LPP;
   const float* qs = c.sm.vec;            // [G][HD]
   const float* kcur = c.sm.vec + G * HD; // [HD]
@@ -869,6 +877,77 @@ __device__ __forceinline__ void att_pass(Cx& c, int l, int g, int sp, int j0, in
       q[j][e] = j < ng ? qs[(j0 + j) * HD + dl * 8 + e] : 0.f;
     }
   }
+#ifdef MK_LONG_DMA
+  // one position group (PPI positions, one per lane slot) into the online softmax; lanes past the
+  // split hold a copy of its last row (the DMA reads that for them) and count as a zero row
+  // with no weight
+  auto group = [&](int grp, const u4& kq, const u4& vq) {
+    const int t = t0 + grp * PPI + sub;
+    const bool valid = t < t1;
+    float kf[8], vf[8];
+    const h8 kh = __builtin_bit_cast(h8, kq), vh = __builtin_bit_cast(h8, vq);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kf[e] = !valid ? 0.f : t == c.pos ? kcur[dl * 8 + e] : (float)kh[e];
+      vf[e] = !valid ? 0.f : t == c.pos ? vcur[dl * 8 + e] : (float)vh[e];
+    }
+#pragma unroll
+    for (int j = 0; j < GP; ++j) {
+      if (GP != kSpecGroup && j >= ng) break;
+      float sc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sc = fmaf(q[j][e], kf[e], sc);
+      sc = slot_sum<LPP>(sc);
+      const float mn = valid ? fmaxf(m[j], sc) : m[j];
+      const float al = mn == -INFINITY ? 0.f : exp2f(m[j] - mn);
+      const float pv = valid ? exp2f(sc - mn) : 0.f;
+      lsum[j] = lsum[j] * al + pv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[j][e] = o[j][e] * al + pv * vf[e];
+      m[j] = mn;
+    }
+  };
+  const int ngroups = (t1 - t0 + PPI - 1) / PPI;
+  // this wavefront's groups: wave, wave + kWaves, ... (the order of the online updates)
+  const int mine = ngroups > c.wave ? (ngroups - c.wave + kWaves - 1) / kWaves : 0;
+  const int64_t head_row0 = ((int64_t)l * kp.nkv + g) * kp.max_seq;
+  // K/V through a 2-group LDS ring per wavefront, filled by DMA (global -> LDS, nontemporal): a
+  // group is 1 KB of K and 1 KB of V (PPI consecutive rows), and a slot's refill goes out as soon
+  // as the slot is read.  With every workgroup starting its split at once, the CU streams these
+  // faster than the same bytes loaded into registers (probe of an 8192-token context: 12.1 vs
+  // 14.0 us per layer with 8 groups per wavefront in registers).  The ring sits in the staged
+  // vector after q and the current K/V row (the plan sizes the vector for it).
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // the kernel's dynamic LDS
+  const uint32_t ring0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)smem + (uint32_t)((const uint8_t*)c.sm.vec - c.sm.base) +
+      (uint32_t)(att_ring_offset(G, HD) * 4 + c.wave * 4096));
+  const uint8_t* kg = (const uint8_t*)uniform_ptr(kp.kc + head_row0 * HD);
+  const uint8_t* vg = (const uint8_t*)uniform_ptr(kp.vc + head_row0 * HD);
+  auto issue = [&](int i) {
+    const int t = min(t0 + (c.wave + i * kWaves) * PPI + sub, t1 - 1);  // rows past the split: a valid row, unused
+    const uint32_t voff = (uint32_t)t * (uint32_t)(HD * 2) + (uint32_t)dl * 16u;
+    const uint32_t slot = ring0 + (uint32_t)(i & 1) * 2048u;
+    dma_chunk(slot, kg, voff);
+    dma_chunk(slot + 1024u, vg, voff);
+  };
+  if (mine > 0) issue(0);
+  if (mine > 1) issue(1);
+  for (int i = 0; i < mine; ++i) {
+    const uint32_t a = ring0 + (uint32_t)(i & 1) * 2048u + (uint32_t)c.lane * 16u;
+    u4 kq, vq;
+    // this group's two DMAs have landed when at most the next group's two are outstanding
+    if (i + 1 < mine)
+      asm volatile("s_waitcnt vmcnt(2)\n\tds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
+                   : "=&v"(kq), "=&v"(vq) : "v"(a));
+    else
+      asm volatile("s_waitcnt vmcnt(0)\n\tds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
+                   : "=&v"(kq), "=&v"(vq) : "v"(a));
+    if (i + 2 < mine) issue(i + 2);
+    if (i == 0) ts_mark(c, 5);  // the first group landed
+    group(c.wave + i * kWaves, kq, vq);
+  }
+#else
+  constexpr int kAttBatch = GP >= 4 ? 4 : 8;  // position groups in flight (registers: 8 per group)
   const int64_t head_off = ((int64_t)l * kp.nkv + g) * kp.max_seq * HD + dl * 8;
   const uint16_t* kbase = kp.kc + head_off;
   const uint16_t* vbase = kp.vc + head_off;
@@ -918,6 +997,7 @@ __device__ __forceinline__ void att_pass(Cx& c, int l, int g, int sp, int j0, in
       }
     }
   }
+#endif
   ts_mark(c, 7);  // this wavefront's positions done
   // merge the PPI position slots of the wavefront (lanes dl, dl + LPP, ...)
 #pragma unroll
@@ -1114,7 +1194,7 @@ __device__ __forceinline__ void op_att(Cx& c, Ring& ring, const Ins& in) {
     const int U = in.u0 + ui, g = U / S, sp = U % S;
     const int t0 = sp * chunk, t1 = min(T, t0 + chunk);
     const bool has_cur = t0 <= c.pos && c.pos < t1;
-    if (t1 - t0 <= kPosBatch * kWaves) {
+    if (t1 - t0 <= kShortSplitMax) {
       // short split (at most kPosBatch positions per wavefront): scores of the batch first, then one softmax per head
       const int dpl = hd / 64;
 #ifdef MK_SPECIALIZED

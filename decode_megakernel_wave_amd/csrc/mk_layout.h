@@ -27,6 +27,8 @@ constexpr int kRedDims = 8;               // output dims per attention-reduce un
 constexpr int kScratchFloats = 4352;      // LDS scratch for cross-wave reductions (17 KB)
 constexpr int kResidRows = 1024;          // LDS rows for residual inputs / staged GEMV outputs
 constexpr int kMaxTopK = 16;              // largest k of top-k sampling
+constexpr int kPosBatch = 4;              // positions per wavefront of a short attention split
+constexpr int kShortSplitMax = kPosBatch * kWaves;  // longer splits take the long-split path
 
 // Small LDS fields after the residual rows (byte offsets within a 1 KB block).
 constexpr int kSmallBytes = 1024;
@@ -73,6 +75,13 @@ struct Ins {
   int32_t pad;
 };
 static_assert(sizeof(Ins) == 32, "Ins must be 32 bytes");
+
+// The attention stage's part of the staged vector (floats): q [G][hd] and
+// the current position's K and V rows, rounded up to 1 KB, then one 4 KB K/V
+// ring per wavefront for long splits (two position groups of 1 KB of K and
+// 1 KB of V, filled by DMA).
+MK_HD int att_ring_offset(int G, int hd) { return ((G + 2) * hd + 255) / 256 * 256; }
+MK_HD int att_stage_floats(int G, int hd) { return att_ring_offset(G, hd) + kWaves * 1024; }
 
 // GEMV split inside one workgroup: units are dealt round-robin to kWaves/ks
 // row groups; each row's chunks are split into ks slices of cps chunks.

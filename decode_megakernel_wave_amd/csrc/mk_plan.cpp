@@ -138,7 +138,7 @@ int plan_lds_bytes(const Dims& dm) {
   auto kpad = [](int K) { return ((K + kChunkHalfs - 1) / kChunkHalfs + 7) / 8 * 8 * kChunkHalfs; };
   if (dm.chain) return lds_bytes_for(kpad(dm.chain_n));
   const int G = dm.nkv > 0 ? dm.nq / dm.nkv : 1;
-  return lds_bytes_for(std::max({kpad(dm.d), kpad(dm.nq * dm.hd), kpad(dm.f), (G + 2) * dm.hd}));
+  return lds_bytes_for(std::max({kpad(dm.d), kpad(dm.nq * dm.hd), kpad(dm.f), att_stage_floats(G, dm.hd)}));
 }
 
 std::string build_plan(const Dims& dm, int n_cta, int S, int R, int sync_mode, Plan* out) {
@@ -189,7 +189,7 @@ std::string build_plan(const Dims& dm, int n_cta, int S, int R, int sync_mode, P
     stages.push_back({OP_LMHEAD, dm.L, dm.V, 1, dm.d, sid_dn(dm.L - 1), 5 * dm.L});
     stages.push_back({OP_ARGMAX, dm.L, 1, 0, 0, 5 * dm.L, -1});
     p.n_sync = 5 * dm.L + 1;
-    kpad_max = std::max({kpad(dm.d), kpad(qd), kpad(dm.f), (G + 2) * dm.hd});
+    kpad_max = std::max({kpad(dm.d), kpad(qd), kpad(dm.f), att_stage_floats(G, dm.hd)});
     const int64_t per_layer = (int64_t)(qd + 2 * dm.nkv * dm.hd) * dm.d + (int64_t)dm.d * qd + 3LL * dm.f * dm.d;
     p.weight_bytes = 2 * (per_layer * dm.L + (int64_t)dm.V * dm.d + (int64_t)dm.d * (2 * dm.L + 1) + dm.d);
   }

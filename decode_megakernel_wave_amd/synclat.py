@@ -116,8 +116,10 @@ def _summary(d: dict) -> dict:
 
 # Phases between the fine marks that wavefront 0 of every workgroup takes per
 # instruction (marks: 0 start, 1 inputs polled, 2 staged after the barrier,
-# 5 activations in registers -- attention: the wavefront's positions done,
-# 7 first weight chunk read -- attention: wavefront partials combined,
+# 5 activations in registers -- short attention split: the wavefront's
+# positions done; long split: its first K/V group loaded,
+# 7 first weight chunk read -- short split: wavefront partials combined; long
+# split: the wavefront's positions done,
 # 6 own rows done -- attention: split partials published, 3 op end (the
 # workgroup's rows published; attention: split merge done), 4 failure vote done).
 FINE_PHASES = (("wait_and_poll", 0, 1), ("barrier", 1, 2), ("activations", 2, 5),

@@ -196,12 +196,17 @@ int mk_generate(mk_ctx* ctx, const int32_t* ids, int32_t n_prompt, int32_t n_ste
  * positive and finite; the state is then unchanged. */
 int mk_set_sampling(mk_ctx* ctx, int32_t top_k, float temperature, uint64_t seed);
 
-/* Name of the monokernel the context's launches run: "mk_monokernel_w4h128"
- * or, in counter sync mode, "mk_monokernel_w4h128_ctr" (specialised to GEMV
- * slices of four 512-column chunks, head_dim 128 and the sync mode, used when
- * every instruction of the schedule fits it) or "mk_monokernel" (general).
- * Both compute the same results; the environment variable MK_GENERAL_KERNEL
- * forces the general one.  "" for a NULL context.  The string is static. */
+/* Name of the monokernel the context's last launch ran (before any launch:
+ * the one a decode from the current position would run):
+ * "mk_monokernel_w4h128" or, in counter sync mode, "mk_monokernel_w4h128_ctr"
+ * (specialised to GEMV slices of four 512-column chunks, head_dim 128 and the
+ * sync mode, used when every instruction of the schedule fits it),
+ * "mk_monokernel_w4h128_long" (the sentinel-mode specialised kernel whose long
+ * attention splits stream K/V through LDS by DMA, run when every split of the
+ * launch's first step is longer than 32 positions) or "mk_monokernel"
+ * (general).  All compute the same results; the environment variable
+ * MK_GENERAL_KERNEL forces the general one.  "" for a NULL context.  The
+ * string is static. */
 const char* mk_kernel_name(const mk_ctx* ctx);
 
 /* Move the generation state back to position pos (1 <= pos <= current): the

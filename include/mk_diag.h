@@ -88,9 +88,11 @@ int mk_debug_streams(const mk_ctx* ctx, const void** base, const void** wave_off
  * instruction, 8 uint64 device-clock (100 MHz) marks taken by thread 0
  * (wavefront 0) {0 instruction start, 1 inputs polled, 2 inputs staged (after
  * the barrier), 3 op end, 4 failure check done, 5 GEMV: activations in
- * registers / attention: the wavefront's positions done, 6 GEMV: the
- * wavefront's own rows done / attention: split partials published, 7 GEMV:
- * first weight chunk read / attention: wavefront partials combined}; zero
+ * registers / short attention split: the wavefront's positions done / long
+ * split: the first K/V group loaded (in LDS, or the first register batch
+ * issued), 6 GEMV: the wavefront's own rows done / attention: split partials
+ * published, 7 GEMV: first weight chunk read / short split: wavefront
+ * partials combined / long split: the wavefront's positions done}; zero
  * where not recorded.  capacity is in uint64 and must be at least
  * grid * max_ins_per_cta * 8. */
 int mk_debug_ts(mk_ctx* ctx, uint64_t* host, int64_t capacity);

@@ -6,7 +6,8 @@ time, so these cases keep every shape that decides which kernel path runs --
 d 2048, 16 query / 8 kv heads of 128 (two query heads per kv head), rows of
 2048 and 8192 columns -- and cut the depth to 2 layers and the vocabulary to
 4096.  Each asserts that the kernel specialised to that geometry
-(``mk_monokernel_w4h128``) is the one that runs, in the benchmark's launch
+(``mk_monokernel_w4h128``, or at long contexts its variant
+``mk_monokernel_w4h128_long``) is the one that runs, in the benchmark's launch
 configuration (grid = CUs x occupancy, 32 attention splits per kv head).
 
 - Long context (the 8192-token benchmark's prompt): every split holds about
@@ -27,6 +28,7 @@ from gpu_util import MARGIN, check_step_logits, oracle_run
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 SPEC = "mk_monokernel_w4h128"
+SPEC_LONG = "mk_monokernel_w4h128_long"  # the same, with long splits' K/V streamed through LDS by DMA
 SHORT_SPLIT_MAX = 4 * 8   # positions per split that the short path takes: 4 per wavefront x 8 wavefronts
 
 
@@ -47,6 +49,7 @@ def _parity(model, P, n, expect_long):
         splits = mk.mk_plan_check(model, P + n + 1, grid)["attn_splits"]
         feed = np.concatenate([[t0_ref], toks_ref[:-1]])
         toks, logits = mk.mk_decode_forced(ctx, feed, vocab=model.vocab)
+        ran = mk.mk_kernel_name(ctx)
         sent = mk.mk_count_sentinels(ctx)
         fault = mk.mk_stats(ctx)["fault"]["code"]
     finally:
@@ -56,8 +59,10 @@ def _parity(model, P, n, expect_long):
     chunks = [-(-(P + s + 1) // splits) for s in range(n)]
     if expect_long:
         assert min(chunks) > SHORT_SPLIT_MAX, chunks
+        assert ran == SPEC_LONG, ran
     else:
         assert all(3 * 8 < c <= SHORT_SPLIT_MAX for c in chunks), chunks
+        assert ran == SPEC, ran
     err = check_step_logits(logits, logs_ref, toks, toks_ref)
     print(f"[{model.name} P={P}] grid {grid}, {splits} splits, split lengths {chunks}: max |dlogit| {err:.2e}")
     if m0 > MARGIN:

@@ -133,10 +133,11 @@ def test_2b_specialised_kernel_equals_general(w2b, monkeypatch):
         assert mk.mk_kernel_name(ctx) == "mk_monokernel_w4h128"
         mk.mk_prefill(ctx, ids)
         a_tok, a_log = mk.mk_decode(ctx, n, vocab=inputs.M2B.vocab)
+        assert mk.mk_kernel_name(ctx) == "mk_monokernel_w4h128"
         monkeypatch.setenv("MK_GENERAL_KERNEL", "1")
-        assert mk.mk_kernel_name(ctx) == "mk_monokernel"
         mk.mk_prefill(ctx, ids)
         b_tok, b_log = mk.mk_decode(ctx, n, vocab=inputs.M2B.vocab)
+        assert mk.mk_kernel_name(ctx) == "mk_monokernel"
     finally:
         mk.mk_destroy(ctx)
         torch.cuda.empty_cache()
