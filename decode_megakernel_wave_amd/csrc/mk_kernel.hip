@@ -857,8 +857,51 @@ __device__ __forceinline__ float slot_sum(float v) {
   return v;
 }
 
+#ifdef MK_LONG_DMA
+// A long split's K/V ring of one wavefront: two slots of one position group
+// (PPI = 512 / HD consecutive rows: 1 KB of K, then 1 KB of V), filled by DMA
+// (global -> LDS, nontemporal), in the staged vector after q and the current
+// K/V row (the plan sizes the vector for it).  The wavefront's groups are
+// wave, wave + kWaves, ...: `mine` of them.
+struct KvRing {
+  uint32_t ring0;
+  const uint8_t* kg;
+  const uint8_t* vg;
+  int mine;
+};
+
+template <int HD>
+__device__ __forceinline__ KvRing kv_ring(const Cx& c, int l, int g, int t0, int t1, int G) {
+  constexpr int PPI = 512 / HD;
+  const KParams& kp = *c.kp;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // the kernel's dynamic LDS
+  const int ngroups = (t1 - t0 + PPI - 1) / PPI;
+  const int64_t head_row0 = ((int64_t)l * kp.nkv + g) * kp.max_seq;
+  KvRing r;
+  r.ring0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem + (uint32_t)((const uint8_t*)c.sm.vec - c.sm.base) +
+                                          (uint32_t)(att_ring_offset(G, HD) * 4 + c.wave * 4096));
+  r.kg = (const uint8_t*)uniform_ptr(kp.kc + head_row0 * HD);
+  r.vg = (const uint8_t*)uniform_ptr(kp.vc + head_row0 * HD);
+  r.mine = ngroups > c.wave ? (ngroups - c.wave + kWaves - 1) / kWaves : 0;
+  return r;
+}
+
+// DMA of the wavefront's group i (< r.mine) into slot i % 2; lanes past the
+// split read the split's last row (valid, unused).
+template <int HD>
+__device__ __forceinline__ void kv_issue(const Cx& c, const KvRing& r, int t0, int t1, int i) {
+  constexpr int LPP = HD / 8, PPI = 64 / LPP;
+  const int sub = c.lane / LPP, dl = c.lane % LPP;
+  const int t = min(t0 + (c.wave + i * kWaves) * PPI + sub, t1 - 1);
+  const uint32_t voff = (uint32_t)t * (uint32_t)(HD * 2) + (uint32_t)dl * 16u;
+  const uint32_t slot = r.ring0 + (uint32_t)(i & 1) * 2048u;
+  dma_chunk(slot, r.kg, voff);
+  dma_chunk(slot + 1024u, r.vg, voff);
+}
+#endif
+
 template <int HD, int GP>
-__device__ __forceinline__ void att_pass(Cx& c, int l, int g, int sp, int j0, int ng, int t0, int t1, int G) {
+__device__ __forceinline__ void att_pass(Cx& c, int l, int g, int sp, int j0, int ng, int t0, int t1, int G, int pre = 0) {
   const KParams& kp = *c.kp;
   const int S = kp.S;
   constexpr int LPP = HD / 8, PPI = 64 / LPP;
@@ -878,18 +921,23 @@ __device__ __forceinline__ void att_pass(Cx& c, int l, int g, int sp, int j0, in
     }
   }
 #ifdef MK_LONG_DMA
-  // one position group (PPI positions, one per lane slot) into the online softmax; lanes past the
-  // split hold a copy of its last row (the DMA reads that for them) and count as a zero row
-  // with no weight
-  auto group = [&](int grp, const u4& kq, const u4& vq) {
+  // one position group (PPI positions, one per lane slot) into the online softmax, rounded as the
+  // register path rounds: rows past the split and the current position's row (read from LDS
+  // instead) are zeroed as raw bits first, and the two updates are written as the fused forms
+  // the compiler chooses there, so this kernel's logits are bitwise those of the others
+  auto group = [&](int grp, u4 kq, u4 vq) {
     const int t = t0 + grp * PPI + sub;
     const bool valid = t < t1;
+    if (!valid || t == c.pos) {
+      kq = u4{0u, 0u, 0u, 0u};
+      vq = u4{0u, 0u, 0u, 0u};
+    }
     float kf[8], vf[8];
     const h8 kh = __builtin_bit_cast(h8, kq), vh = __builtin_bit_cast(h8, vq);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      kf[e] = !valid ? 0.f : t == c.pos ? kcur[dl * 8 + e] : (float)kh[e];
-      vf[e] = !valid ? 0.f : t == c.pos ? vcur[dl * 8 + e] : (float)vh[e];
+      kf[e] = t == c.pos ? kcur[dl * 8 + e] : (float)kh[e];
+      vf[e] = t == c.pos ? vcur[dl * 8 + e] : (float)vh[e];
     }
 #pragma unroll
     for (int j = 0; j < GP; ++j) {
@@ -901,39 +949,21 @@ __device__ __forceinline__ void att_pass(Cx& c, int l, int g, int sp, int j0, in
       const float mn = valid ? fmaxf(m[j], sc) : m[j];
       const float al = mn == -INFINITY ? 0.f : exp2f(m[j] - mn);
       const float pv = valid ? exp2f(sc - mn) : 0.f;
-      lsum[j] = lsum[j] * al + pv;
+      lsum[j] = fmaf(lsum[j], al, pv);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[j][e] = o[j][e] * al + pv * vf[e];
+      for (int e = 0; e < 8; ++e) o[j][e] = fmaf(vf[e], pv, o[j][e] * al);
       m[j] = mn;
     }
   };
-  const int ngroups = (t1 - t0 + PPI - 1) / PPI;
-  // this wavefront's groups: wave, wave + kWaves, ... (the order of the online updates)
-  const int mine = ngroups > c.wave ? (ngroups - c.wave + kWaves - 1) / kWaves : 0;
-  const int64_t head_row0 = ((int64_t)l * kp.nkv + g) * kp.max_seq;
-  // K/V through a 2-group LDS ring per wavefront, filled by DMA (global -> LDS, nontemporal): a
-  // group is 1 KB of K and 1 KB of V (PPI consecutive rows), and a slot's refill goes out as soon
-  // as the slot is read.  With every workgroup starting its split at once, the CU streams these
-  // faster than the same bytes loaded into registers (probe of an 8192-token context: 12.1 vs
-  // 14.0 us per layer with 8 groups per wavefront in registers).  The ring sits in the staged
-  // vector after q and the current K/V row (the plan sizes the vector for it).
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // the kernel's dynamic LDS
-  const uint32_t ring0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)smem + (uint32_t)((const uint8_t*)c.sm.vec - c.sm.base) +
-      (uint32_t)(att_ring_offset(G, HD) * 4 + c.wave * 4096));
-  const uint8_t* kg = (const uint8_t*)uniform_ptr(kp.kc + head_row0 * HD);
-  const uint8_t* vg = (const uint8_t*)uniform_ptr(kp.vc + head_row0 * HD);
-  auto issue = [&](int i) {
-    const int t = min(t0 + (c.wave + i * kWaves) * PPI + sub, t1 - 1);  // rows past the split: a valid row, unused
-    const uint32_t voff = (uint32_t)t * (uint32_t)(HD * 2) + (uint32_t)dl * 16u;
-    const uint32_t slot = ring0 + (uint32_t)(i & 1) * 2048u;
-    dma_chunk(slot, kg, voff);
-    dma_chunk(slot + 1024u, vg, voff);
-  };
-  if (mine > 0) issue(0);
-  if (mine > 1) issue(1);
+  // K/V through the wavefront's 2-group LDS ring, a slot's refill issued as soon as the slot is
+  // read.  With every workgroup starting its split at once, the CU streams these faster than the
+  // same bytes loaded into registers (probe of an 8192-token context: 12.1 vs 14.0 us per layer
+  // with 8 groups per wavefront in registers).  `pre` groups were issued before q was polled.
+  const KvRing r = kv_ring<HD>(c, l, g, t0, t1, G);
+  const int mine = r.mine;
+  for (int i = pre; i < 2 && i < mine; ++i) kv_issue<HD>(c, r, t0, t1, i);
   for (int i = 0; i < mine; ++i) {
-    const uint32_t a = ring0 + (uint32_t)(i & 1) * 2048u + (uint32_t)c.lane * 16u;
+    const uint32_t a = r.ring0 + (uint32_t)(i & 1) * 2048u + (uint32_t)c.lane * 16u;
     u4 kq, vq;
     // this group's two DMAs have landed when at most the next group's two are outstanding
     if (i + 1 < mine)
@@ -942,7 +972,7 @@ __device__ __forceinline__ void att_pass(Cx& c, int l, int g, int sp, int j0, in
     else
       asm volatile("s_waitcnt vmcnt(0)\n\tds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
                    : "=&v"(kq), "=&v"(vq) : "v"(a));
-    if (i + 2 < mine) issue(i + 2);
+    if (i + 2 < mine) kv_issue<HD>(c, r, t0, t1, i + 2);
     if (i == 0) ts_mark(c, 5);  // the first group landed
     group(c.wave + i * kWaves, kq, vq);
   }
@@ -1063,15 +1093,16 @@ __device__ __forceinline__ void att_pass(Cx& c, int l, int g, int sp, int j0, in
 
 // Query heads per pass: at most 4 (2 for head_dim 256), so the combine fits
 // the scratch: kWaves * heads * (HD + 2) floats.
+// (pre: K/V groups of the first pass already issued; the DMA-fed pass only)
 template <int HD>
-__device__ __forceinline__ void att_heads(Cx& c, int l, int g, int sp, int t0, int t1, int G) {
+__device__ __forceinline__ void att_heads(Cx& c, int l, int g, int sp, int t0, int t1, int G, int pre = 0) {
   constexpr int kMaxPass = HD == 256 ? 2 : 4;
   if (G == 1) {
-    att_pass<HD, 1>(c, l, g, sp, 0, 1, t0, t1, G);
+    att_pass<HD, 1>(c, l, g, sp, 0, 1, t0, t1, G, pre);
   } else if (G == 2 || kMaxPass == 2) {
-    for (int j0 = 0; j0 < G; j0 += 2) att_pass<HD, 2>(c, l, g, sp, j0, min(2, G - j0), t0, t1, G);
+    for (int j0 = 0; j0 < G; j0 += 2) att_pass<HD, 2>(c, l, g, sp, j0, min(2, G - j0), t0, t1, G, j0 == 0 ? pre : 0);
   } else {
-    for (int j0 = 0; j0 < G; j0 += 4) att_pass<HD, 4>(c, l, g, sp, j0, min(4, G - j0), t0, t1, G);
+    for (int j0 = 0; j0 < G; j0 += 4) att_pass<HD, 4>(c, l, g, sp, j0, min(4, G - j0), t0, t1, G, j0 == 0 ? pre : 0);
   }
 }
 
@@ -1206,11 +1237,23 @@ __device__ __forceinline__ void op_att(Cx& c, Ring& ring, const Ins& in) {
       else att_short<2, 4>(c, ring, l, g, sp, t0, t1, G, has_cur, ui == 0);
 #endif
     } else {
+#ifdef MK_LONG_DMA
+      // the wavefront's first two K/V groups go out before q is polled (their rows are in the
+      // cache already) and land while it waits; pulling the split's whole K/V towards L2 there
+      // instead was measured slower (it delayed the q polls)
+      int pre = 0;
+      {
+        const KvRing r = kv_ring<128>(c, l, g, t0, t1, G);
+        for (; pre < 2 && pre < r.mine; ++pre) kv_issue<128>(c, r, t0, t1, pre);
+      }
+#else
       // (no prefetch of the split's K/V rows before the wait: pulling them
       // towards L2 first was measured slower at 2048 and 8192 positions)
+      const int pre = 0;
+#endif
       att_stage(c, l, g, has_cur, ui == 0);
 #ifdef MK_SPECIALIZED
-      att_heads<128>(c, l, g, sp, t0, t1, G);
+      att_heads<128>(c, l, g, sp, t0, t1, G, pre);
 #else
       if (hd == 64) att_heads<64>(c, l, g, sp, t0, t1, G);
       else if (hd == 128) att_heads<128>(c, l, g, sp, t0, t1, G);
@@ -2083,7 +2126,7 @@ MK_INTERNAL hipError_t mk_scratch_address(int device, void** out, size_t* bytes)
     if (e == hipSuccess && cur != device) e = hipSetDevice(device);
     void* p = nullptr;
     if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-    if (cur != device) hipSetDevice(cur);
+    if (cur != device) (void)hipSetDevice(cur);  // best effort: the caller's device back
     if (e != hipSuccess) return e;
     addr[device] = p;
   }

@@ -8,7 +8,9 @@ d 2048, 16 query / 8 kv heads of 128 (two query heads per kv head), rows of
 4096.  Each asserts that the kernel specialised to that geometry
 (``mk_monokernel_w4h128``, or at long contexts its variant
 ``mk_monokernel_w4h128_long``) is the one that runs, in the benchmark's launch
-configuration (grid = CUs x occupancy, 32 attention splits per kv head).
+configuration (grid = CUs x occupancy, 32 attention splits per kv head), and
+that the general kernel (``mk_monokernel``, register-loaded long splits) gives
+bitwise the same logits for the same steps.
 
 - Long context (the 8192-token benchmark's prompt): every split holds about
   257 positions, so attention takes the long-split path for head_dim 128 with
@@ -17,6 +19,8 @@ configuration (grid = CUs x occupancy, 32 attention splits per kv head).
   32 splits of 25..32 positions, so each wavefront of a short split holds 4
   positions (the full short-split batch).
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -52,9 +56,19 @@ def _parity(model, P, n, expect_long):
         ran = mk.mk_kernel_name(ctx)
         sent = mk.mk_count_sentinels(ctx)
         fault = mk.mk_stats(ctx)["fault"]["code"]
+        # the same steps again on the general kernel (register-loaded long splits): bitwise equal
+        mk.mk_rewind(ctx, P)
+        os.environ["MK_GENERAL_KERNEL"] = "1"
+        try:
+            g_toks, g_logits = mk.mk_decode_forced(ctx, feed, vocab=model.vocab)
+            assert mk.mk_kernel_name(ctx) == "mk_monokernel"
+        finally:
+            del os.environ["MK_GENERAL_KERNEL"]
     finally:
         mk.mk_destroy(ctx)
         torch.cuda.empty_cache()
+    assert np.array_equal(g_toks, toks)
+    assert np.array_equal(g_logits.view(np.uint32), logits.view(np.uint32)), "general and specialised kernels differ"
     # which attention path ran: split length ceil(T / S) for every decoded position T = P + s + 1
     chunks = [-(-(P + s + 1) // splits) for s in range(n)]
     if expect_long:
