@@ -1302,9 +1302,9 @@ int mk_probe_read(int device, void* hip_stream, const void* buf, int64_t bytes, 
   PROBE_HIP(hipSetDevice(device), "hipSetDevice");
   hipDeviceProp_t prop;
   PROBE_HIP(hipGetDeviceProperties(&prop, device), "device properties");
-  const int grid = prop.multiProcessorCount * 8;
+  const int grid = prop.multiProcessorCount * 2;  // two workgroups of 512 threads per CU
   void* sink = nullptr;
-  PROBE_HIP(hipMalloc(&sink, (size_t)grid * 256 * 16), "sink allocation");
+  PROBE_HIP(hipMalloc(&sink, (size_t)grid * 512 * 16), "sink allocation");
   hipEvent_t a = nullptr, b = nullptr;
   hipError_t e = hipEventCreate(&a);
   if (e == hipSuccess) e = hipEventCreate(&b);

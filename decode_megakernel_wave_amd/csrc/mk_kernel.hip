@@ -1990,23 +1990,6 @@ static __device__ __align__(256) unsigned long long scratch[kScratchWords];
 // An empty kernel: launch overhead.
 __global__ void mk_probe_empty() {}
 
-// Stream n16 16-byte words with nontemporal loads, 8 in flight per thread; the
-// XOR of everything read goes to sink[thread] so no load can be dropped.
-__global__ __launch_bounds__(256) void mk_probe_read_k(const u4* __restrict__ p, int64_t n16, u4* __restrict__ sink) {
-  u4 acc = {0u, 0u, 0u, 0u};
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 7 * stride < n16; i += 8 * stride) {
-    u4 v[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = __builtin_nontemporal_load(p + i + k * stride);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) acc ^= v[k];
-  }
-  for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(p + i);
-  sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
-}
-
 // `rounds` naive grid barriers: every workgroup's first thread releases, adds 1
 // to one counter and polls it (system scope) until it reaches round x grid --
 // the pattern the atomic-counter path pays per stage.  Workgroup 0 records the
@@ -2087,10 +2070,6 @@ MK_INTERNAL hipError_t mk_launch_gather(uint16_t* dst, const void* desc, int64_t
 }
 MK_INTERNAL hipError_t mk_launch_probe_empty(hipStream_t s) {
   hipLaunchKernelGGL(mk_probe_empty, dim3(1), dim3(64), 0, s);
-  return hipGetLastError();
-}
-MK_INTERNAL hipError_t mk_launch_probe_read(const void* p, int64_t n16, void* sink, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(mk_probe_read_k, dim3(grid), dim3(256), 0, s, (const u4*)p, n16, (u4*)sink);
   return hipGetLastError();
 }
 MK_INTERNAL hipError_t mk_launch_probe_barrier(uint32_t* counter, int rounds, uint64_t deadline_ticks, uint64_t* out,

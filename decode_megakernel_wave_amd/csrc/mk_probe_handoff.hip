@@ -19,6 +19,9 @@
 // with same_xcd, (k, k+8) in blocks of 16, which the round-robin dispatch puts
 // on one XCD; the kernel records each member's XCC_ID so the host can report
 // how many pairs really shared one.  Every wait is bounded by a spin limit.
+//
+// The file also holds the read-ceiling probe: the rate at which the chip
+// streams a large buffer with nontemporal 16-byte loads.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -122,6 +125,34 @@ __global__ __launch_bounds__(512, 1) void mk_probe_handoff_k(HandoffArgs a) {
   a.sink[(int64_t)wg * 512 + threadIdx.x] = acc;
 }
 
+// Read ceiling: n16 16-byte words with nontemporal loads, in blocks of 16
+// consecutive 1 KB chunks (one per load instruction of a wavefront, 16 KB in
+// flight per wavefront), block b read by wavefront b mod (waves in the grid);
+// then the chunks past the last whole block and the words past the last
+// chunk.  The XOR of everything read goes to sink[thread] so that no load can
+// be dropped.  (A grid-stride loop whose 8 loads per thread lay 8 MB apart
+// read 6.0 TB/s; consecutive kilobytes per wavefront read 7.0.)
+__global__ __launch_bounds__(512) void mk_probe_read_k(const u4* __restrict__ p, int64_t n16, u4* __restrict__ sink) {
+  constexpr int kBlk = 16;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / 64);
+  const int64_t nch = n16 / 64, nblk = nch / kBlk;
+  u4 acc = {0u, 0u, 0u, 0u};
+  for (int64_t b = wave; b < nblk; b += nwaves) {
+    const u4* q = p + b * kBlk * 64 + lane;
+    u4 v[kBlk];
+#pragma unroll
+    for (int k = 0; k < kBlk; ++k) v[k] = __builtin_nontemporal_load(q + k * 64);
+#pragma unroll
+    for (int k = 0; k < kBlk; ++k) acc ^= v[k];
+  }
+  for (int64_t c = nblk * kBlk + wave; c < nch; c += nwaves) acc ^= __builtin_nontemporal_load(p + c * 64 + lane);
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (nch * 64 + t < n16) acc ^= __builtin_nontemporal_load(p + nch * 64 + t);
+  sink[t] = acc;
+}
+
 }  // namespace
 }  // namespace mk
 
@@ -151,5 +182,11 @@ MK_INTERNAL hipError_t mk_probe_handoff_occupancy(int* occupancy) {
 }
 
 MK_INTERNAL int mk_probe_handoff_pairs() { return mk::kProbePairs; }
+
+// The read-ceiling probe over `grid` workgroups of 512 threads; sink holds grid * 512 u4.
+MK_INTERNAL hipError_t mk_launch_probe_read(const void* p, int64_t n16, void* sink, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(mk::mk_probe_read_k, dim3(grid), dim3(512), 0, s, (const mk::u4*)p, n16, (mk::u4*)sink);
+  return hipGetLastError();
+}
 
 }  // extern "C"

@@ -110,8 +110,9 @@ int mk_chain_debug_ts(mk_chain* ch, uint64_t* host, int64_t capacity);
  *   (host microseconds per launch -> *us_pipelined), and n_launches launch + synchronise
  *   pairs (-> *us_round_trip).
  * mk_probe_read: reads `bytes` (a multiple of 16, 16-byte aligned device buffer, borrowed)
- *   `repeats` times with nontemporal 16-byte loads from 8 workgroups per CU; GB/s from HIP
- *   events (one untimed warm-up pass first).
+ *   `repeats` times with nontemporal 16-byte loads, two workgroups of 512 threads per CU, each
+ *   wavefront reading 16 consecutive KB per round; GB/s from HIP events (one untimed warm-up
+ *   pass first).
  * mk_probe_barrier: `rounds` (1..1e6) grid barriers of one workgroup per CU, each a release,
  *   an atomic add to one counter and system-scope polls until every workgroup has arrived;
  *   microseconds per barrier on the device clock.  A round that does not complete within 1 s
