@@ -98,6 +98,13 @@ def test_2b_geometry_upper_half_context(P):
     _parity(inputs.M2B_GEOM_L2, P=P, n=4, expect_long=False)
 
 
+def test_2b_geometry_long_kernel_just_past_the_short_bound():
+    """T = 1031..1034: splits of 33 positions (9 groups of 4), so the long-context kernel runs and
+    each wavefront's K/V ring holds one or two groups (the prefetch before the q poll is partial
+    for most); the last split holds 8..11 positions and takes the short path inside that kernel."""
+    _parity(inputs.M2B_GEOM_L2, P=1030, n=4, expect_long=True)
+
+
 def test_2b_geometry_prompt_6000_partial_attention_round():
     """Prompt of 6000 tokens: 47 super-blocks of 128 queries x 8 kv heads = 376 prefill attention
     items, so the second round of the static deal (dealt in reverse super-block order) is partial
