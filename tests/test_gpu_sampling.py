@@ -10,6 +10,8 @@ takes u = floor(word / 2^8) / 2^24, so a draw whose running sum lies within
 1e-5 (relative) of u * total, or whose k-th and (k+1)-th logits are within
 1e-5, could go either way; those draws are skipped (and counted).
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -105,6 +107,36 @@ def test_half_billion_model_draws_match(tiny):
     assert sent == 0 and t0 == t0b
     n = _check_draws(toks, logits, 16 + np.arange(8), 16, 1.0, 77)
     assert n >= 6
+
+
+def test_long_context_kernel_draws_match_and_equal_the_general_kernel():
+    """Top-16 sampling on the ~2B geometry (2 layers) after a 1100-token prompt: every split is
+    longer than 32 positions, so the long-context kernel (DMA-fed K/V rings) draws the tokens;
+    the draws match the oracle's choice on its logits, and the general kernel draws the same
+    tokens from bitwise the same logits."""
+    cfg = inputs.M2B_GEOM_L2
+    w = inputs.make_weights(cfg, seed=0)
+    ids = inputs.make_prompt(cfg, 1100, seed=2)
+    n, top_k, temperature, seed = 6, 16, 1.0, 91
+    ctx = load(mk, cfg, w, len(ids) + n + 1)
+    try:
+        mk.mk_set_sampling(ctx, top_k, temperature, seed)
+        mk.mk_prefill(ctx, ids)
+        toks, logits = mk.mk_decode(ctx, n, vocab=cfg.vocab)
+        assert mk.mk_kernel_name(ctx) == "mk_monokernel_w4h128_long"
+        sent = mk.mk_count_sentinels(ctx)
+        mk.mk_rewind(ctx, len(ids))
+        os.environ["MK_GENERAL_KERNEL"] = "1"
+        try:
+            g_toks, g_logits = mk.mk_decode(ctx, n, vocab=cfg.vocab)
+        finally:
+            del os.environ["MK_GENERAL_KERNEL"]
+    finally:
+        mk.mk_destroy(ctx)
+    assert sent == 0
+    assert np.array_equal(g_toks, toks)
+    assert np.array_equal(g_logits.view(np.uint32), logits.view(np.uint32))
+    assert _check_draws(toks, logits, len(ids) + np.arange(n), top_k, temperature, seed) >= n - 1
 
 
 def test_invalid_sampling_arguments(tiny):
