@@ -439,8 +439,9 @@ __device__ __forceinline__ void ring_read_n(Ring& ring, u4 (&w)[4], int n, bool 
 // CUs that stream takes about 1.8 us, between two that do not 0.6-0.8 us, with
 // the rest of the chip streaming in both cases.  Issuing the last refills after
 // the stores lets the outputs leave first.  QKV's are issued later still, in
-// the attention stage after its q polls, K/V loads and scores (the attention
-// reads no weights, so they still land before the next GEMV): 2 % faster
+// the attention stage after its q polls, K/V loads and the split's published
+// partials (the attention reads no weights, so they still land before the
+// next GEMV): 2 % faster
 // decode than issuing them after QKV's stores, where they sat ahead of those
 // polls.  The
 // other GEMVs' could not wait that long: issued only after the next GEMV had
@@ -796,9 +797,6 @@ __device__ __forceinline__ void att_pos_core(Cx& c, Ring& ring, int l, int g, in
     }
   }
   ts_mark(c, 5);
-  // the refills QKV left owed go out here, behind the q polls, the K/V loads and the scores (issued
-  // before the scores they could hold the wavefront at the issue: 456.3 vs 457.3 ms per 512 tokens)
-  ring_settle(ring);
   // combine the wavefronts: scratch [wave][ng][hd + 2]
   float* scr = c.sm.scratch;
   const int rec = hd + 2;
@@ -842,6 +840,12 @@ __device__ __forceinline__ void att_pos_core(Cx& c, Ring& ring, int l, int g, in
       }
     }
   }
+  // the refills QKV left owed go out here, behind the q polls, the K/V loads and the split's
+  // published partials, which would otherwise leave the CU behind them: 447.9 vs 451.5 ms per 512
+  // tokens against issuing them before the wavefronts combine (456.3 there vs 457.3 before the
+  // scores, where they could hold the wavefront at the issue); issued only after the split merge
+  // they arrive late for O-proj (464.1 vs 449.8)
+  ring_settle(ring);
   cta_sync(c);  // scratch reused by the next pass
 }
 
